@@ -1,0 +1,226 @@
+"""fp64 reference of jagged attention, forward and backward (test infrastructure only).
+
+Operands are packed jagged tensors: ``q``, ``dout`` are ``[Tq, H, D]`` and ``k``, ``v`` are
+``[Tkv, H, D]`` with sequence ``b`` in rows ``off[b]:off[b+1]`` (values + offsets, vibekk.com GEM
+page, FAQ entry on jagged tensors). Nothing is padded: each (sequence, head) is handled on its
+own slice. Query rows are processed in chunks so that the longest sequence fits in memory; the
+chunking changes no arithmetic beyond the order of independent rows.
+
+For one sequence b and head h (i < Lq_b, j < Lkv_b):
+
+  s_ij   = scale * <Q_i, K_j> + beta_h(i, j)        beta: 0 | c_h | T[h, bucket(i - j)]
+  vis_ij = (mask == none) or (j <= i)
+
+softmax (FlashAttention's result on jagged tensors; aihot.vn GEM page, "Jagged Sequence Flash
+Attention"; kerneldigest.dev page, "Fundamentos Teóricos"):
+
+  P_ij = exp(s_ij - m_i) / l_i on visible pairs,  m_i = max_vis s_ij,  l_i = sum_vis exp(s_ij - m_i)
+  O_i  = sum_j P_ij V_j,   lse_i = m_i + ln l_i;    a row with nothing visible gives O_i = 0, lse_i = -inf
+
+GDPA (two matrix products with a pointwise activation in place of softmax; aihot.vn GEM page,
+"Generalized Dot-Product Attention (GDPA)"), normalised by the sequence's key count:
+
+  O_i = (1 / Lkv_b) sum_vis act(s_ij) V_j,   act = SiLU or GELU (tanh form)
+
+Masked pairs contribute exactly nothing in both modes: the pages describe masking "by
+subtraction" (kerneldigest.dev page, "Arquitectura del Sistema") — a device mechanism, read here
+as exclusion.
+
+The backward pass is the gradient of <O, dO> (plus nothing from lse) with respect to q, k, v and
+the bias parameters, written out:
+
+  softmax: dP = dO V^T, Delta_i = sum_j P_ij dP_ij, dS = P (dP - Delta)
+  GDPA:    dP = dO V^T / Lkv_b, dS = dP act'(s) on visible pairs
+  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO (softmax) | act(s)^T dO / Lkv_b (GDPA)
+  dc_h = sum dS,    dT[h, u] = sum of dS over pairs with bucket(i - j) = u
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+from .bucket import NUM_BUCKETS, bucket
+
+_SQRT_2_OVER_PI = math.sqrt(2.0 / math.pi)
+_GELU_C = 0.044715
+_ROW_CHUNK_ELEMS = 1 << 23      # bound on rows * Lkv per chunk (64 MiB of fp64 scores)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns (uint16) to float64."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def silu(x):
+    """SiLU(x) = x / (1 + exp(-x))."""
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def silu_grad(x):
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-x))
+    return sig * (1.0 + x * (1.0 - sig))
+
+
+def gelu_tanh(x):
+    """GELU, tanh form: x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    return 0.5 * x * (1.0 + np.tanh(_SQRT_2_OVER_PI * (x + _GELU_C * x ** 3)))
+
+
+def gelu_tanh_grad(x):
+    t = np.tanh(_SQRT_2_OVER_PI * (x + _GELU_C * x ** 3))
+    du = _SQRT_2_OVER_PI * (1.0 + 3.0 * _GELU_C * x ** 2)
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * du
+
+
+_ACTS = {"silu": (silu, silu_grad), "gelu_tanh": (gelu_tanh, gelu_tanh_grad)}
+
+
+def _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias):
+    q_off = np.asarray(q_off, dtype=np.int64)
+    kv_off = np.asarray(kv_off, dtype=np.int64)
+    if q_off.ndim != 1 or q_off.shape != kv_off.shape or len(q_off) < 2:
+        raise ValueError("offsets must be [B+1]")
+    if q_off[0] != 0 or kv_off[0] != 0 or np.any(np.diff(q_off) < 0) or np.any(np.diff(kv_off) < 0):
+        raise ValueError("offsets must start at 0 and be non-decreasing")
+    if q.shape[0] != q_off[-1] or k.shape[0] != kv_off[-1] or v.shape != k.shape:
+        raise ValueError("tensor rows do not match offsets")
+    if mask not in ("none", "causal") or act not in ("softmax", "silu", "gelu_tanh"):
+        raise ValueError("bad mode")
+    H = q.shape[1]
+    if bias_kind == "scalar":
+        assert bias is not None and np.shape(bias) == (H,)
+    elif bias_kind == "bucket":
+        assert bias is not None and np.shape(bias) == (H, NUM_BUCKETS)
+    elif bias_kind != "none":
+        raise ValueError("bad bias kind")
+    return q_off, kv_off
+
+
+def _scores(Qc, K, i0, scale, mask, bias_kind, bias_h):
+    """Scores and visibility of query rows i0.. of one (sequence, head) against all its keys."""
+    rows, lkv = Qc.shape[0], K.shape[0]
+    S = scale * (Qc @ K.T)
+    i = i0 + np.arange(rows)[:, None]
+    j = np.arange(lkv)[None, :]
+    if bias_kind == "scalar":
+        S = S + bias_h
+    elif bias_kind == "bucket":
+        S = S + bias_h[bucket(i - j)]
+    if mask == "causal":
+        vis = j <= i
+    else:
+        vis = np.ones((rows, lkv), dtype=bool)
+    return S, vis, i - j
+
+
+def _softmax_rows(S, vis):
+    """Normalised probabilities and log-sum-exp of each row over its visible entries."""
+    any_vis = vis.any(axis=1)
+    m = np.where(vis, S, -np.inf).max(axis=1, initial=-np.inf)
+    m_safe = np.where(any_vis, m, 0.0)
+    E = np.where(vis, np.exp(S - m_safe[:, None]), 0.0)
+    l = E.sum(axis=1)
+    P = np.where(any_vis[:, None], E / np.where(any_vis, l, 1.0)[:, None], 0.0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(any_vis, m + np.log(np.where(any_vis, l, 1.0)), -np.inf)
+    return P, lse
+
+
+def _chunks(lq, lkv):
+    step = max(1, min(1024, _ROW_CHUNK_ELEMS // max(1, lkv)))
+    for i0 in range(0, lq, step):
+        yield i0, min(lq, i0 + step)
+
+
+def _select(n, subset):
+    return range(n) if subset is None else subset
+
+
+def forward(q, k, v, q_off, kv_off, *, mask="none", act="softmax", bias_kind="none", bias=None,
+            scale: Optional[float] = None, seqs: Optional[Sequence[int]] = None,
+            heads: Optional[Sequence[int]] = None):
+    """Attention output ``[Tq, H, D]`` and, for softmax, ``lse [H, Tq]`` (natural log).
+
+    ``q``, ``k``, ``v`` are float64 (use :func:`bf16_bits_to_f64` for bf16 operands). ``seqs`` /
+    ``heads`` restrict the work to a subset; entries outside it are left NaN.
+    """
+    q_off, kv_off = _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias)
+    Tq, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = np.full((Tq, H, D), np.nan)
+    lse = np.full((H, Tq), np.nan) if act == "softmax" else None
+    for b in _select(len(q_off) - 1, seqs):
+        qs, qe, ks, ke = q_off[b], q_off[b + 1], kv_off[b], kv_off[b + 1]
+        lq, lkv = qe - qs, ke - ks
+        for h in _select(H, heads):
+            K, V = k[ks:ke, h], v[ks:ke, h]
+            bias_h = None if bias is None else np.asarray(bias, dtype=np.float64)[h]
+            for i0, i1 in _chunks(lq, lkv):
+                S, vis, _ = _scores(q[qs + i0:qs + i1, h], K, i0, scale, mask, bias_kind, bias_h)
+                if act == "softmax":
+                    P, lse_c = _softmax_rows(S, vis)
+                    out[qs + i0:qs + i1, h] = P @ V
+                    lse[h, qs + i0:qs + i1] = lse_c
+                else:
+                    f, _ = _ACTS[act]
+                    A = np.where(vis, f(S), 0.0)
+                    out[qs + i0:qs + i1, h] = (A @ V) / lkv if lkv > 0 else 0.0
+    return out, lse
+
+
+def backward(q, k, v, q_off, kv_off, dout, *, mask="none", act="softmax", bias_kind="none", bias=None,
+             scale: Optional[float] = None, seqs: Optional[Sequence[int]] = None,
+             heads: Optional[Sequence[int]] = None):
+    """Gradients ``(dq, dk, dv, dbias)`` of ``<forward(...).out, dout>``.
+
+    ``dbias`` has the bias shape (``[H]`` or ``[H, 64]``) or is None without a bias; when
+    ``seqs`` / ``heads`` select a subset, ``dbias`` sums over that subset only.
+    """
+    q_off, kv_off = _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias)
+    Tq, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    dbias = None if bias is None else np.zeros(np.shape(bias))
+    for b in _select(len(q_off) - 1, seqs):
+        qs, qe, ks, ke = q_off[b], q_off[b + 1], kv_off[b], kv_off[b + 1]
+        lq, lkv = qe - qs, ke - ks
+        for h in _select(H, heads):
+            K, V = k[ks:ke, h], v[ks:ke, h]
+            bias_h = None if bias is None else np.asarray(bias, dtype=np.float64)[h]
+            dK = np.zeros((lkv, D))
+            dV = np.zeros((lkv, D))
+            for i0, i1 in _chunks(lq, lkv):
+                Qc = q[qs + i0:qs + i1, h]
+                dOc = dout[qs + i0:qs + i1, h]
+                S, vis, rel = _scores(Qc, K, i0, scale, mask, bias_kind, bias_h)
+                if act == "softmax":
+                    P, _ = _softmax_rows(S, vis)
+                    dP = dOc @ V.T
+                    delta = (P * dP).sum(axis=1)
+                    dS = P * (dP - delta[:, None])
+                    dV += P.T @ dOc
+                else:
+                    f, fprime = _ACTS[act]
+                    inv_l = 1.0 / lkv if lkv > 0 else 0.0
+                    A = np.where(vis, f(S), 0.0)
+                    dP = (dOc @ V.T) * inv_l
+                    dS = np.where(vis, dP * fprime(S), 0.0)
+                    dV += (A.T @ dOc) * inv_l
+                dq[qs + i0:qs + i1, h] = scale * (dS @ K)
+                dK += scale * (dS.T @ Qc)
+                if bias_kind == "scalar":
+                    dbias[h] += dS.sum()
+                elif bias_kind == "bucket":
+                    dbias[h] += np.bincount(bucket(rel[vis]), weights=dS[vis], minlength=NUM_BUCKETS)
+            dk[ks:ke, h] = dK
+            dv[ks:ke, h] = dV
+    return dq, dk, dv, dbias

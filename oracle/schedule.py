@@ -1,0 +1,78 @@
+"""Work lists of the jagged tile scheduler, written from its rules (test infrastructure only).
+
+Padding jagged sequences to a common length wastes compute, and without padding the naive grid
+leaves compute units idle once short sequences finish (aihot.vn GEM page, "Jagged Sequence Flash
+Attention"); after padding is gone the bottleneck moves to tile scheduling and load balance
+(vibekk.com GEM page, section on moving from padding to jagged kernels). The planner therefore
+emits one work item per tile of useful work, splits items that alone exceed a fair share, and
+orders the list longest first so that greedy in-order dispatch approximates longest-processing-
+time scheduling. These are the rules, restated here independently of the C++ planner so that the
+two can be compared entry by entry:
+
+query-tile lists (forward and dQ), tile BM queries x BN keys:
+  for b, h, t in lexicographic order with t < ceil(Lq_b / BM):
+      n_kv = ceil(Lkv_b / BN)
+      cost = min(ceil((t + 1) BM / BN), n_kv) under the causal mask, else n_kv
+      item covers key tiles [0, cost)
+key-tile lists (dK/dV), tile BNk keys x BMq queries:
+  for b, h, kt in lexicographic order with kt < ceil(Lkv_b / BNk):
+      n_q = ceil(Lq_b / BMq);  first = floor(kt BNk / BMq) under the causal mask, else 0
+      cost = max(0, n_q - first);  item covers query tiles [first, first + cost)
+splitting (both lists), given the number of concurrent workgroups ``slots``:
+  target = max(1, ceil(sum(cost) / slots)); an item with cost > target becomes
+  R = ceil(cost / target) pieces, piece r covering [lo + floor(r cost / R), lo + floor((r+1) cost / R));
+  split groups are numbered in the lexicographic order above and own partial slots
+  slot0 .. slot0 + R - 1 (piece r -> slot0 + r); unsplit items carry slot -1
+order: by (piece length descending, b, h, tile, range start) ascending.
+
+Each item is the tuple (b, h, tile, lo, hi, slot); each split group is (b, h, tile, slot0, R).
+"""
+from __future__ import annotations
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def _finish(raw, slots: int, split: bool):
+    total = sum(hi - lo for (_, _, _, lo, hi) in raw)
+    target = max(1, _ceil_div(total, max(1, slots)))
+    items, groups = [], []
+    next_slot = 0
+    for (b, h, t, lo, hi) in raw:
+        cost = hi - lo
+        if split and cost > target:
+            R = _ceil_div(cost, target)
+            groups.append((b, h, t, next_slot, R))
+            for r in range(R):
+                items.append((b, h, t, lo + (r * cost) // R, lo + ((r + 1) * cost) // R, next_slot + r))
+            next_slot += R
+        else:
+            items.append((b, h, t, lo, hi, -1))
+    items.sort(key=lambda it: (-(it[4] - it[3]), it[0], it[1], it[2], it[3]))
+    return items, groups, next_slot
+
+
+def query_tile_items(lq, lkv, H: int, causal: bool, BM: int, BN: int, slots: int, split: bool = True):
+    """(items, groups, n_partial_slots) for a kernel that owns query tiles and loops over keys."""
+    raw = []
+    for b in range(len(lq)):
+        n_kv = _ceil_div(int(lkv[b]), BN)
+        for h in range(H):
+            for t in range(_ceil_div(int(lq[b]), BM)):
+                cost = min(_ceil_div((t + 1) * BM, BN), n_kv) if causal else n_kv
+                raw.append((b, h, t, 0, cost))
+    return _finish(raw, slots, split)
+
+
+def key_tile_items(lq, lkv, H: int, causal: bool, BMq: int, BNk: int, slots: int, split: bool = True):
+    """(items, groups, n_partial_slots) for a kernel that owns key tiles and loops over queries."""
+    raw = []
+    for b in range(len(lq)):
+        n_q = _ceil_div(int(lq[b]), BMq)
+        for h in range(H):
+            for kt in range(_ceil_div(int(lkv[b]), BNk)):
+                first = (kt * BNk) // BMq if causal else 0
+                cost = max(0, n_q - first)
+                raw.append((b, h, kt, first, first + cost))
+    return _finish(raw, slots, split)
