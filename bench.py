@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark: useful (unpadded, unmasked) attention TFLOPS of jagged attention fwd+bwd on 1 MI355X.
+
+A step is one pass of the whole hot path over one batch: the forward pass (work-list driven
+forward kernel and, when the plan split items, the combine kernel) and the backward pass
+(Delta preprocess, dK/dV kernel, dQ kernel, partial reduces), all through the C ABI. The plan
+(offset validation and the longest-first work lists) is built once per batch of offsets before
+the timed region; its host time is reported as ``plan_ms``.
+
+Useful FLOPs per visible (query, key) pair and head: 4 D forward + 10 D backward. Inputs are the
+seeded synthetic workload from ``jfa_inputs``, resident in HBM before timing starts.
+
+Prints ONE JSON line. ``--gpus`` above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+METRIC = "useful (unpadded) attention TFLOPS fwd+bwd and % of bf16 MFMA peak, 1×MI355X"
+DEFAULT_WORKLOAD = "causal_bucket"
+# FLOPs each kernel must execute per visible pair and head (its own matrix products):
+#   forward: S = QK^T, O = PV; dK/dV: S, dP = dO V^T, dV = P^T dO, dK = dS^T Q; dQ: S, dP, dQ = dS K
+KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dkdv": 8, "dq": 6}
+KERNEL_SOURCES = {"forward": ["fwd.hip", "device_common.h", "jfa_internal.h"],
+                  "dkdv": ["bwd.hip", "device_common.h", "jfa_internal.h"],
+                  "dq": ["bwd.hip", "device_common.h", "jfa_internal.h"]}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "jagged_sequence_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
+
+    The summary under profiles/ records FETCH_SIZE and WRITE_SIZE per dispatch (KiB), the copy-kernel
+    calibration factor and the hash of the kernel sources it was taken with; a changed kernel makes
+    the figure stale and it is not reported.
+    """
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_hash:\s*(\w+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != source_hash(kernel):
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(x, workload, seconds_target=15.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the workload's sequences."""
+    import numpy as np
+
+    from oracle import attention as A
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    from jagged_sequence_amd.flops import useful_flops
+    f = A.bf16_bits_to_f64
+    lq = np.diff(x.q_off.astype(np.int64))
+    lkv = np.diff(x.kv_off.astype(np.int64))
+    causal = x.mask == "causal"
+    # greedy sample: sequences in order until the estimated oracle work reaches the target
+    est_rate = 8e9  # fp64 useful FLOP/s of the oracle on a 16-core host, for sizing the sample only
+    budget = seconds_target * est_rate
+    seqs, acc = [], 0.0
+    for b in range(len(lq)):
+        n = int(min(lq[b], lkv[b]))
+        pairs = n * (n + 1) // 2 if causal else int(lq[b]) * int(lkv[b])
+        w = (4 + (10 if workload_backward(workload) else 0)) * x.D * pairs * x.H
+        if seqs and acc + w > budget:
+            break
+        seqs.append(b)
+        acc += w
+    rows = np.concatenate([np.arange(x.q_off[b], x.q_off[b + 1]) for b in seqs])
+    krows = np.concatenate([np.arange(x.kv_off[b], x.kv_off[b + 1]) for b in seqs])
+    sq = np.concatenate([[0], np.cumsum(lq[seqs])])
+    sk = np.concatenate([[0], np.cumsum(lkv[seqs])])
+    q, k, v = f(x.q[rows]), f(x.k[krows]), f(x.v[krows])
+    bias = None if x.bias is None else x.bias.astype(np.float64)
+    kw = dict(mask=x.mask, act=x.act, bias_kind=x.bias_kind, bias=bias)
+    t0 = time.perf_counter()
+    A.forward(q, k, v, sq, sk, **kw)
+    if workload_backward(workload):
+        A.backward(q, k, v, sq, sk, f(x.do[rows]), **kw)
+    dt = time.perf_counter() - t0
+    fw, bw = useful_flops(sq, sk, x.H, x.D, causal, workload_backward(workload))
+    return {"value": (fw + bw) / dt / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(seqs)} of {len(lq)} sequences (the first ones), all {x.H} heads, "
+                      f"fwd{'+bwd' if workload_backward(workload) else ''}, {dt:.1f} s, numpy float64"}
+
+
+def workload_backward(name: str) -> bool:
+    import jfa_inputs as ji
+    return ji.WORKLOADS[name].backward
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU only "
+              f"(the attention shards by heads or sequences with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import jfa_inputs as ji
+    from jagged_sequence_amd import binding as J
+    from jagged_sequence_amd.flops import useful_flops, visible_pairs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    w = ji.WORKLOADS[args.workload]
+    x = ji.workload_inputs(args.workload)
+    causal = w.mask == "causal"
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    do = dev(x.do) if w.backward else None
+    qo, ko = torch.from_numpy(x.q_off).cuda(), torch.from_numpy(x.kv_off).cuda()
+    bias = torch.from_numpy(x.bias).cuda() if x.bias is not None else None
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    plan = J.Plan(x.q_off, x.kv_off, w.H, w.D, mask=w.mask, act=w.act, bias=w.bias, out_dtype=args.out_dtype,
+                  grad_dtype=args.out_dtype)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    fwd_ws, bwd_ws = plan.workspace_bytes()
+    ws_f = torch.empty(max(fwd_ws, 1), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(max(bwd_ws, 1), dtype=torch.uint8, device="cuda")
+    odt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
+    out = torch.empty((x.q.shape[0], w.H, w.D), dtype=odt, device="cuda")
+    lse = torch.empty((w.H, x.q.shape[0]), dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(out)
+    dk = torch.empty((x.k.shape[0], w.H, w.D), dtype=odt, device="cuda")
+    dv = torch.empty_like(dk)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        plan.forward(q, k, v, qo, ko, bias, out=out, lse=lse, workspace=ws_f, stream=stream)
+        if w.backward:
+            plan.backward(q, k, v, qo, ko, bias, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    plan.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernels = {}
+    for name in J.KERNELS:
+        ms, n = plan.timing_read(name)
+        if n:
+            kernels[name] = {"avg_ms": ms / n, "launches_per_step": n / args.steps, "total_ms": ms}
+    plan.timing_enable(False)
+
+    fw, bw = useful_flops(x.q_off, x.kv_off, w.H, w.D, causal, w.backward)
+    ms_per_step = elapsed / args.steps * 1e3
+    value = (fw + bw) / (elapsed / args.steps) / 1e12
+    pairs = visible_pairs(x.q_off, x.kv_off, causal) * w.H
+
+    # roofline of the dominant kernel (largest share of the timed region)
+    dom = max((kk for kk in kernels if kk in KERNEL_FLOPS_PER_PAIR_D), key=lambda kk: kernels[kk]["total_ms"])
+    per_launch_flops = KERNEL_FLOPS_PER_PAIR_D[dom] * w.D * pairs / kernels[dom]["launches_per_step"]
+    achieved = per_launch_flops / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+    traffic = counter_traffic(dom, args.workload)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom,
+                "algorithmic_flops_per_launch": per_launch_flops}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded jagged lengths and N(0,1) bf16 values; no dataset)",
+        "config": {"workload": args.workload, "B": w.B, "H": w.H, "D": w.D, "mask": w.mask, "act": w.act,
+                   "bias": w.bias, "tokens_q": int(x.q_off[-1]), "tokens_kv": int(x.kv_off[-1]),
+                   "visible_pairs_x_heads": int(pairs), "out_dtype": args.out_dtype, "description": w.description},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "plan_ms": round(plan_ms, 3),
+        "kernels": {kk: {"avg_ms": round(vv["avg_ms"], 5), "per_step": vv["launches_per_step"]}
+                    for kk, vv in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x, args.workload)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,147 @@
+/*
+ * jfa.h — C ABI of the MI355X (gfx950) jagged flash attention library.
+ *
+ * The library computes attention directly on jagged tensors: packed values plus offsets, no
+ * padding (vibekk.com GEM page, FAQ entry on jagged tensors; aihot.vn GEM page, section "Jagged
+ * Sequence Flash Attention", which asks for custom attention bias, asymmetric query vs key/value
+ * lengths and an efficient backward pass). The score activation is either online softmax
+ * (FlashAttention) or a pointwise SiLU / GELU-tanh with the result divided by the sequence's key
+ * count (aihot.vn GEM page, section "Generalized Dot-Product Attention (GDPA)": two matrix
+ * products with a pointwise activation between them in place of softmax). Masking excludes
+ * pairs exactly; on the device it is done by subtracting infinity from the score (kerneldigest.dev
+ * page, section "Arquitectura del Sistema").
+ *
+ * For sequence b with Lq = q_off[b+1]-q_off[b] queries and Lkv = kv_off[b+1]-kv_off[b] keys, head h,
+ * query i < Lq, key j < Lkv:
+ *   s_ij = scale * <q_i, k_j> + beta_h(i, j),  beta = 0 | c_h | T[h][bucket(|i - j|)]
+ *   visible(i, j) = (mask == NONE) || (j <= i)
+ *   softmax: out_i = sum_j P_ij v_j with P the softmax of s_i over visible j; lse_i = ln sum exp
+ *            (a row with no visible key gives out_i = 0 and lse_i = -inf)
+ *   GDPA:    out_i = (1 / Lkv) * sum_{visible j} act(s_ij) v_j,  act = SiLU | GELU (tanh form)
+ *   bucket(d) = d for d < 16, else min(63, 16 + 4 (e - 4) + ((d >> (e - 2)) & 3)), e = floor(log2 d)
+ *
+ * Layouts (all row-major, contiguous, device memory unless named *_host):
+ *   q, out, dout, dq : [Tq,  H, D]   Tq  = q_off[B]
+ *   k, v, dk, dv     : [Tkv, H, D]   Tkv = kv_off[B]
+ *   element type bf16; out may be fp32 (out_dtype), dq/dk/dv may be fp32 (grad_dtype)
+ *   lse              : [H, Tq] fp32 (natural log)
+ *   bias             : fp32 [H] (HEAD_SCALAR) or [H, 64] (REL_BUCKET64)
+ *   offsets          : int32 [B+1], offsets[0] == 0, non-decreasing; empty sequences are legal
+ *   Every tensor pointer must be 16-byte aligned (JFA_ERR_MISALIGNED otherwise).
+ *
+ * Ownership: the caller owns every tensor, both copies of the offsets and the workspace. A plan
+ * owns its host schedule and its device copy of the work lists and frees them in
+ * jfa_plan_destroy. A plan is immutable after jfa_plan and may be used on several streams at
+ * once when each call gets its own workspace. jfa_forward / jfa_backward allocate nothing, never
+ * synchronise the stream, and only enqueue kernels on the stream they are given.
+ *
+ * Errors: every call returns a jfa_status; nothing aborts and no exception crosses the ABI. All
+ * argument checks run before the first launch, so on error no output has been touched.
+ * jfa_last_error() gives a thread-local description of the last failure. A launch failure is
+ * JFA_ERR_HIP; a device fault shows at the caller's next synchronisation.
+ */
+#ifndef JFA_H
+#define JFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* jfa_stream_t; /* a hipStream_t; NULL is the default stream */
+typedef struct jfa_plan_s* jfa_plan_t;     /* opaque; created by jfa_plan, freed by jfa_plan_destroy */
+
+typedef enum {
+  JFA_OK = 0,
+  JFA_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
+  JFA_ERR_BAD_OFFSETS = 2,  /* offsets[0] != 0, decreasing offsets, or a total beyond int32 */
+  JFA_ERR_BAD_SHAPE = 3,    /* B < 1, H < 1, D not 64/128, causal with some Lq != Lkv */
+  JFA_ERR_UNSUPPORTED = 4,  /* enum out of range, or a feature this build does not provide */
+  JFA_ERR_MISALIGNED = 5,   /* a tensor pointer is not 16-byte aligned */
+  JFA_ERR_WORKSPACE = 6,    /* workspace smaller than jfa_workspace_bytes reports */
+  JFA_ERR_HIP = 7,          /* a HIP runtime call or launch failed */
+  JFA_ERR_HOST_ONLY = 8     /* the plan was built with JFA_PLAN_HOST_ONLY and cannot launch */
+} jfa_status;
+
+typedef enum { JFA_MASK_NONE = 0, JFA_MASK_CAUSAL = 1 } jfa_mask;
+typedef enum { JFA_ACT_SOFTMAX = 0, JFA_ACT_SILU = 1, JFA_ACT_GELU_TANH = 2 } jfa_act;
+typedef enum { JFA_BIAS_NONE = 0, JFA_BIAS_HEAD_SCALAR = 1, JFA_BIAS_REL_BUCKET64 = 2 } jfa_bias;
+typedef enum { JFA_BF16 = 0, JFA_F32 = 1 } jfa_dtype;
+
+/* jfa_problem.flags */
+#define JFA_PLAN_HOST_ONLY 0x1u /* build the schedule on the host only: no HIP call, no launches */
+#define JFA_PLAN_NO_SPLIT 0x2u  /* never split a work item into key (or query) ranges */
+
+typedef struct {
+  int32_t num_seqs;               /* B >= 1 */
+  int32_t num_heads;              /* H >= 1 */
+  int32_t head_dim;               /* D in {64, 128} */
+  const int32_t* q_offsets_host;  /* [B+1] host array, read during jfa_plan only */
+  const int32_t* kv_offsets_host; /* [B+1] host array, read during jfa_plan only */
+  int32_t mask;                   /* jfa_mask; causal requires Lq == Lkv for every sequence */
+  int32_t act;                    /* jfa_act */
+  int32_t bias;                   /* jfa_bias */
+  float scale;                    /* score scale; 0 means 1/sqrt(D) */
+  int32_t out_dtype;              /* jfa_dtype of out */
+  int32_t grad_dtype;             /* jfa_dtype of dq, dk, dv */
+  int32_t num_slots;              /* concurrent workgroups the split rule balances for; 0: from the device
+                                     (CUs x resident workgroups), or 512 for a host-only plan */
+  uint32_t flags;                 /* JFA_PLAN_* */
+} jfa_problem;
+
+/* Validate the problem, build the longest-first work lists (jagged tile scheduler) and, unless
+ * JFA_PLAN_HOST_ONLY, upload them to device memory with an asynchronous copy on `stream`. */
+jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t* plan_out);
+
+/* Device bytes of workspace each pass needs (0 when nothing is split and no scratch is used).
+ * Either pointer may be NULL. */
+jfa_status jfa_workspace_bytes(jfa_plan_t plan, size_t* fwd_bytes, size_t* bwd_bytes);
+
+/* Forward pass. `bias` may be NULL only without bias; `lse` may be NULL only for GDPA (it is
+ * not defined there). `q_offsets` / `kv_offsets` are device copies equal to the host offsets
+ * given to jfa_plan. `workspace` may be NULL when its size is 0. */
+jfa_status jfa_forward(jfa_plan_t plan, const void* q, const void* k, const void* v,
+                       const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias,
+                       void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       jfa_stream_t stream);
+
+/* Backward pass: gradients of <out, dout> with respect to q, k and v. `out` and `lse` are the
+ * forward results (softmax only; they may be NULL for GDPA). `dbias` must be NULL: the bias
+ * gradient is not provided by this build (JFA_ERR_UNSUPPORTED otherwise). */
+jfa_status jfa_backward(jfa_plan_t plan, const void* q, const void* k, const void* v,
+                        const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias,
+                        const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                        void* dv, float* dbias, void* workspace, size_t workspace_bytes,
+                        jfa_stream_t stream);
+
+/* Work lists, for inspection and tests. `which`: 0 forward items, 1 forward split groups,
+ * 2 dQ items, 3 dQ split groups, 4 dK/dV items, 5 dK/dV split groups. Items are 6 int32 each
+ * (b, h, tile, lo, hi, slot): query-tile lists own query tile `tile` and cover key tiles
+ * [lo, hi); the dK/dV list owns key tile `tile` and covers query tiles [lo, hi); slot is the
+ * partial-result slot of a split piece or -1. Groups are 5 int32 each (b, h, tile, slot0, R).
+ * Writes min(count, cap) records and sets *count to the total number of records. */
+jfa_status jfa_plan_schedule(jfa_plan_t plan, int32_t which, int32_t* out, size_t cap, size_t* count);
+
+/* Tile geometry and slot counts the plan used: writes up to `n` of
+ * {fwd BM, fwd BN, dq BM, dq BN, dkdv BM, dkdv BN, fwd slots, dq slots, dkdv slots}. */
+jfa_status jfa_plan_info(jfa_plan_t plan, int32_t* info, size_t n);
+
+/* Per-kernel timing with HIP events recorded around every launch of this plan (for
+ * measurement; adds two event records per launch while on). Kernel ids: 0 forward,
+ * 1 forward combine, 2 backward preprocess, 3 dK/dV, 4 dQ, 5 backward partial reduce.
+ * jfa_timing_read waits for the recorded events and returns their summed time and count;
+ * jfa_timing_enable(plan, 1) also clears previous records. Not thread safe. */
+jfa_status jfa_timing_enable(jfa_plan_t plan, int32_t enable);
+jfa_status jfa_timing_read(jfa_plan_t plan, int32_t kernel, float* total_ms, int32_t* launches);
+
+void jfa_plan_destroy(jfa_plan_t plan);
+const char* jfa_status_string(jfa_status status);
+const char* jfa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JFA_H */

@@ -1,0 +1,225 @@
+"""ctypes binding of ``libjfa.so`` (the C ABI in include/jfa.h).
+
+Argument marshalling only: every step of the attention path runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream. If the library is missing or cannot be
+loaded, importing the binding raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libjfa.so")
+
+JFA_OK = 0
+STATUS_NAMES = {0: "JFA_OK", 1: "JFA_ERR_NULL_ARG", 2: "JFA_ERR_BAD_OFFSETS", 3: "JFA_ERR_BAD_SHAPE",
+                4: "JFA_ERR_UNSUPPORTED", 5: "JFA_ERR_MISALIGNED", 6: "JFA_ERR_WORKSPACE", 7: "JFA_ERR_HIP",
+                8: "JFA_ERR_HOST_ONLY"}
+MASKS = {"none": 0, "causal": 1}
+ACTS = {"softmax": 0, "silu": 1, "gelu_tanh": 2}
+BIASES = {"none": 0, "scalar": 1, "bucket": 2}
+DTYPES = {"bf16": 0, "f32": 1}
+PLAN_HOST_ONLY = 0x1
+PLAN_NO_SPLIT = 0x2
+KERNELS = {"forward": 0, "combine": 1, "preprocess": 2, "dkdv": 3, "dq": 4, "reduce": 5}
+SYMBOLS = ["jfa_plan", "jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_plan_schedule", "jfa_plan_info",
+           "jfa_timing_enable", "jfa_timing_read", "jfa_plan_destroy", "jfa_status_string", "jfa_last_error"]
+
+
+class JfaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("q_offsets_host", ctypes.POINTER(ctypes.c_int32)), ("kv_offsets_host", ctypes.POINTER(ctypes.c_int32)),
+                ("mask", ctypes.c_int32), ("act", ctypes.c_int32), ("bias", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("out_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32), ("num_slots", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m jagged_sequence_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int
+    lib.jfa_plan.argtypes = [ctypes.POINTER(Problem), vp, ctypes.POINTER(vp)]
+    lib.jfa_workspace_bytes.argtypes = [vp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.jfa_forward.argtypes = [vp] * 9 + [vp, sz, vp]
+    lib.jfa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.jfa_plan_schedule.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int32), sz, ctypes.POINTER(sz)]
+    lib.jfa_plan_info.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), sz]
+    lib.jfa_timing_enable.argtypes = [vp, i32]
+    lib.jfa_timing_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
+    lib.jfa_plan_destroy.argtypes = [vp]
+    lib.jfa_plan_destroy.restype = None
+    lib.jfa_status_string.argtypes = [st]
+    lib.jfa_status_string.restype = ctypes.c_char_p
+    lib.jfa_last_error.argtypes = []
+    lib.jfa_last_error.restype = ctypes.c_char_p
+    for name in ["jfa_plan", "jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_plan_schedule",
+                 "jfa_plan_info", "jfa_timing_enable", "jfa_timing_read"]:
+        getattr(lib, name).restype = st
+    return lib
+
+
+LIB = _load()
+
+
+def _check(status: int):
+    if status != JFA_OK:
+        raise JfaError(status, LIB.jfa_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a torch tensor (or None)."""
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _i32(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+class Plan:
+    """A jagged attention plan: validated problem plus longest-first work lists on the device."""
+
+    def __init__(self, q_offsets, kv_offsets, num_heads: int, head_dim: int, *, mask: str = "none",
+                 act: str = "softmax", bias: str = "none", scale: float = 0.0, out_dtype: str = "bf16",
+                 grad_dtype: str = "bf16", num_slots: int = 0, host_only: bool = False, no_split: bool = False,
+                 stream=None):
+        self._q_off = _i32(q_offsets)
+        self._kv_off = _i32(kv_offsets)
+        self.B = len(self._q_off) - 1
+        self.H, self.D = int(num_heads), int(head_dim)
+        self.mask, self.act, self.bias_kind = mask, act, bias
+        self.out_dtype, self.grad_dtype = out_dtype, grad_dtype
+        self.Tq = int(self._q_off[-1]) if self.B >= 0 and len(self._q_off) else 0
+        self.Tkv = int(self._kv_off[-1]) if len(self._kv_off) else 0
+        p = Problem()
+        p.num_seqs = self.B
+        p.num_heads = self.H
+        p.head_dim = self.D
+        p.q_offsets_host = self._q_off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        p.kv_offsets_host = self._kv_off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        p.mask = MASKS[mask]
+        p.act = ACTS[act]
+        p.bias = BIASES[bias]
+        p.scale = float(scale)
+        p.out_dtype = DTYPES[out_dtype]
+        p.grad_dtype = DTYPES[grad_dtype]
+        p.num_slots = int(num_slots)
+        p.flags = (PLAN_HOST_ONLY if host_only else 0) | (PLAN_NO_SPLIT if no_split else 0)
+        handle = ctypes.c_void_p()
+        s = None if host_only else _stream_handle(stream)
+        _check(LIB.jfa_plan(ctypes.byref(p), s, ctypes.byref(handle)))
+        self._h = handle
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            LIB.jfa_plan_destroy(h)
+            self._h = None
+
+    # ------------------------------------------------------------------ inspection
+    def workspace_bytes(self) -> tuple[int, int]:
+        f, b = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(LIB.jfa_workspace_bytes(self._h, ctypes.byref(f), ctypes.byref(b)))
+        return f.value, b.value
+
+    def schedule(self, which: int) -> np.ndarray:
+        n = ctypes.c_size_t()
+        _check(LIB.jfa_plan_schedule(self._h, which, None, 0, ctypes.byref(n)))
+        per = 5 if which & 1 else 6
+        out = np.zeros(n.value * per, dtype=np.int32)
+        _check(LIB.jfa_plan_schedule(self._h, which, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value,
+                                     ctypes.byref(n)))
+        return out.reshape(n.value, per)
+
+    def info(self) -> dict:
+        buf = (ctypes.c_int32 * 9)()
+        _check(LIB.jfa_plan_info(self._h, buf, 9))
+        keys = ["fwd_bm", "fwd_bn", "dq_bm", "dq_bn", "kv_bm", "kv_bn", "fwd_slots", "dq_slots", "kv_slots"]
+        return dict(zip(keys, list(buf)))
+
+    def timing_enable(self, on: bool = True):
+        _check(LIB.jfa_timing_enable(self._h, 1 if on else 0))
+
+    def timing_read(self, kernel: str) -> tuple[float, int]:
+        ms, n = ctypes.c_float(), ctypes.c_int32()
+        _check(LIB.jfa_timing_read(self._h, KERNELS[kernel], ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
+
+    # ------------------------------------------------------------------ compute
+    def _workspace(self, nbytes: int, ws):
+        import torch
+        if nbytes == 0:
+            return None
+        if ws is None:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        return ws
+
+    def forward(self, q, k, v, q_offsets, kv_offsets, bias=None, out=None, lse=None, workspace=None, stream=None):
+        """Forward pass; returns (out, lse). Tensors are torch device tensors in the ABI layouts."""
+        import torch
+        if out is None:
+            out = torch.empty((self.Tq, self.H, self.D), device=q.device,
+                              dtype=torch.float32 if self.out_dtype == "f32" else torch.bfloat16)
+        if lse is None and self.act == "softmax":
+            lse = torch.empty((self.H, self.Tq), device=q.device, dtype=torch.float32)
+        fwd_bytes, _ = self.workspace_bytes()
+        ws = self._workspace(fwd_bytes, workspace)
+        _check(LIB.jfa_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias),
+                               _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                               _stream_handle(stream)))
+        return out, lse
+
+    def backward(self, q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq=None, dk=None, dv=None,
+                 workspace=None, stream=None):
+        """Backward pass; returns (dq, dk, dv)."""
+        import torch
+        gdt = torch.float32 if self.grad_dtype == "f32" else torch.bfloat16
+        if dq is None:
+            dq = torch.empty((self.Tq, self.H, self.D), device=q.device, dtype=gdt)
+        if dk is None:
+            dk = torch.empty((self.Tkv, self.H, self.D), device=q.device, dtype=gdt)
+        if dv is None:
+            dv = torch.empty((self.Tkv, self.H, self.D), device=q.device, dtype=gdt)
+        _, bwd_bytes = self.workspace_bytes()
+        ws = self._workspace(bwd_bytes, workspace)
+        _check(LIB.jfa_backward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias),
+                                _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), None, _ptr(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(), _stream_handle(stream)))
+        return dq, dk, dv
+
+
+# ---------------------------------------------------------------------- C-named entry points
+def jfa_plan(q_offsets, kv_offsets, num_heads: int, head_dim: int, **kw) -> Plan:
+    """``jfa_plan``: validate the problem and build the device work lists (see :class:`Plan`)."""
+    return Plan(q_offsets, kv_offsets, num_heads, head_dim, **kw)
+
+
+def jfa_forward(plan: Plan, q, k, v, q_offsets, kv_offsets, bias=None, out=None, lse=None, workspace=None,
+                stream=None):
+    """``jfa_forward``: returns (out, lse)."""
+    return plan.forward(q, k, v, q_offsets, kv_offsets, bias, out, lse, workspace, stream)
+
+
+def jfa_backward(plan: Plan, q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq=None, dk=None, dv=None,
+                 workspace=None, stream=None):
+    """``jfa_backward``: returns (dq, dk, dv)."""
+    return plan.backward(q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq, dk, dv, workspace, stream)

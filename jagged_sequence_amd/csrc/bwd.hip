@@ -1,0 +1,585 @@
+// Backward pass of jagged attention on gfx950 (aihot.vn GEM page, "Jagged Sequence Flash
+// Attention": efficient backward passes; kerneldigest.dev page, "Arquitectura del Sistema":
+// backward-pass parallelisation). Two independent kernels, neither uses atomics:
+//   dK/dV: one workgroup per (sequence, head, 128-key tile), looping over 64-query tiles;
+//   dQ:    one workgroup per (sequence, head, 128-query tile), looping over 64-key tiles.
+// Both recompute the scores from Q, K and the forward log-sum-exp. Split items write fp32
+// partials that a fixed-order reduce sums, so results do not depend on scheduling.
+//
+// Gradients (per visible pair, s = scale <q_i, k_j> + bias):
+//   softmax: P = exp(s - lse_i), dP = <dO_i, v_j>, dS = P (dP - Delta_i), Delta_i = <dO_i, O_i>
+//   GDPA:    P = act(s) / Lkv,   dP = <dO_i, v_j>, dS = dP act'(s) / Lkv
+//   dV_j += P dO_i,  dK_j += scale dS q_i,  dQ_i += scale dS k_j
+#include "device_common.h"
+
+namespace jfa {
+namespace {
+
+// ---------------------------------------------------------------- Delta_i = <dO_i, O_i>
+template <int D>
+__global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdArgs a) {
+  constexpr int TPR = D / 8;  // threads per (token, head) row, 8 elements each
+  const int rows = a.Tq * a.H;
+  const int row = blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float acc = 0.0f;
+  if (row < rows) {
+    const size_t base = (size_t)row * D + part * 8;
+    uint4 g = load16(a.dout + base);
+    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+    float o[8];
+    if (a.out_f32) {
+      const float* op = reinterpret_cast<const float*>(a.out) + base;
+      float4 x0 = *reinterpret_cast<const float4*>(op), x1 = *reinterpret_cast<const float4*>(op + 4);
+      o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w; o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
+    } else {
+      uint4 x = load16(reinterpret_cast<const uint16_t*>(a.out) + base);
+      const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] = __builtin_bit_cast(float, xw[j] << 16);
+        o[2 * j + 1] = __builtin_bit_cast(float, xw[j] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc += __builtin_bit_cast(float, gw[j] << 16) * o[2 * j];
+      acc += __builtin_bit_cast(float, gw[j] & 0xffff0000u) * o[2 * j + 1];
+    }
+  }
+#pragma unroll
+  for (int w = TPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
+  if (row < rows && part == 0) {
+    const int tok = row / a.H, h = row % a.H;
+    a.delta[(size_t)h * a.Tq + tok] = acc;
+  }
+}
+
+// 4 rows x 8 dims of a [T, H, D] tensor: loaded so that one thread can store them both row-major
+// (4 x 16 bytes) and transposed (8 x 8 bytes).
+template <int D, int ROWS>
+struct Units {
+  static constexpr int CPR = D / 8;
+  static constexpr int N = (ROWS / 4) * CPR;
+  uint4 r[4];
+};
+
+template <int D, int ROWS>
+__device__ __forceinline__ void load_units(Units<D, ROWS>& u, const uint16_t* base, int rs, int row0, int limit,
+                                           int tid) {
+  constexpr int CPR = D / 8, N = Units<D, ROWS>::N;
+  if (N >= kThreads || tid < N) {
+    const int dg = tid % CPR, g = tid / CPR;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = row0 + 4 * g + j;
+      u.r[j] = row < limit ? load16(base + (size_t)row * rs + dg * 8) : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+template <int D, int ROWS>
+__device__ __forceinline__ void store_units(const Units<D, ROWS>& u, __bf16* rowmajor, int RS, __bf16* trans, int TS,
+                                            int tid) {
+  constexpr int CPR = D / 8, N = Units<D, ROWS>::N;
+  if (N >= kThreads || tid < N) {
+    const int dg = tid % CPR, g = tid / CPR;
+    if (rowmajor) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&rowmajor[(4 * g + j) * RS + dg * 8]) = u.r[j];
+    }
+    if (trans) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2*>(&trans[(dg * 8 + e) * TS + 4 * g]) = column4(u.r, e);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dQ, query-tile parallel
+template <int D>
+struct alignas(16) DqSmem {
+  static constexpr int RS = D + 8, TS = kDqBN + 8;
+  __bf16 k[kDqBN * RS];
+  __bf16 kt[D * TS];
+  __bf16 v[kDqBN * RS];
+  float tab[kBuckets];
+};
+
+template <int D, int ACT, int BIAS, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdArgs a) {
+  constexpr int BM = kDqBM, BN = kDqBN, NKB = D / 16, NDB = D / 32;
+  constexpr int RS = DqSmem<D>::RS, TS = DqSmem<D>::TS;
+  constexpr bool SOFTMAX = ACT == kSoftmax;
+  __shared__ DqSmem<D> sm;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int32_t* it = a.dq_items + (size_t)blockIdx.x * kItemInts;
+  const int b = it[0], h = it[1], t = it[2], k0 = it[3], k1 = it[4], slot = it[5];
+  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
+  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const int rs = a.H * D;
+  const int row0 = t * BM + wave * 32;
+  const int qi = row0 + l32;
+
+  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid] * (SOFTMAX ? kLog2e : 1.0f);
+  const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
+
+  bf16x8 qf[NKB], df[NKB];
+  {
+    const size_t off = (size_t)(qs + qi) * rs + h * D + hh * 8;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      uint4 w = qi < Lq ? load16(a.q + off + kb * 16) : make_uint4(0, 0, 0, 0);
+      uint4 g = qi < Lq ? load16(a.dout + off + kb * 16) : make_uint4(0, 0, 0, 0);
+      qf[kb] = __builtin_bit_cast(bf16x8, w);
+      df[kb] = __builtin_bit_cast(bf16x8, g);
+    }
+  }
+  float lse2 = __builtin_huge_valf(), dlt = 0.0f;
+  if (SOFTMAX && qi < Lq) {
+    const float l = a.lse[(size_t)h * a.Tq + qs + qi];
+    lse2 = l == kNegInf ? __builtin_huge_valf() : (l - (BIAS == kBiasScalar ? bias_c : 0.0f)) * kLog2e;
+    dlt = a.delta[(size_t)h * a.Tq + qs + qi];
+  }
+  const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
+  const float invL = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
+
+  f32x16 qacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) qacc[db] = f32x16{};
+
+  const uint16_t* kbase = a.k + (size_t)ks * rs + h * D;
+  const uint16_t* vbase = a.v + (size_t)ks * rs + h * D;
+  Units<D, kDqBN> uk, uv;
+  if (k0 < k1) {
+    load_units<D, kDqBN>(uk, kbase, rs, k0 * BN, Lkv, tid);
+    load_units<D, kDqBN>(uv, vbase, rs, k0 * BN, Lkv, tid);
+  }
+  for (int kt = k0; kt < k1; ++kt) {
+    __syncthreads();
+    store_units<D, kDqBN>(uk, sm.k, RS, sm.kt, TS, tid);
+    store_units<D, kDqBN>(uv, sm.v, RS, nullptr, 0, tid);
+    __syncthreads();
+    if (kt + 1 < k1) {
+      load_units<D, kDqBN>(uk, kbase, rs, (kt + 1) * BN, Lkv, tid);
+      load_units<D, kDqBN>(uv, vbase, rs, (kt + 1) * BN, Lkv, tid);
+    }
+    const int key0 = kt * BN;
+
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      sacc[sb] = f32x16{};
+      pacc[sb] = f32x16{};
+      const __bf16* kr = &sm.k[(32 * sb + kappa(l32)) * RS + hh * 8];
+      const __bf16* vr = &sm.v[(32 * sb + kappa(l32)) * RS + hh * 8];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        sacc[sb] = mfma32(lds_load8(kr + kb * 16), qf[kb], sacc[sb]);
+        pacc[sb] = mfma32(lds_load8(vr + kb * 16), df[kb], pacc[sb]);
+      }
+    }
+
+    const bool need_mask = (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
+    float ds[2][16];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * sb + acc_row(r, hh);
+        float x = sacc[sb][r] * smul;
+        if (BIAS == kBiasBucket) x += sm.tab[rel_bucket(qi - key)];
+        if (BIAS == kBiasScalar && !SOFTMAX) x += bias_c;
+        const bool masked = need_mask && (key >= Lkv || (CAUSAL && key > qi));
+        float d;
+        if (SOFTMAX) {
+          const float p = fast_exp2(x - lse2);
+          d = p * (pacc[sb][r] - dlt);
+        } else {
+          float f, g;
+          act_fwd_grad<ACT>(x, f, g);
+          d = pacc[sb][r] * g * invL;
+        }
+        ds[sb][r] = masked ? 0.0f : d;
+      }
+    }
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dsb[c] = pack8(&ds[c >> 1][8 * (c & 1)]);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const __bf16* kr = &sm.kt[(32 * db + l32) * TS + 8 * hh];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qacc[db] = mfma32(lds_load8(kr + 16 * c), dsb[c], qacc[db]);
+    }
+  }
+
+  if (slot < 0) {
+    if (qi < Lq) {
+      const size_t base = ((size_t)(qs + qi) * a.H + h) * D;
+      const float sc = a.scale;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(a.dq, base + 32 * db + 8 * g + 4 * hh, qacc[db][4 * g] * sc, qacc[db][4 * g + 1] * sc,
+                 qacc[db][4 * g + 2] * sc, qacc[db][4 * g + 3] * sc, a.grad_f32);
+    }
+  } else {
+    float* po = a.part_dq + ((size_t)slot * BM + wave * 32 + l32) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * g + 4 * hh) =
+            make_float4(qacc[db][4 * g], qacc[db][4 * g + 1], qacc[db][4 * g + 2], qacc[db][4 * g + 3]);
+  }
+}
+
+// ---------------------------------------------------------------- dK/dV, key-tile parallel
+template <int D>
+struct alignas(16) KvSmem {
+  static constexpr int RS = D + 8, TS = kKvBM + 8;
+  __bf16 q[kKvBM * RS];
+  __bf16 qt[D * TS];
+  __bf16 g[kKvBM * RS];
+  __bf16 gt[D * TS];
+  float lse2[kKvBM];
+  float dlt[kKvBM];
+  float tab[kBuckets];
+};
+
+template <int D, int ACT, int BIAS, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int BM = kKvBM, BN = kKvBN, NKB = D / 16, NDB = D / 32;
+  constexpr int RS = KvSmem<D>::RS, TS = KvSmem<D>::TS;
+  constexpr bool SOFTMAX = ACT == kSoftmax;
+  __shared__ KvSmem<D> sm;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int32_t* it = a.kv_items + (size_t)blockIdx.x * kItemInts;
+  const int b = it[0], h = it[1], kt = it[2], q0 = it[3], q1 = it[4], slot = it[5];
+  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
+  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const int rs = a.H * D;
+  const int key_w = kt * BN + wave * 32;  // first key of this wave
+  const int kj = key_w + l32;
+
+  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid] * (SOFTMAX ? kLog2e : 1.0f);
+  const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
+
+  bf16x8 kf[NKB], vf[NKB];
+  {
+    const size_t off = (size_t)(ks + kj) * rs + h * D + hh * 8;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      uint4 w = kj < Lkv ? load16(a.k + off + kb * 16) : make_uint4(0, 0, 0, 0);
+      uint4 x = kj < Lkv ? load16(a.v + off + kb * 16) : make_uint4(0, 0, 0, 0);
+      kf[kb] = __builtin_bit_cast(bf16x8, w);
+      vf[kb] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
+  const float invL = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
+  const float lse_shift = (SOFTMAX && BIAS == kBiasScalar) ? bias_c : 0.0f;
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  const uint16_t* qbase = a.q + (size_t)qs * rs + h * D;
+  const uint16_t* gbase = a.dout + (size_t)qs * rs + h * D;
+  Units<D, kKvBM> uq, ug;
+  float pl = 0.0f, pd = 0.0f;
+  auto load_stats = [&](int qt) {
+    if (SOFTMAX && tid < BM) {
+      const int q = qt * BM + tid;
+      pl = __builtin_huge_valf();
+      pd = 0.0f;
+      if (q < Lq) {
+        const float l = a.lse[(size_t)h * a.Tq + qs + q];
+        pl = l == kNegInf ? __builtin_huge_valf() : (l - lse_shift) * kLog2e;
+        pd = a.delta[(size_t)h * a.Tq + qs + q];
+      }
+    }
+  };
+  if (q0 < q1) {
+    load_units<D, kKvBM>(uq, qbase, rs, q0 * BM, Lq, tid);
+    load_units<D, kKvBM>(ug, gbase, rs, q0 * BM, Lq, tid);
+    load_stats(q0);
+  }
+  for (int qt = q0; qt < q1; ++qt) {
+    __syncthreads();
+    store_units<D, kKvBM>(uq, sm.q, RS, sm.qt, TS, tid);
+    store_units<D, kKvBM>(ug, sm.g, RS, sm.gt, TS, tid);
+    if (SOFTMAX && tid < BM) {
+      sm.lse2[tid] = pl;
+      sm.dlt[tid] = pd;
+    }
+    __syncthreads();
+    if (qt + 1 < q1) {
+      load_units<D, kKvBM>(uq, qbase, rs, (qt + 1) * BM, Lq, tid);
+      load_units<D, kKvBM>(ug, gbase, rs, (qt + 1) * BM, Lq, tid);
+      load_stats(qt + 1);
+    }
+    const int qrow0 = qt * BM;
+
+    // S = Q K^T and dP = dO V^T for 64 queries x this wave's 32 keys: lane column = key kj,
+    // register r of block qb = query qrow0 + 32 qb + acc_row(r, hh).
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      sacc[qb] = f32x16{};
+      pacc[qb] = f32x16{};
+      const __bf16* qr = &sm.q[(32 * qb + kappa(l32)) * RS + hh * 8];
+      const __bf16* gr = &sm.g[(32 * qb + kappa(l32)) * RS + hh * 8];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        sacc[qb] = mfma32(lds_load8(qr + kb * 16), kf[kb], sacc[qb]);
+        pacc[qb] = mfma32(lds_load8(gr + kb * 16), vf[kb], pacc[qb]);
+      }
+    }
+
+    const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0);
+    float p[2][16], ds[2][16];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int c8 = 0; c8 < 2; ++c8) {
+        const int rbase = 32 * qb + 16 * c8 + 8 * hh;  // 8 consecutive query rows of this lane
+        float l8[8], d8[8];
+        if (SOFTMAX) {
+          float4 x0 = *reinterpret_cast<const float4*>(&sm.lse2[rbase]);
+          float4 x1 = *reinterpret_cast<const float4*>(&sm.lse2[rbase + 4]);
+          float4 y0 = *reinterpret_cast<const float4*>(&sm.dlt[rbase]);
+          float4 y1 = *reinterpret_cast<const float4*>(&sm.dlt[rbase + 4]);
+          l8[0] = x0.x; l8[1] = x0.y; l8[2] = x0.z; l8[3] = x0.w; l8[4] = x1.x; l8[5] = x1.y; l8[6] = x1.z; l8[7] = x1.w;
+          d8[0] = y0.x; d8[1] = y0.y; d8[2] = y0.z; d8[3] = y0.w; d8[4] = y1.x; d8[5] = y1.y; d8[6] = y1.z; d8[7] = y1.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = 8 * c8 + j;
+          const int qi = qrow0 + rbase + j;
+          float x = sacc[qb][r] * smul;
+          if (BIAS == kBiasBucket) x += sm.tab[rel_bucket(qi - kj)];
+          if (BIAS == kBiasScalar && !SOFTMAX) x += bias_c;
+          const bool masked = (need_mask && (kj >= Lkv || (CAUSAL && kj > qi))) || (!SOFTMAX && qi >= Lq);
+          float pv, dv_;
+          if (SOFTMAX) {
+            pv = fast_exp2(x - l8[j]);
+            dv_ = pv * (pacc[qb][r] - d8[j]);
+          } else {
+            float f, g;
+            act_fwd_grad<ACT>(x, f, g);
+            pv = f * invL;
+            dv_ = pacc[qb][r] * g * invL;
+          }
+          p[qb][r] = masked ? 0.0f : pv;
+          ds[qb][r] = masked ? 0.0f : dv_;
+        }
+      }
+    }
+    bf16x8 pb[4], dsb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      pb[c] = pack8(&p[c >> 1][8 * (c & 1)]);
+      dsb[c] = pack8(&ds[c >> 1][8 * (c & 1)]);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const __bf16* gr = &sm.gt[(32 * db + l32) * TS + 8 * hh];
+      const __bf16* qr = &sm.qt[(32 * db + l32) * TS + 8 * hh];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        dv[db] = mfma32(lds_load8(gr + 16 * c), pb[c], dv[db]);
+        dk[db] = mfma32(lds_load8(qr + 16 * c), dsb[c], dk[db]);
+      }
+    }
+  }
+
+  // Accumulator register r of d-block db: dimension 32 db + 8 (r/4) + 4 hh + r%4, key kj.
+  if (slot < 0) {
+    if (kj < Lkv) {
+      const size_t base = ((size_t)(ks + kj) * a.H + h) * D;
+      const float sc = a.scale;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const size_t i = base + 32 * db + 8 * g + 4 * hh;
+          store4(a.dk, i, dk[db][4 * g] * sc, dk[db][4 * g + 1] * sc, dk[db][4 * g + 2] * sc, dk[db][4 * g + 3] * sc,
+                 a.grad_f32);
+          store4(a.dv, i, dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3], a.grad_f32);
+        }
+    }
+  } else {
+    const size_t prow = (size_t)slot * BN + wave * 32 + l32;
+    float* pk = a.part_dk + prow * D;
+    float* pv = a.part_dv + prow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i = 32 * db + 8 * g + 4 * hh;
+        *reinterpret_cast<float4*>(pk + i) = make_float4(dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]);
+        *reinterpret_cast<float4*>(pv + i) = make_float4(dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------- fixed-order partial sums
+// One workgroup per split group (b, h, tile, slot0, R); 2 threads per row, D/2 columns each.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce_dq_kernel(BwdArgs a) {
+  constexpr int BM = kDqBM, HALF = D / 2;
+  const int32_t* g = a.dq_groups + (size_t)blockIdx.x * kGroupInts;
+  const int b = g[0], h = g[1], t = g[2], slot0 = g[3], R = g[4];
+  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
+  const int row = threadIdx.x >> 1, part = threadIdx.x & 1;
+  const int qi = t * BM + row;
+  if (qi >= Lq) return;
+  float acc[HALF];
+#pragma unroll
+  for (int d = 0; d < HALF; ++d) acc[d] = 0.0f;
+  for (int r = 0; r < R; ++r) {
+    const float* p = a.part_dq + ((size_t)(slot0 + r) * BM + row) * D + part * HALF;
+#pragma unroll
+    for (int d = 0; d < HALF; d += 4) {
+      float4 x = *reinterpret_cast<const float4*>(p + d);
+      acc[d] += x.x; acc[d + 1] += x.y; acc[d + 2] += x.z; acc[d + 3] += x.w;
+    }
+  }
+  const size_t base = ((size_t)(qs + qi) * a.H + h) * D + part * HALF;
+  const float sc = a.scale;
+#pragma unroll
+  for (int d = 0; d < HALF; d += 4)
+    store4(a.dq, base + d, acc[d] * sc, acc[d + 1] * sc, acc[d + 2] * sc, acc[d + 3] * sc, a.grad_f32);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce_dkdv_kernel(BwdArgs a) {
+  constexpr int BN = kKvBN, HALF = D / 2;
+  const int32_t* g = a.kv_groups + (size_t)blockIdx.x * kGroupInts;
+  const int b = g[0], h = g[1], kt = g[2], slot0 = g[3], R = g[4];
+  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const int row = threadIdx.x >> 1, part = threadIdx.x & 1;
+  const int kj = kt * BN + row;
+  if (kj >= Lkv) return;
+  for (int which = 0; which < 2; ++which) {
+    const float* src = which == 0 ? a.part_dk : a.part_dv;
+    float acc[HALF];
+#pragma unroll
+    for (int d = 0; d < HALF; ++d) acc[d] = 0.0f;
+    for (int r = 0; r < R; ++r) {
+      const float* p = src + ((size_t)(slot0 + r) * BN + row) * D + part * HALF;
+#pragma unroll
+      for (int d = 0; d < HALF; d += 4) {
+        float4 x = *reinterpret_cast<const float4*>(p + d);
+        acc[d] += x.x; acc[d + 1] += x.y; acc[d + 2] += x.z; acc[d + 3] += x.w;
+      }
+    }
+    const size_t base = ((size_t)(ks + kj) * a.H + h) * D + part * HALF;
+    const float sc = which == 0 ? a.scale : 1.0f;
+    void* dst = which == 0 ? a.dk : a.dv;
+#pragma unroll
+    for (int d = 0; d < HALF; d += 4)
+      store4(dst, base + d, acc[d] * sc, acc[d + 1] * sc, acc[d + 2] * sc, acc[d + 3] * sc, a.grad_f32);
+  }
+}
+
+// ---------------------------------------------------------------- dispatch
+
+#define JFA_DISPATCH_MODES(KERNEL, m, n, s, a)                                                          \
+  [&]() -> hipError_t {                                                                                 \
+    auto go = [&](auto kern) {                                                                          \
+      hipLaunchKernelGGL(kern, dim3(n), dim3(kThreads), 0, s, a);                                       \
+      return hipGetLastError();                                                                         \
+    };                                                                                                  \
+    if (m.D == 64) {                                                                                    \
+      JFA_DISPATCH_ACT(KERNEL, 64, m, go)                                                               \
+    } else {                                                                                            \
+      JFA_DISPATCH_ACT(KERNEL, 128, m, go)                                                              \
+    }                                                                                                   \
+  }()
+
+#define JFA_DISPATCH_ACT(KERNEL, DD, m, go)                                                             \
+  switch (m.act) {                                                                                      \
+    case kSoftmax: JFA_DISPATCH_BIAS(KERNEL, DD, kSoftmax, m, go)                                       \
+    case kSilu: JFA_DISPATCH_BIAS(KERNEL, DD, kSilu, m, go)                                             \
+    default: JFA_DISPATCH_BIAS(KERNEL, DD, kGeluTanh, m, go)                                            \
+  }
+
+#define JFA_DISPATCH_BIAS(KERNEL, DD, AA, m, go)                                                        \
+  switch (m.bias) {                                                                                     \
+    case kBiasNone:                                                                                     \
+      return m.causal ? go(KERNEL<DD, AA, kBiasNone, true>) : go(KERNEL<DD, AA, kBiasNone, false>);     \
+    case kBiasScalar:                                                                                   \
+      return m.causal ? go(KERNEL<DD, AA, kBiasScalar, true>) : go(KERNEL<DD, AA, kBiasScalar, false>); \
+    default:                                                                                            \
+      return m.causal ? go(KERNEL<DD, AA, kBiasBucket, true>) : go(KERNEL<DD, AA, kBiasBucket, false>); \
+  }
+
+}  // namespace
+
+hipError_t launch_bwd_preprocess(const BwdArgs& a, const Modes& m, hipStream_t s) {
+  const long rows = (long)a.Tq * a.H;
+  if (rows <= 0) return hipSuccess;
+  const int per_block = kThreads / (m.D / 8);
+  const int grid = (int)((rows + per_block - 1) / per_block);
+  if (m.D == 64)
+    hipLaunchKernelGGL(bwd_preprocess_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_preprocess_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  return JFA_DISPATCH_MODES(bwd_dq_kernel, m, n, s, a);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  return JFA_DISPATCH_MODES(bwd_dkdv_kernel, m, n, s, a);
+}
+
+hipError_t launch_bwd_reduce_dq(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (m.D == 64)
+    hipLaunchKernelGGL(bwd_reduce_dq_kernel<64>, dim3(n), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_reduce_dq_kernel<128>, dim3(n), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce_dkdv(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (m.D == 64)
+    hipLaunchKernelGGL(bwd_reduce_dkdv_kernel<64>, dim3(n), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_reduce_dkdv_kernel<128>, dim3(n), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+int occupancy_dq(const Modes& m) {
+  int n = 0;
+  hipError_t e = m.D == 64
+                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dq_kernel<64, kSoftmax, kBiasBucket, true>, kThreads, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dq_kernel<128, kSoftmax, kBiasBucket, true>, kThreads, 0);
+  return (e == hipSuccess && n > 0) ? n : 1;
+}
+
+int occupancy_dkdv(const Modes& m) {
+  int n = 0;
+  hipError_t e = m.D == 64
+                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dkdv_kernel<64, kSoftmax, kBiasBucket, true>, kThreads, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dkdv_kernel<128, kSoftmax, kBiasBucket, true>, kThreads, 0);
+  return (e == hipSuccess && n > 0) ? n : 1;
+}
+
+}  // namespace jfa

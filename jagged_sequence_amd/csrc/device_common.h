@@ -1,0 +1,124 @@
+// Device helpers shared by the gfx950 attention kernels: MFMA wrappers, bf16 packing, the
+// relative-distance bucket, activations built from exp2 and reciprocal, and tile loaders.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "jfa_internal.h"
+
+namespace jfa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// 32x32x16 bf16 MFMA, fp32 accumulate. Operand lane layout (gfx950): lane l holds row (A) or
+// column (B) l%32 and the 8 contraction elements 8*(l/32)..+7; the accumulator holds column l%32
+// and rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Accumulator row m = 8*(r/4) + 4*(l/32) + r%4 is loaded from operand row kappa(m) (bits 2 and 3
+// swapped). Then accumulator registers 8c..8c+7 of lane l hold operand rows 16c + 8*(l/32) + 0..7,
+// which is exactly the B-operand layout of the next MFMA whose contraction runs over those rows:
+// scores computed this way feed the second product straight from registers.
+__device__ __forceinline__ int kappa(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Operand row held by accumulator register r of lane-half hh after the kappa load.
+__device__ __forceinline__ int acc_row(int r, int hh) { return 16 * (r >> 3) + 8 * hh + (r & 7); }
+
+__device__ __forceinline__ bf16x8 lds_load8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    f32x2 f = {x[j], x[j + 1]};
+    bf16x2 p = __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
+    r[j] = p[0];
+    r[j + 1] = p[1];
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Relative-distance bucket: exact below 16, then four equal-width buckets per octave, capped at 63.
+__device__ __forceinline__ int rel_bucket(int d) {
+  d = d < 0 ? -d : d;
+  if (d < 16) return d;
+  int e = 31 - __builtin_clz(d);
+  int b = 16 + 4 * (e - 4) + ((d >> (e - 2)) & 3);
+  return b < 63 ? b : 63;
+}
+
+// Score activations for GDPA. sigma(z) = 1 / (1 + 2^(-z log2 e)); SiLU(x) = x sigma(x);
+// GELU_tanh(x) = x sigma(2u), u = sqrt(2/pi) (x + 0.044715 x^3), using 1 + tanh(u) = 2 sigma(2u).
+// Only the exp2 and reciprocal units are used, no tanh.
+constexpr float kGeluK2 = 2.0f * 0.7978845608028654f;  // 2 sqrt(2/pi)
+constexpr float kGeluC = 0.044715f;
+
+template <int ACT>
+__device__ __forceinline__ float act_fwd(float x) {
+  if (ACT == kSilu) {
+    return x * fast_rcp(1.0f + fast_exp2(-kLog2e * x));
+  } else {
+    float z = kGeluK2 * x * (1.0f + kGeluC * x * x);
+    return x * fast_rcp(1.0f + fast_exp2(-kLog2e * z));
+  }
+}
+
+// act(x) and act'(x) together.
+template <int ACT>
+__device__ __forceinline__ void act_fwd_grad(float x, float& f, float& g) {
+  if (ACT == kSilu) {
+    float sg = fast_rcp(1.0f + fast_exp2(-kLog2e * x));
+    f = x * sg;
+    g = sg * (1.0f + x * (1.0f - sg));
+  } else {
+    float x2 = x * x;
+    float z = kGeluK2 * x * (1.0f + kGeluC * x2);           // 2u
+    float dz = kGeluK2 * (1.0f + 3.0f * kGeluC * x2);        // 2u'
+    float sg = fast_rcp(1.0f + fast_exp2(-kLog2e * z));     // sigma(2u)
+    f = x * sg;
+    g = sg + x * sg * (1.0f - sg) * dz;
+  }
+}
+
+// Store 4 consecutive fp32 values as bf16 (8 bytes) or fp32 (16 bytes).
+__device__ __forceinline__ void store4(void* base, size_t idx, float a, float b, float c, float d, int f32) {
+  if (f32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = make_float4(a, b, c, d);
+  } else {
+    uint2 w = make_uint2(pack2_bf16(a, b), pack2_bf16(c, d));
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) = w;
+  }
+}
+
+__device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Pack element e (0..7) of four 8-element bf16 rows into 4 consecutive bf16 (a column slice).
+__device__ __forceinline__ uint2 column4(const uint4 (&r)[4], int e) {
+  auto half = [&](const uint4& x) -> uint32_t {
+    uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+    return (e & 1) ? (w >> 16) : (w & 0xffffu);
+  };
+  return make_uint2(half(r[0]) | (half(r[1]) << 16), half(r[2]) | (half(r[3]) << 16));
+}
+
+}  // namespace jfa

@@ -1,0 +1,356 @@
+// Forward pass of jagged attention on gfx950.
+//
+// One workgroup (4 waves) runs one work item: a 128-row query tile of one (sequence, head) over a
+// range of 64-key tiles. Each wave owns 32 query rows. Per key tile:
+//   S^T = K Q^T            (32x32x16 bf16 MFMA; K rows from LDS in kappa order, Q^T from registers)
+//   score -> log2 domain, bias added, mask by -inf only on tiles that straddle the sequence end
+//            or the diagonal (aihot.vn GEM page, "Jagged Sequence Flash Attention": no padding;
+//            kerneldigest.dev page, "Arquitectura del Sistema": masking by subtraction)
+//   online softmax (running max / sum per query lane) or the GDPA activation
+//            (aihot.vn GEM page, "Generalized Dot-Product Attention (GDPA)")
+//   O^T += V^T P^T         (V^T from LDS, P^T straight from the score registers)
+// The query of lane l is column l%32 of every accumulator, so row statistics reduce inside the
+// lane plus one exchange with lane l^32.
+#include "device_common.h"
+
+namespace jfa {
+namespace {
+
+template <int D>
+struct alignas(16) FwdSmem {
+  static constexpr int KS = D + 8;          // K row stride (bf16): 16-byte reads are conflict free
+  static constexpr int VS = kFwdBN + 8;     // V^T row stride
+  __bf16 k[kFwdBN * KS];
+  __bf16 vt[D * VS];
+  float tab[kBuckets];
+};
+
+template <int D>
+struct KvRegs {
+  static constexpr int KCH = kFwdBN * D / 8 / kThreads;  // 16-byte K chunks per thread
+  uint4 k[KCH];
+  uint4 v[4];                                           // 4 keys x 8 dims, stored transposed
+};
+
+template <int D>
+__device__ __forceinline__ void load_kv(KvRegs<D>& r, const uint16_t* kb, const uint16_t* vb, int rs, int key0,
+                                        int Lkv, int tid) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int u = 0; u < KvRegs<D>::KCH; ++u) {
+    int c = tid + kThreads * u, row = c / CPR, col = c % CPR, key = key0 + row;
+    r.k[u] = key < Lkv ? load16(kb + (size_t)key * rs + col * 8) : make_uint4(0, 0, 0, 0);
+  }
+  constexpr int UNITS = (kFwdBN / 4) * CPR;
+  if (UNITS >= kThreads || tid < UNITS) {
+    int dg = tid % CPR, kg = tid / CPR;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int key = key0 + 4 * kg + j;
+      r.v[j] = key < Lkv ? load16(vb + (size_t)key * rs + dg * 8) : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_kv(const KvRegs<D>& r, FwdSmem<D>& sm, int tid) {
+  constexpr int CPR = D / 8, KS = FwdSmem<D>::KS, VS = FwdSmem<D>::VS;
+#pragma unroll
+  for (int u = 0; u < KvRegs<D>::KCH; ++u) {
+    int c = tid + kThreads * u, row = c / CPR, col = c % CPR;
+    *reinterpret_cast<uint4*>(&sm.k[row * KS + col * 8]) = r.k[u];
+  }
+  constexpr int UNITS = (kFwdBN / 4) * CPR;
+  if (UNITS >= kThreads || tid < UNITS) {
+    int dg = tid % CPR, kg = tid / CPR;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<uint2*>(&sm.vt[(dg * 8 + e) * VS + 4 * kg]) = column4(r.v, e);
+  }
+}
+
+template <int D, int ACT, int BIAS, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void fwd_kernel(FwdArgs a) {
+  constexpr int BM = kFwdBM, BN = kFwdBN, NKB = D / 16, NDB = D / 32;
+  constexpr int KS = FwdSmem<D>::KS, VS = FwdSmem<D>::VS;
+  constexpr bool SOFTMAX = ACT == kSoftmax;
+  __shared__ FwdSmem<D> sm;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int32_t* it = a.items + (size_t)blockIdx.x * kItemInts;
+  const int b = it[0], h = it[1], t = it[2], k0 = it[3], k1 = it[4], slot = it[5];
+  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
+  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const int rs = a.H * D;
+  const int row0 = t * BM + wave * 32;
+  const int qi = row0 + l32;
+
+  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid] * (SOFTMAX ? kLog2e : 1.0f);
+  const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
+
+  bf16x8 qf[NKB];
+  {
+    const uint16_t* qp = a.q + (size_t)(qs + qi) * rs + h * D + hh * 8;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      uint4 w = qi < Lq ? load16(qp + kb * 16) : make_uint4(0, 0, 0, 0);
+      qf[kb] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  float m_run = kNegInf, l_run = 0.0f;
+  const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
+
+  const uint16_t* kbase = a.k + (size_t)ks * rs + h * D;
+  const uint16_t* vbase = a.v + (size_t)ks * rs + h * D;
+  KvRegs<D> pf;
+  if (k0 < k1) load_kv<D>(pf, kbase, vbase, rs, k0 * BN, Lkv, tid);
+
+  for (int kt = k0; kt < k1; ++kt) {
+    __syncthreads();
+    store_kv<D>(pf, sm, tid);
+    __syncthreads();
+    if (kt + 1 < k1) load_kv<D>(pf, kbase, vbase, rs, (kt + 1) * BN, Lkv, tid);
+    const int key0 = kt * BN;
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      sacc[sb] = f32x16{};
+      const __bf16* kr = &sm.k[(32 * sb + kappa(l32)) * KS + hh * 8];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sacc[sb] = mfma32(lds_load8(kr + kb * 16), qf[kb], sacc[sb]);
+    }
+
+    const bool need_mask = (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
+    float s[2][16];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * sb + acc_row(r, hh);
+        float x = sacc[sb][r] * smul;
+        if (BIAS == kBiasBucket) x += sm.tab[rel_bucket(qi - key)];
+        if (BIAS == kBiasScalar && !SOFTMAX) x += bias_c;
+        const bool masked = need_mask && (key >= Lkv || (CAUSAL && key > qi));
+        if (SOFTMAX) {
+          s[sb][r] = masked ? kNegInf : x;
+        } else {
+          s[sb][r] = masked ? 0.0f : act_fwd<ACT>(x);
+        }
+      }
+    }
+
+    if (SOFTMAX) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == kNegInf ? 0.0f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float lsum = 0.0f;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(s[sb][r] - m_use);
+          s[sb][r] = p;
+          lsum += p;
+        }
+      l_run = l_run * alpha + lsum;
+      if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      m_run = m_new;
+    }
+
+    bf16x8 pb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pb[c] = pack8(&s[c >> 1][8 * (c & 1)]);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const __bf16* vr = &sm.vt[(32 * db + l32) * VS + 8 * hh];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[db] = mfma32(lds_load8(vr + 16 * c), pb[c], o[db]);
+    }
+  }
+
+  // Epilogue. Accumulator register r of d-block db holds dimension 32 db + 8 (r/4) + 4 hh + r%4.
+  float inv;
+  float l_tot = 0.0f;
+  if (SOFTMAX) {
+    l_tot = l_run + __shfl_xor(l_run, 32);
+    inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  } else {
+    inv = (slot < 0 && Lkv > 0) ? 1.0f / (float)Lkv : 1.0f;
+  }
+  if (slot < 0) {
+    if (qi < Lq) {
+      const size_t base = ((size_t)(qs + qi) * a.H + h) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(a.out, base + 32 * db + 8 * g + 4 * hh, o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
+                 o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv, a.out_f32);
+      if (SOFTMAX && hh == 0)
+        a.lse[(size_t)h * a.Tq + qs + qi] =
+            l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 + (BIAS == kBiasScalar ? bias_c : 0.0f) : kNegInf;
+    }
+  } else {
+    const int prow = wave * 32 + l32;
+    float* po = a.part_o + ((size_t)slot * BM + prow) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * g + 4 * hh) =
+            make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+    if (SOFTMAX && hh == 0)
+      a.part_lse[(size_t)slot * BM + prow] = l_tot > 0.0f ? m_run + fast_log2(l_tot) : kNegInf;
+  }
+}
+
+// Merge the pieces of split items in fixed order r = 0..R-1:
+//   softmax: lse* = log2 sum_r 2^lse_r,  O = sum_r 2^(lse_r - lse*) O_r   (O_r normalised per piece)
+//   GDPA:    O = (sum_r O_r) / Lkv
+template <int D, int ACT, int BIAS>
+__global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
+  constexpr int BM = kFwdBM;
+  constexpr bool SOFTMAX = ACT == kSoftmax;
+  const int32_t* g = a.groups + (size_t)blockIdx.x * kGroupInts;
+  const int b = g[0], h = g[1], t = g[2], slot0 = g[3], R = g[4];
+  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
+  const int Lkv = a.kv_off[b + 1] - a.kv_off[b];
+  const int row = threadIdx.x >> 1, part = threadIdx.x & 1;
+  const int qi = t * BM + row;
+  if (qi >= Lq) return;
+  constexpr int HALF = D / 2;
+  float acc[HALF];
+#pragma unroll
+  for (int d = 0; d < HALF; ++d) acc[d] = 0.0f;
+  float lse2 = kNegInf;
+  if (SOFTMAX) {
+    float mx = kNegInf;
+    for (int r = 0; r < R; ++r) mx = fmaxf(mx, a.part_lse[(size_t)(slot0 + r) * BM + row]);
+    if (mx != kNegInf) {
+      float sum = 0.0f;
+      for (int r = 0; r < R; ++r) sum += fast_exp2(a.part_lse[(size_t)(slot0 + r) * BM + row] - mx);
+      lse2 = mx + fast_log2(sum);
+      for (int r = 0; r < R; ++r) {
+        const float w = fast_exp2(a.part_lse[(size_t)(slot0 + r) * BM + row] - lse2);
+        const float* po = a.part_o + ((size_t)(slot0 + r) * BM + row) * D + part * HALF;
+#pragma unroll
+        for (int d = 0; d < HALF; d += 4) {
+          float4 x = *reinterpret_cast<const float4*>(po + d);
+          acc[d] += w * x.x;
+          acc[d + 1] += w * x.y;
+          acc[d + 2] += w * x.z;
+          acc[d + 3] += w * x.w;
+        }
+      }
+    }
+  } else {
+    for (int r = 0; r < R; ++r) {
+      const float* po = a.part_o + ((size_t)(slot0 + r) * BM + row) * D + part * HALF;
+#pragma unroll
+      for (int d = 0; d < HALF; d += 4) {
+        float4 x = *reinterpret_cast<const float4*>(po + d);
+        acc[d] += x.x;
+        acc[d + 1] += x.y;
+        acc[d + 2] += x.z;
+        acc[d + 3] += x.w;
+      }
+    }
+    const float inv = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
+#pragma unroll
+    for (int d = 0; d < HALF; ++d) acc[d] *= inv;
+  }
+  const size_t base = ((size_t)(qs + qi) * a.H + h) * D + part * HALF;
+#pragma unroll
+  for (int d = 0; d < HALF; d += 4) store4(a.out, base + d, acc[d], acc[d + 1], acc[d + 2], acc[d + 3], a.out_f32);
+  if (SOFTMAX && part == 0)
+    a.lse[(size_t)h * a.Tq + qs + qi] =
+        lse2 == kNegInf ? kNegInf : lse2 * kLn2 + (BIAS == kBiasScalar ? a.bias[h] : 0.0f);
+}
+
+template <int D, int ACT, int BIAS, bool CAUSAL>
+hipError_t fwd_launch_t(const FwdArgs& a, int n, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_kernel<D, ACT, BIAS, CAUSAL>), dim3(n), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int ACT, int BIAS>
+hipError_t fwd_launch_c(const FwdArgs& a, const Modes& m, int n, hipStream_t s) {
+  return m.causal ? fwd_launch_t<D, ACT, BIAS, true>(a, n, s) : fwd_launch_t<D, ACT, BIAS, false>(a, n, s);
+}
+
+template <int D, int ACT>
+hipError_t fwd_launch_b(const FwdArgs& a, const Modes& m, int n, hipStream_t s) {
+  switch (m.bias) {
+    case kBiasNone: return fwd_launch_c<D, ACT, kBiasNone>(a, m, n, s);
+    case kBiasScalar: return fwd_launch_c<D, ACT, kBiasScalar>(a, m, n, s);
+    default: return fwd_launch_c<D, ACT, kBiasBucket>(a, m, n, s);
+  }
+}
+
+template <int D>
+hipError_t fwd_launch_a(const FwdArgs& a, const Modes& m, int n, hipStream_t s) {
+  switch (m.act) {
+    case kSoftmax: return fwd_launch_b<D, kSoftmax>(a, m, n, s);
+    case kSilu: return fwd_launch_b<D, kSilu>(a, m, n, s);
+    default: return fwd_launch_b<D, kGeluTanh>(a, m, n, s);
+  }
+}
+
+template <int D, int ACT>
+hipError_t comb_launch_b(const FwdArgs& a, const Modes& m, int n, hipStream_t s) {
+  if (m.bias == kBiasScalar)
+    hipLaunchKernelGGL((fwd_combine_kernel<D, ACT, kBiasScalar>), dim3(n), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_combine_kernel<D, ACT, kBiasNone>), dim3(n), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t comb_launch_a(const FwdArgs& a, const Modes& m, int n, hipStream_t s) {
+  switch (m.act) {
+    case kSoftmax: return comb_launch_b<D, kSoftmax>(a, m, n, s);
+    case kSilu: return comb_launch_b<D, kSilu>(a, m, n, s);
+    default: return comb_launch_b<D, kGeluTanh>(a, m, n, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_forward(const FwdArgs& a, const Modes& m, int n_items, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  return m.D == 64 ? fwd_launch_a<64>(a, m, n_items, s) : fwd_launch_a<128>(a, m, n_items, s);
+}
+
+hipError_t launch_forward_combine(const FwdArgs& a, const Modes& m, int n_groups, hipStream_t s) {
+  if (n_groups <= 0) return hipSuccess;
+  return m.D == 64 ? comb_launch_a<64>(a, m, n_groups, s) : comb_launch_a<128>(a, m, n_groups, s);
+}
+
+int occupancy_forward(const Modes& m) {
+  int n = 0;
+  hipError_t e;
+  if (m.D == 64)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<64, kSoftmax, kBiasBucket, true>, kThreads, 0);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<128, kSoftmax, kBiasBucket, true>, kThreads, 0);
+  return (e == hipSuccess && n > 0) ? n : 1;
+}
+
+}  // namespace jfa

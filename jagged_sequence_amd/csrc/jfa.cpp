@@ -1,0 +1,531 @@
+// Host side of the jagged attention library: argument checks, the jagged tile scheduler, the
+// workspace layout and the C ABI entry points declared in include/jfa.h.
+//
+// Scheduler. Removing padding leaves compute units idle when short sequences finish early, and the
+// bottleneck moves to tile scheduling and load balance (aihot.vn GEM page, "Jagged Sequence Flash
+// Attention"; vibekk.com GEM page, section on moving from padding to jagged kernels). Every tile of
+// useful work becomes one work item; an item whose cost (visible tiles on its inner loop) exceeds a
+// fair share ceil(total / slots) is split into R = ceil(cost / share) equal ranges whose partial
+// results are merged in a fixed order; the list is sorted longest first, ties by (b, h, tile,
+// range start), so that greedy in-order dispatch of workgroups is longest-processing-time
+// scheduling and the list is unique.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "jfa.h"
+#include "jfa_internal.h"
+
+using namespace jfa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+jfa_status fail(jfa_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+jfa_status hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return JFA_ERR_HIP;
+}
+
+enum ListId { kFwd = 0, kDq = 1, kKv = 2 };
+
+struct List {
+  std::vector<int32_t> items;   // 6 ints per item: b, h, tile, lo, hi, slot
+  std::vector<int32_t> groups;  // 5 ints per group: b, h, tile, slot0, R
+  int nslots = 0;
+  int slots = 0;                // concurrency the split rule balanced for
+  int32_t* d_items = nullptr;
+  int32_t* d_groups = nullptr;
+  size_t n_items() const { return items.size() / 6; }
+  size_t n_groups() const { return groups.size() / 5; }
+};
+
+struct Raw {
+  int b, h, t, lo, hi;
+};
+
+void finish(const std::vector<Raw>& raw, int slots, bool split, List& out) {
+  int64_t total = 0;
+  for (const Raw& r : raw) total += r.hi - r.lo;
+  const int64_t s = std::max(1, slots);
+  const int64_t target = std::max<int64_t>(1, (total + s - 1) / s);
+  struct Item {
+    int b, h, t, lo, hi, slot;
+  };
+  std::vector<Item> items;
+  items.reserve(raw.size());
+  int next = 0;
+  for (const Raw& r : raw) {
+    const int64_t cost = r.hi - r.lo;
+    if (split && cost > target) {
+      const int64_t R = (cost + target - 1) / target;
+      out.groups.insert(out.groups.end(), {r.b, r.h, r.t, next, (int32_t)R});
+      for (int64_t k = 0; k < R; ++k)
+        items.push_back({r.b, r.h, r.t, (int)(r.lo + (k * cost) / R), (int)(r.lo + ((k + 1) * cost) / R), next + (int)k});
+      next += (int)R;
+    } else {
+      items.push_back({r.b, r.h, r.t, r.lo, r.hi, -1});
+    }
+  }
+  std::sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
+    const int cx = x.hi - x.lo, cy = y.hi - y.lo;
+    if (cx != cy) return cx > cy;
+    if (x.b != y.b) return x.b < y.b;
+    if (x.h != y.h) return x.h < y.h;
+    if (x.t != y.t) return x.t < y.t;
+    return x.lo < y.lo;
+  });
+  out.items.reserve(items.size() * 6);
+  for (const Item& i : items) out.items.insert(out.items.end(), {i.b, i.h, i.t, i.lo, i.hi, i.slot});
+  out.nslots = next;
+  out.slots = slots;
+}
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Query-tile list: item (b, h, t) covers key tiles [0, cost).
+void query_tile_list(const std::vector<int>& lq, const std::vector<int>& lkv, int H, bool causal, int BM, int BN,
+                     int slots, bool split, List& out) {
+  std::vector<Raw> raw;
+  for (size_t b = 0; b < lq.size(); ++b) {
+    const int n_kv = ceil_div(lkv[b], BN);
+    const int n_t = ceil_div(lq[b], BM);
+    for (int h = 0; h < H; ++h)
+      for (int t = 0; t < n_t; ++t) {
+        const int cost = causal ? std::min(ceil_div((t + 1) * BM, BN), n_kv) : n_kv;
+        raw.push_back({(int)b, h, t, 0, cost});
+      }
+  }
+  finish(raw, slots, split, out);
+}
+
+// Key-tile list: item (b, h, kt) covers query tiles [first, first + cost).
+void key_tile_list(const std::vector<int>& lq, const std::vector<int>& lkv, int H, bool causal, int BMq, int BNk,
+                   int slots, bool split, List& out) {
+  std::vector<Raw> raw;
+  for (size_t b = 0; b < lq.size(); ++b) {
+    const int n_q = ceil_div(lq[b], BMq);
+    const int n_kt = ceil_div(lkv[b], BNk);
+    for (int h = 0; h < H; ++h)
+      for (int kt = 0; kt < n_kt; ++kt) {
+        const int first = causal ? (int)(((int64_t)kt * BNk) / BMq) : 0;
+        const int cost = std::max(0, n_q - first);
+        raw.push_back({(int)b, h, kt, first, first + cost});
+      }
+  }
+  finish(raw, slots, split, out);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct jfa_plan_s {
+  int B = 0, H = 0, D = 0, Tq = 0, Tkv = 0;
+  Modes modes{};
+  float scale = 0.0f;
+  int out_f32 = 0, grad_f32 = 0;
+  uint32_t flags = 0;
+  std::vector<int32_t> q_off, kv_off;
+  List lists[3];
+  void* dev = nullptr;  // device copy of all work lists
+  int device = -1;
+  // workspace layout
+  size_t ws_fwd = 0, off_part_lse = 0;
+  size_t ws_bwd = 0, off_delta = 0, off_part_dq = 0, off_part_dk = 0, off_part_dv = 0;
+  // timing
+  bool timing = false;
+  struct Rec {
+    int kernel;
+    hipEvent_t start, stop;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t pool_used = 0;
+};
+
+namespace {
+
+jfa_status check_problem(const jfa_problem* p, std::vector<int>& lq, std::vector<int>& lkv) {
+  if (!p) return fail(JFA_ERR_NULL_ARG, "problem is NULL");
+  if (!p->q_offsets_host || !p->kv_offsets_host) return fail(JFA_ERR_NULL_ARG, "host offsets are NULL");
+  if (p->num_seqs < 1) return fail(JFA_ERR_BAD_SHAPE, "num_seqs must be >= 1");
+  if (p->num_heads < 1) return fail(JFA_ERR_BAD_SHAPE, "num_heads must be >= 1");
+  if (p->head_dim != 64 && p->head_dim != 128) return fail(JFA_ERR_BAD_SHAPE, "head_dim must be 64 or 128");
+  if (p->mask < 0 || p->mask > 1) return fail(JFA_ERR_UNSUPPORTED, "unknown mask mode");
+  if (p->act < 0 || p->act > 2) return fail(JFA_ERR_UNSUPPORTED, "unknown activation");
+  if (p->bias < 0 || p->bias > 2) return fail(JFA_ERR_UNSUPPORTED, "unknown bias kind");
+  if (p->out_dtype < 0 || p->out_dtype > 1 || p->grad_dtype < 0 || p->grad_dtype > 1)
+    return fail(JFA_ERR_UNSUPPORTED, "unknown dtype");
+  if (p->num_slots < 0) return fail(JFA_ERR_BAD_SHAPE, "num_slots must be >= 0");
+  if (!std::isfinite(p->scale)) return fail(JFA_ERR_UNSUPPORTED, "scale must be finite");
+  if ((p->flags & ~(JFA_PLAN_HOST_ONLY | JFA_PLAN_NO_SPLIT)) != 0) return fail(JFA_ERR_UNSUPPORTED, "unknown flags");
+  const int B = p->num_seqs;
+  if (p->q_offsets_host[0] != 0 || p->kv_offsets_host[0] != 0) return fail(JFA_ERR_BAD_OFFSETS, "offsets[0] must be 0");
+  lq.resize(B);
+  lkv.resize(B);
+  for (int b = 0; b < B; ++b) {
+    const int64_t a = (int64_t)p->q_offsets_host[b + 1] - p->q_offsets_host[b];
+    const int64_t c = (int64_t)p->kv_offsets_host[b + 1] - p->kv_offsets_host[b];
+    if (a < 0 || c < 0) return fail(JFA_ERR_BAD_OFFSETS, "offsets must be non-decreasing (sequence " + std::to_string(b) + ")");
+    lq[b] = (int)a;
+    lkv[b] = (int)c;
+    if (p->mask == JFA_MASK_CAUSAL && a != c)
+      return fail(JFA_ERR_BAD_SHAPE, "causal mask needs Lq == Lkv (sequence " + std::to_string(b) + ")");
+  }
+  const int64_t tq = p->q_offsets_host[B], tkv = p->kv_offsets_host[B];
+  if (tq * p->num_heads * (int64_t)p->head_dim >= ((int64_t)1 << 40) || tkv * p->num_heads * (int64_t)p->head_dim >= ((int64_t)1 << 40))
+    return fail(JFA_ERR_BAD_SHAPE, "tensor too large");
+  return JFA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+hipEvent_t take_event(jfa_plan_s* P) {
+  if (P->pool_used == P->pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    P->pool.push_back(e);
+  }
+  return P->pool[P->pool_used++];
+}
+
+// Launch `fn` on stream s, bracketed by timing events when timing is on.
+template <class F>
+jfa_status timed(jfa_plan_s* P, int kernel, hipStream_t s, F fn, const char* what) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (P->timing) {
+    a = take_event(P);
+    b = take_event(P);
+    if (!a || !b) return fail(JFA_ERR_HIP, "hipEventCreate failed");
+    hipEventRecord(a, s);
+  }
+  hipError_t e = fn();
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (P->timing) {
+    hipEventRecord(b, s);
+    P->recs.push_back({kernel, a, b});
+  }
+  return JFA_OK;
+}
+
+jfa_status debug_check_offsets(jfa_plan_s* P, const int32_t* dq, const int32_t* dkv, hipStream_t s) {
+  static const bool on = [] {
+    const char* v = std::getenv("JFA_DEBUG");
+    return v && v[0] == '1';
+  }();
+  if (!on) return JFA_OK;
+  std::vector<int32_t> a(P->B + 1), b(P->B + 1);
+  if (hipStreamSynchronize(s) != hipSuccess) return fail(JFA_ERR_HIP, "JFA_DEBUG sync failed");
+  if (hipMemcpy(a.data(), dq, a.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(b.data(), dkv, b.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(JFA_ERR_HIP, "JFA_DEBUG offset copy failed");
+  if (a != P->q_off || b != P->kv_off) return fail(JFA_ERR_BAD_OFFSETS, "device offsets differ from the planned host offsets");
+  return JFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t* plan_out) {
+  if (!plan_out) return fail(JFA_ERR_NULL_ARG, "plan_out is NULL");
+  *plan_out = nullptr;
+  std::vector<int> lq, lkv;
+  jfa_status st = check_problem(problem, lq, lkv);
+  if (st != JFA_OK) return st;
+  const jfa_problem& p = *problem;
+  jfa_plan_s* P = new (std::nothrow) jfa_plan_s();
+  if (!P) return fail(JFA_ERR_UNSUPPORTED, "out of host memory");
+  P->B = p.num_seqs;
+  P->H = p.num_heads;
+  P->D = p.head_dim;
+  P->q_off.assign(p.q_offsets_host, p.q_offsets_host + P->B + 1);
+  P->kv_off.assign(p.kv_offsets_host, p.kv_offsets_host + P->B + 1);
+  P->Tq = P->q_off[P->B];
+  P->Tkv = P->kv_off[P->B];
+  P->modes = Modes{p.head_dim, p.act, p.bias, p.mask == JFA_MASK_CAUSAL ? 1 : 0};
+  P->scale = p.scale != 0.0f ? p.scale : 1.0f / std::sqrt((float)p.head_dim);
+  P->out_f32 = p.out_dtype == JFA_F32;
+  P->grad_f32 = p.grad_dtype == JFA_F32;
+  P->flags = p.flags;
+  const bool host_only = (p.flags & JFA_PLAN_HOST_ONLY) != 0;
+  const bool split = (p.flags & JFA_PLAN_NO_SPLIT) == 0;
+
+  int slots[3] = {p.num_slots, p.num_slots, p.num_slots};
+  if (p.num_slots == 0) {
+    if (host_only) {
+      slots[0] = slots[1] = slots[2] = 512;
+    } else {
+      int dev = 0, cus = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) {
+        delete P;
+        return hip_fail(e, "device query");
+      }
+      slots[kFwd] = cus * occupancy_forward(P->modes);
+      slots[kDq] = cus * occupancy_dq(P->modes);
+      slots[kKv] = cus * occupancy_dkdv(P->modes);
+    }
+  }
+  const bool causal = P->modes.causal != 0;
+  query_tile_list(lq, lkv, P->H, causal, kFwdBM, kFwdBN, slots[kFwd], split, P->lists[kFwd]);
+  query_tile_list(lq, lkv, P->H, causal, kDqBM, kDqBN, slots[kDq], split, P->lists[kDq]);
+  key_tile_list(lq, lkv, P->H, causal, kKvBM, kKvBN, slots[kKv], split, P->lists[kKv]);
+
+  // workspace layout
+  const size_t D = P->D;
+  P->ws_fwd = align256((size_t)P->lists[kFwd].nslots * kFwdBM * D * 4);
+  P->off_part_lse = P->ws_fwd;
+  P->ws_fwd += align256((size_t)P->lists[kFwd].nslots * kFwdBM * 4);
+  size_t o = 0;
+  P->off_delta = o;
+  if (P->modes.act == kSoftmax) o += align256((size_t)P->H * P->Tq * 4);
+  P->off_part_dq = o;
+  o += align256((size_t)P->lists[kDq].nslots * kDqBM * D * 4);
+  P->off_part_dk = o;
+  o += align256((size_t)P->lists[kKv].nslots * kKvBN * D * 4);
+  P->off_part_dv = o;
+  o += align256((size_t)P->lists[kKv].nslots * kKvBN * D * 4);
+  P->ws_bwd = o;
+  if (P->lists[kFwd].nslots == 0) P->ws_fwd = 0;
+
+  if (!host_only) {
+    // device records: 8 int32 per item / group
+    size_t total = 0;
+    for (auto& L : P->lists) total += (L.n_items() + L.n_groups()) * 8;
+    std::vector<int32_t> host(std::max<size_t>(total, 8), 0);
+    size_t pos = 0;
+    size_t offs[3][2];
+    for (int l = 0; l < 3; ++l) {
+      List& L = P->lists[l];
+      offs[l][0] = pos;
+      for (size_t i = 0; i < L.n_items(); ++i, pos += 8) std::copy_n(&L.items[i * 6], 6, &host[pos]);
+      offs[l][1] = pos;
+      for (size_t g = 0; g < L.n_groups(); ++g, pos += 8) std::copy_n(&L.groups[g * 5], 5, &host[pos]);
+    }
+    hipError_t e = hipGetDevice(&P->device);
+    if (e == hipSuccess) e = hipMalloc(&P->dev, host.size() * 4);
+    if (e != hipSuccess) {
+      delete P;
+      return hip_fail(e, "plan device allocation");
+    }
+    // synchronous copy: the host staging vector dies with this call
+    e = hipMemcpyAsync(P->dev, host.data(), host.size() * 4, hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) {
+      (void)hipFree(P->dev);
+      delete P;
+      return hip_fail(e, "plan upload");
+    }
+    for (int l = 0; l < 3; ++l) {
+      P->lists[l].d_items = static_cast<int32_t*>(P->dev) + offs[l][0];
+      P->lists[l].d_groups = static_cast<int32_t*>(P->dev) + offs[l][1];
+    }
+  }
+  *plan_out = P;
+  return JFA_OK;
+}
+
+jfa_status jfa_workspace_bytes(jfa_plan_t P, size_t* fwd_bytes, size_t* bwd_bytes) {
+  if (!P) return fail(JFA_ERR_NULL_ARG, "plan is NULL");
+  if (fwd_bytes) *fwd_bytes = P->ws_fwd;
+  if (bwd_bytes) *bwd_bytes = P->ws_bwd;
+  return JFA_OK;
+}
+
+jfa_status jfa_forward(jfa_plan_t P, const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                       const int32_t* kv_offsets, const float* bias, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, jfa_stream_t stream) {
+  if (!P) return fail(JFA_ERR_NULL_ARG, "plan is NULL");
+  if (P->flags & JFA_PLAN_HOST_ONLY) return fail(JFA_ERR_HOST_ONLY, "plan was built host-only");
+  const bool softmax = P->modes.act == kSoftmax;
+  if (!q || !k || !v || !q_offsets || !kv_offsets || !out) return fail(JFA_ERR_NULL_ARG, "a tensor or offsets pointer is NULL");
+  if (P->modes.bias != kBiasNone && !bias) return fail(JFA_ERR_NULL_ARG, "bias is NULL");
+  if (softmax && !lse) return fail(JFA_ERR_NULL_ARG, "lse is NULL (required for softmax)");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)) ||
+      (bias && !aligned16(bias)) || !aligned16(workspace))
+    return fail(JFA_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
+  if (workspace_bytes < P->ws_fwd || (P->ws_fwd > 0 && !workspace))
+    return fail(JFA_ERR_WORKSPACE, "forward workspace needs " + std::to_string(P->ws_fwd) + " bytes");
+  hipStream_t s = (hipStream_t)stream;
+  jfa_status st = debug_check_offsets(P, q_offsets, kv_offsets, s);
+  if (st != JFA_OK) return st;
+
+  FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.q_off = q_offsets;
+  a.kv_off = kv_offsets;
+  a.bias = bias;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + P->off_part_lse) : nullptr;
+  a.items = P->lists[kFwd].d_items;
+  a.groups = P->lists[kFwd].d_groups;
+  a.H = P->H;
+  a.Tq = P->Tq;
+  a.scale = P->scale;
+  a.out_f32 = P->out_f32;
+  const List& L = P->lists[kFwd];
+  st = timed(P, 0, s, [&] { return launch_forward(a, P->modes, (int)L.n_items(), s); }, "forward launch");
+  if (st != JFA_OK) return st;
+  if (L.n_groups() > 0)
+    st = timed(P, 1, s, [&] { return launch_forward_combine(a, P->modes, (int)L.n_groups(), s); }, "combine launch");
+  return st;
+}
+
+jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                        const int32_t* kv_offsets, const float* bias, const void* out, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, float* dbias, void* workspace,
+                        size_t workspace_bytes, jfa_stream_t stream) {
+  if (!P) return fail(JFA_ERR_NULL_ARG, "plan is NULL");
+  if (P->flags & JFA_PLAN_HOST_ONLY) return fail(JFA_ERR_HOST_ONLY, "plan was built host-only");
+  const bool softmax = P->modes.act == kSoftmax;
+  if (dbias) return fail(JFA_ERR_UNSUPPORTED, "the bias gradient is not provided; pass dbias = NULL");
+  if (!q || !k || !v || !q_offsets || !kv_offsets || !dout || !dq || !dk || !dv)
+    return fail(JFA_ERR_NULL_ARG, "a tensor or offsets pointer is NULL");
+  if (P->modes.bias != kBiasNone && !bias) return fail(JFA_ERR_NULL_ARG, "bias is NULL");
+  if (softmax && (!out || !lse)) return fail(JFA_ERR_NULL_ARG, "out and lse are required for softmax");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || (out && !aligned16(out)) || (lse && !aligned16(lse)) || (bias && !aligned16(bias)) ||
+      !aligned16(workspace))
+    return fail(JFA_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
+  if (workspace_bytes < P->ws_bwd || (P->ws_bwd > 0 && !workspace))
+    return fail(JFA_ERR_WORKSPACE, "backward workspace needs " + std::to_string(P->ws_bwd) + " bytes");
+  hipStream_t s = (hipStream_t)stream;
+  jfa_status st = debug_check_offsets(P, q_offsets, kv_offsets, s);
+  if (st != JFA_OK) return st;
+
+  char* ws = static_cast<char*>(workspace);
+  BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.q_off = q_offsets;
+  a.kv_off = kv_offsets;
+  a.bias = bias;
+  a.out = out;
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = ws ? reinterpret_cast<float*>(ws + P->off_delta) : nullptr;
+  a.part_dq = ws ? reinterpret_cast<float*>(ws + P->off_part_dq) : nullptr;
+  a.part_dk = ws ? reinterpret_cast<float*>(ws + P->off_part_dk) : nullptr;
+  a.part_dv = ws ? reinterpret_cast<float*>(ws + P->off_part_dv) : nullptr;
+  a.dq_items = P->lists[kDq].d_items;
+  a.dq_groups = P->lists[kDq].d_groups;
+  a.kv_items = P->lists[kKv].d_items;
+  a.kv_groups = P->lists[kKv].d_groups;
+  a.H = P->H;
+  a.Tq = P->Tq;
+  a.Tkv = P->Tkv;
+  a.scale = P->scale;
+  a.out_f32 = P->out_f32;
+  a.grad_f32 = P->grad_f32;
+  const Modes& m = P->modes;
+  if (softmax) {
+    st = timed(P, 2, s, [&] { return launch_bwd_preprocess(a, m, s); }, "backward preprocess launch");
+    if (st != JFA_OK) return st;
+  }
+  st = timed(P, 3, s, [&] { return launch_bwd_dkdv(a, m, (int)P->lists[kKv].n_items(), s); }, "dK/dV launch");
+  if (st != JFA_OK) return st;
+  st = timed(P, 4, s, [&] { return launch_bwd_dq(a, m, (int)P->lists[kDq].n_items(), s); }, "dQ launch");
+  if (st != JFA_OK) return st;
+  if (P->lists[kDq].n_groups() > 0) {
+    st = timed(P, 5, s, [&] { return launch_bwd_reduce_dq(a, m, (int)P->lists[kDq].n_groups(), s); }, "dQ reduce launch");
+    if (st != JFA_OK) return st;
+  }
+  if (P->lists[kKv].n_groups() > 0)
+    st = timed(P, 5, s, [&] { return launch_bwd_reduce_dkdv(a, m, (int)P->lists[kKv].n_groups(), s); }, "dK/dV reduce launch");
+  return st;
+}
+
+jfa_status jfa_plan_schedule(jfa_plan_t P, int32_t which, int32_t* out, size_t cap, size_t* count) {
+  if (!P || !count) return fail(JFA_ERR_NULL_ARG, "plan or count is NULL");
+  if (which < 0 || which > 5) return fail(JFA_ERR_UNSUPPORTED, "which must be 0..5");
+  const List& L = P->lists[which / 2];
+  const bool groups = (which & 1) != 0;
+  const std::vector<int32_t>& v = groups ? L.groups : L.items;
+  const size_t per = groups ? 5 : 6;
+  *count = v.size() / per;
+  if (out) std::copy_n(v.data(), std::min(*count, cap) * per, out);
+  return JFA_OK;
+}
+
+jfa_status jfa_plan_info(jfa_plan_t P, int32_t* info, size_t n) {
+  if (!P || !info) return fail(JFA_ERR_NULL_ARG, "plan or info is NULL");
+  const int32_t v[9] = {kFwdBM, kFwdBN, kDqBM, kDqBN, kKvBM, kKvBN, P->lists[kFwd].slots, P->lists[kDq].slots,
+                        P->lists[kKv].slots};
+  std::copy_n(v, std::min<size_t>(n, 9), info);
+  return JFA_OK;
+}
+
+jfa_status jfa_timing_enable(jfa_plan_t P, int32_t enable) {
+  if (!P) return fail(JFA_ERR_NULL_ARG, "plan is NULL");
+  P->timing = enable != 0;
+  P->recs.clear();
+  P->pool_used = 0;
+  return JFA_OK;
+}
+
+jfa_status jfa_timing_read(jfa_plan_t P, int32_t kernel, float* total_ms, int32_t* launches) {
+  if (!P || !total_ms || !launches) return fail(JFA_ERR_NULL_ARG, "NULL argument");
+  float sum = 0.0f;
+  int n = 0;
+  for (const auto& r : P->recs) {
+    if (r.kernel != kernel) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "timing read");
+    sum += ms;
+    ++n;
+  }
+  *total_ms = sum;
+  *launches = n;
+  return JFA_OK;
+}
+
+void jfa_plan_destroy(jfa_plan_t P) {
+  if (!P) return;
+  if (P->dev) (void)hipFree(P->dev);
+  for (hipEvent_t e : P->pool) (void)hipEventDestroy(e);
+  delete P;
+}
+
+const char* jfa_status_string(jfa_status s) {
+  switch (s) {
+    case JFA_OK: return "JFA_OK";
+    case JFA_ERR_NULL_ARG: return "JFA_ERR_NULL_ARG";
+    case JFA_ERR_BAD_OFFSETS: return "JFA_ERR_BAD_OFFSETS";
+    case JFA_ERR_BAD_SHAPE: return "JFA_ERR_BAD_SHAPE";
+    case JFA_ERR_UNSUPPORTED: return "JFA_ERR_UNSUPPORTED";
+    case JFA_ERR_MISALIGNED: return "JFA_ERR_MISALIGNED";
+    case JFA_ERR_WORKSPACE: return "JFA_ERR_WORKSPACE";
+    case JFA_ERR_HIP: return "JFA_ERR_HIP";
+    case JFA_ERR_HOST_ONLY: return "JFA_ERR_HOST_ONLY";
+  }
+  return "JFA_ERR_UNKNOWN";
+}
+
+const char* jfa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal interface between the host planner / ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace jfa {
+
+// Tile geometry. Query-tile kernels (forward, dQ) run 4 waves x 32 query rows = 128 rows and walk
+// the keys 64 at a time; the dK/dV kernel runs 4 waves x 32 keys = 128 keys and walks the queries
+// 64 at a time. Every wave owns 32 rows/columns of one 32x32 MFMA block.
+constexpr int kFwdBM = 128, kFwdBN = 64;
+constexpr int kDqBM = 128, kDqBN = 64;
+constexpr int kKvBM = 64, kKvBN = 128;
+constexpr int kThreads = 256;
+constexpr int kItemInts = 8;   // device record: b, h, tile, lo, hi, slot, 0, 0
+constexpr int kGroupInts = 8;  // device record: b, h, tile, slot0, R, 0, 0, 0
+constexpr int kBuckets = 64;
+
+enum Act { kSoftmax = 0, kSilu = 1, kGeluTanh = 2 };
+enum BiasKind { kBiasNone = 0, kBiasScalar = 1, kBiasBucket = 2 };
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* q_off;
+  const int32_t* kv_off;
+  const float* bias;
+  void* out;
+  float* lse;
+  float* part_o;    // [slots][kFwdBM][D] fp32: per-piece normalised output (softmax) or raw sum (GDPA)
+  float* part_lse;  // [slots][kFwdBM] fp32: per-piece log2-sum-exp2 (softmax)
+  const int32_t* items;
+  const int32_t* groups;
+  int H;
+  int Tq;
+  float scale;
+  int out_f32;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* q_off;
+  const int32_t* kv_off;
+  const float* bias;
+  const void* out;
+  const float* lse;
+  const uint16_t* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;    // [H][Tq] fp32 (softmax)
+  float* part_dq;  // [slots][kDqBM][D]
+  float* part_dk;  // [slots][kKvBN][D]
+  float* part_dv;  // [slots][kKvBN][D]
+  const int32_t* dq_items;
+  const int32_t* dq_groups;
+  const int32_t* kv_items;
+  const int32_t* kv_groups;
+  int H;
+  int Tq;
+  int Tkv;
+  float scale;
+  int out_f32;
+  int grad_f32;
+};
+
+struct Modes {
+  int D;
+  int act;
+  int bias;
+  int causal;
+};
+
+// Launchers (defined next to their kernels). Each returns the hipGetLastError() of its launch.
+hipError_t launch_forward(const FwdArgs& a, const Modes& m, int n_items, hipStream_t s);
+hipError_t launch_forward_combine(const FwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
+hipError_t launch_bwd_preprocess(const BwdArgs& a, const Modes& m, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n_items, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n_items, hipStream_t s);
+hipError_t launch_bwd_reduce_dq(const BwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
+hipError_t launch_bwd_reduce_dkdv(const BwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
+
+// Resident workgroups per CU of each kernel for the given modes (occupancy query).
+int occupancy_forward(const Modes& m);
+int occupancy_dq(const Modes& m);
+int occupancy_dkdv(const Modes& m);
+
+}  // namespace jfa

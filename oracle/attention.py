@@ -224,3 +224,32 @@ def backward(q, k, v, q_off, kv_off, dout, *, mask="none", act="softmax", bias_k
             dk[ks:ke, h] = dK
             dv[ks:ke, h] = dV
     return dq, dk, dv, dbias
+
+
+def gdpa_magnitude(q, k, v, q_off, kv_off, *, mask="none", act="silu", bias_kind="none", bias=None,
+                   scale: Optional[float] = None, seqs=None, heads=None):
+    """(1 / Lkv_b) sum_vis |act(s_ij)| |V_jd|: the scale of each GDPA output element.
+
+    Rounding act(s) to a bfloat16 matrix operand changes output element (i, d) by at most the unit
+    roundoff 2^-8 times this magnitude; GPU tolerances for GDPA use it.
+    """
+    if act == "softmax":
+        raise ValueError("GDPA only")
+    q_off, kv_off = _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias)
+    Tq, H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out = np.full((Tq, H, D), np.nan)
+    f, _ = _ACTS[act]
+    for b in _select(len(q_off) - 1, seqs):
+        qs, qe, ks, ke = q_off[b], q_off[b + 1], kv_off[b], kv_off[b + 1]
+        lq, lkv = qe - qs, ke - ks
+        for h in _select(H, heads):
+            K, V = k[ks:ke, h], np.abs(v[ks:ke, h])
+            bias_h = None if bias is None else np.asarray(bias, dtype=np.float64)[h]
+            for i0, i1 in _chunks(lq, lkv):
+                S, vis, _ = _scores(q[qs + i0:qs + i1, h], K, i0, scale, mask, bias_kind, bias_h)
+                Aa = np.where(vis, np.abs(f(S)), 0.0)
+                out[qs + i0:qs + i1, h] = (Aa @ V) / lkv if lkv > 0 else 0.0
+    return out
+

@@ -1,0 +1,140 @@
+"""The C ABI on the CPU: exported symbols, host-only schedules vs the spec, argument checks.
+
+No compute call is made here (no GPU): plans are built with JFA_PLAN_HOST_ONLY.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import jfa_inputs as ji
+from oracle import schedule as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+B = pytest.importorskip("jagged_sequence_amd.binding", reason="libjfa.so not built")
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "jfa.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:jfa_status|void|const char\*)\s+(jfa_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(B.LIB, n), n
+    assert sorted(B.SYMBOLS) == names
+
+
+def test_status_strings():
+    for code, name in B.STATUS_NAMES.items():
+        assert B.LIB.jfa_status_string(code).decode() == name
+
+
+def _host_plan(lq, lkv, H, D=128, **kw):
+    return B.Plan(ji.offsets(lq), ji.offsets(lkv), H, D, host_only=True, **kw)
+
+
+CASES = [
+    ([5, 130, 0, 257, 64], [5, 130, 0, 257, 64], "causal"),
+    ([1, 40, 3, 64, 0], [300, 17, 0, 1000, 9], "none"),
+    ([700, 129, 1, 128, 256], [700, 129, 1, 128, 256], "causal"),
+    ([2000], [2000], "causal"),
+]
+
+
+def _compare(plan, lq, lkv, H, causal, slots, split):
+    info = plan.info()
+    fi, fg, _ = S.query_tile_items(lq, lkv, H, causal, info["fwd_bm"], info["fwd_bn"], slots, split)
+    qi, qg, _ = S.query_tile_items(lq, lkv, H, causal, info["dq_bm"], info["dq_bn"], slots, split)
+    ki, kg, _ = S.key_tile_items(lq, lkv, H, causal, info["kv_bm"], info["kv_bn"], slots, split)
+    for which, expect in enumerate([fi, fg, qi, qg, ki, kg]):
+        got = plan.schedule(which)
+        np.testing.assert_array_equal(got, np.array(expect, dtype=np.int32).reshape(got.shape), err_msg=str(which))
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("slots", [1, 3, 64, 512])
+@pytest.mark.parametrize("split", [True, False])
+def test_schedule_bit_exact_vs_spec(case, slots, split):
+    lq, lkv, mask = CASES[case]
+    plan = _host_plan(lq, lkv, 3, mask=mask, num_slots=slots, no_split=not split)
+    assert plan.info()["fwd_slots"] == slots
+    _compare(plan, lq, lkv, 3, mask == "causal", slots, split)
+
+
+@pytest.mark.parametrize("name", ["small_fwd", "causal_bucket", "target_attn", "gdpa_silu", "longtail"])
+def test_workload_schedules_bit_exact(name):
+    w = ji.WORKLOADS[name]
+    lq, lkv = ji.lengths(w)
+    plan = _host_plan(lq, lkv, w.H, w.D, mask=w.mask, act=w.act, bias=w.bias)
+    assert plan.info()["fwd_slots"] == 512
+    _compare(plan, lq, lkv, w.H, w.mask == "causal", 512, True)
+
+
+def test_workspace_sizes():
+    lq = [700, 129, 1]
+    plan = _host_plan(lq, lq, 2, mask="causal", num_slots=16)
+    fwd, bwd = plan.workspace_bytes()
+    nf = sum(R for (*_g, R) in plan.schedule(1))
+    nq = sum(R for (*_g, R) in plan.schedule(3))
+    nk = sum(R for (*_g, R) in plan.schedule(5))
+    al = lambda x: (x + 255) // 256 * 256
+    assert nf > 0 and nq > 0 and nk > 0
+    assert fwd == al(nf * 128 * 128 * 4) + al(nf * 128 * 4)
+    assert bwd == al(2 * 830 * 4) + al(nq * 128 * 128 * 4) + 2 * al(nk * 128 * 128 * 4)
+    plan2 = _host_plan(lq, lq, 2, mask="causal", num_slots=4, no_split=True, act="silu")
+    assert plan2.workspace_bytes() == (0, 0)
+
+
+def _status_of(fn):
+    with pytest.raises(B.JfaError) as e:
+        fn()
+    return B.STATUS_NAMES[e.value.status]
+
+
+def test_plan_validation_errors():
+    ok = ([3, 4], [3, 4])
+    assert _status_of(lambda: _host_plan(*ok, 2, D=96)) == "JFA_ERR_BAD_SHAPE"
+    assert _status_of(lambda: _host_plan(*ok, 0)) == "JFA_ERR_BAD_SHAPE"
+    assert _status_of(lambda: B.Plan([0], [0], 2, 64, host_only=True)) == "JFA_ERR_BAD_SHAPE"
+    assert _status_of(lambda: B.Plan([1, 3], [0, 3], 2, 64, host_only=True)) == "JFA_ERR_BAD_OFFSETS"
+    assert _status_of(lambda: B.Plan([0, 3, 2], [0, 3, 4], 2, 64, host_only=True)) == "JFA_ERR_BAD_OFFSETS"
+    assert _status_of(lambda: _host_plan([3, 4], [3, 5], 2, mask="causal")) == "JFA_ERR_BAD_SHAPE"
+    assert _status_of(lambda: _host_plan(*ok, 2, num_slots=-1)) == "JFA_ERR_BAD_SHAPE"
+    assert _status_of(lambda: _host_plan(*ok, 2, scale=float("nan"))) == "JFA_ERR_UNSUPPORTED"
+    # causal with equal lengths and an empty sequence is fine
+    _host_plan([3, 0, 4], [3, 0, 4], 2, mask="causal")
+
+
+def test_raw_abi_null_and_enum_errors():
+    lib = B.LIB
+    h = ctypes.c_void_p()
+    assert lib.jfa_plan(None, None, ctypes.byref(h)) == 1  # JFA_ERR_NULL_ARG
+    off = np.array([0, 3], dtype=np.int32)
+    p = B.Problem()
+    p.num_seqs, p.num_heads, p.head_dim = 1, 1, 64
+    p.q_offsets_host = off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    p.kv_offsets_host = None
+    p.flags = B.PLAN_HOST_ONLY
+    assert lib.jfa_plan(ctypes.byref(p), None, ctypes.byref(h)) == 1
+    p.kv_offsets_host = off.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    for field, bad in [("mask", 2), ("act", 3), ("bias", 7), ("out_dtype", 2)]:
+        setattr(p, field, bad)
+        assert lib.jfa_plan(ctypes.byref(p), None, ctypes.byref(h)) == 4, field  # UNSUPPORTED
+        setattr(p, field, 0)
+    p.flags = B.PLAN_HOST_ONLY | 0x80
+    assert lib.jfa_plan(ctypes.byref(p), None, ctypes.byref(h)) == 4
+    p.flags = B.PLAN_HOST_ONLY
+    assert lib.jfa_plan(ctypes.byref(p), None, ctypes.byref(h)) == 0
+    # a host-only plan refuses to launch, before touching any pointer
+    assert lib.jfa_forward(h, *([None] * 8), None, 0, None) == 8
+    assert b"host-only" in lib.jfa_last_error()
+    assert lib.jfa_backward(h, *([None] * 13), None, 0, None) == 8
+    assert lib.jfa_forward(None, *([None] * 8), None, 0, None) == 1
+    lib.jfa_plan_destroy(h)
+    lib.jfa_plan_destroy(None)

@@ -1,0 +1,139 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element by element."""
+import numpy as np
+import pytest
+import torch
+
+import jfa_inputs as ji
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU hosts, skipped there
+    pytest.skip("no GPU", allow_module_level=True)
+
+from tests.gpu_util import compare, oracle, run_gpu, say, to_np  # noqa: E402
+
+# lengths spanning several 64/128 tiles with ragged tails, one single-token sequence
+SELF_LENS = [1, 37, 130, 257]
+CROSS_Q = [1, 37, 130, 64]
+CROSS_KV = [5, 300, 64, 129]
+MODES = [(D, m, a, b) for D in (64, 128) for m in ("none", "causal") for a in ("softmax", "silu", "gelu_tanh")
+         for b in ("none", "scalar", "bucket")]
+
+
+@pytest.mark.parametrize("D,mask,act,bias", MODES, ids=["-".join(map(str, m)) for m in MODES])
+def test_tiny_all_modes(D, mask, act, bias):
+    lq, lkv = (SELF_LENS, SELF_LENS) if mask == "causal" else (CROSS_Q, CROSS_KV)
+    x = ji.make_inputs(lq, lkv, 2, D, wid=40, mask=mask, act=act, bias_kind=bias, bias_sigma=0.5)
+    say(f"case tiny D={D} mask={mask} act={act} bias={bias}")
+    gpu = run_gpu(x)
+    rep = compare(x, gpu, oracle(x))
+    say(f"  {rep}")
+
+
+@pytest.mark.parametrize("act", ["softmax", "silu"])
+@pytest.mark.parametrize("slots", [16, 64])
+def test_forced_split_matches_oracle_and_unsplit(act, slots):
+    lens = [700, 129, 1, 300]
+    x = ji.make_inputs(lens, lens, 2, 128, wid=41, mask="causal", act=act, bias_kind="bucket", bias_sigma=0.5)
+    say(f"case split act={act} slots={slots}")
+    g1 = run_gpu(x, num_slots=slots)
+    assert len(g1["plan"].schedule(1)) > 0 and len(g1["plan"].schedule(3)) > 0 and len(g1["plan"].schedule(5)) > 0
+    g0 = run_gpu(x, no_split=True)
+    assert len(g0["plan"].schedule(1)) == 0
+    compare(x, g1, oracle(x))
+    # a split piece rounds P to bf16 against its own running max, so the two paths agree to the
+    # bf16 operand rounding (unit roundoff 2^-8), not to fp32 rounding
+    for name in ["out", "dq", "dk", "dv"]:
+        a, b = to_np(g1[name]), to_np(g0[name])
+        d = float(np.abs(a - b).max())
+        assert d <= 2.0 ** -8 * max(1.0, float(np.abs(b).max())), f"{name}: split vs unsplit differ by {d}"
+
+
+def test_bf16_outputs():
+    lens = [300, 45, 128]
+    x = ji.make_inputs(lens, lens, 3, 128, wid=42, mask="causal", act="softmax", bias_kind="bucket")
+    say("case bf16 outputs")
+    gpu = run_gpu(x, out_dtype="bf16", grad_dtype="bf16")
+    assert gpu["out"].dtype == torch.bfloat16 and gpu["dq"].dtype == torch.bfloat16
+    compare(x, gpu, oracle(x), out_bf16=True)
+
+
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh"])
+def test_empty_sequences(act):
+    lq, lkv = [3, 0, 70, 0], [0, 40, 65, 0]
+    x = ji.make_inputs(lq, lkv, 2, 64, wid=43, act=act, bias_kind="scalar")
+    say(f"case empty act={act}")
+    gpu = run_gpu(x)
+    ref = oracle(x)
+    assert np.all(to_np(gpu["out"])[:3] == 0.0)
+    if act == "softmax":
+        assert np.all(np.isneginf(to_np(gpu["lse"])[:, :3]))
+    assert np.all(to_np(gpu["dq"])[:3] == 0.0) and np.all(to_np(gpu["dk"])[:40] == 0.0)
+    compare(x, gpu, ref)
+
+
+def test_deterministic_and_no_out_of_range_writes():
+    lens = [500, 3, 260]
+    x = ji.make_inputs(lens, lens, 2, 128, wid=44, mask="causal", bias_kind="bucket")
+    say("case determinism + canaries")
+    a = run_gpu(x, num_slots=5)
+    b = run_gpu(x, num_slots=5)
+    for name in ["out", "lse", "dq", "dk", "dv"]:
+        assert torch.equal(a[name], b[name]), name
+    # canary bands around every output: the kernels must write inside their tensors only
+    from jagged_sequence_amd import binding as J
+    from tests.gpu_util import to_dev
+    plan = a["plan"]
+    q, k, v, do = to_dev(x.q), to_dev(x.k), to_dev(x.v), to_dev(x.do)
+    qo, ko = torch.from_numpy(x.q_off).cuda(), torch.from_numpy(x.kv_off).cuda()
+    bias = torch.from_numpy(x.bias).cuda()
+    n = x.q.size
+    band = 4096
+
+    def guarded(numel):
+        t = torch.full((numel + 2 * band,), 1234.5, dtype=torch.float32, device="cuda")
+        return t, t[band:band + numel]
+
+    out_g, out = guarded(n)
+    lse_g, lse = guarded(x.H * len(x.q))
+    dq_g, dq = guarded(n)
+    dk_g, dk = guarded(x.k.size)
+    dv_g, dv = guarded(x.v.size)
+    out = out.view(x.q.shape)
+    plan.forward(q, k, v, qo, ko, bias, out=out, lse=lse.view(x.H, -1))
+    plan.backward(q, k, v, qo, ko, bias, out, lse.view(x.H, -1), do, dq=dq.view(x.q.shape), dk=dk.view(x.k.shape),
+                  dv=dv.view(x.v.shape))
+    torch.cuda.synchronize()
+    for g in [out_g, lse_g, dq_g, dk_g, dv_g]:
+        assert torch.all(g[:band] == 1234.5) and torch.all(g[-band:] == 1234.5)
+    assert torch.equal(out, a["out"]) and torch.equal(dk.view(x.k.shape), a["dk"])
+
+
+def test_small_workload_forward():
+    x = ji.workload_inputs("small_fwd")
+    say("case workload small_fwd")
+    gpu = run_gpu(x, backward=False)
+    rep = compare(x, gpu, oracle(x, backward=False), backward=False)
+    gpu16 = run_gpu(x, backward=False, out_dtype="bf16")
+    compare(x, gpu16, oracle(x, backward=False), backward=False, out_bf16=True)
+    say(f"  {rep}")
+
+
+def _sample(lq, n_random, seed):
+    order = np.argsort(lq)
+    rng = np.random.default_rng(seed)
+    pick = {int(order[-1]), int(order[0])} | set(rng.choice(len(lq), size=n_random, replace=False).tolist())
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", ["causal_bucket", "target_attn", "gdpa_silu", "gdpa_gelu"])
+def test_full_size_workloads_sampled(name):
+    """Full-size run in the benchmark's launch configuration; the oracle checks sampled sequences."""
+    x = ji.workload_inputs(name)
+    lq, _ = ji.lengths(ji.WORKLOADS[name])
+    seqs = _sample(lq, 3, 7)
+    say(f"case workload {name} seqs={seqs}")
+    gpu = run_gpu(x, out_dtype="bf16", grad_dtype="bf16")
+    ref = oracle(x, seqs=seqs)
+    rep = compare(x, gpu, ref, seqs=seqs, out_bf16=True, plain=True)
+    say(f"  {rep}")

@@ -215,3 +215,18 @@ def test_subset_selection_matches_full():
     s, e = x.q_off[1], x.q_off[2]
     np.testing.assert_array_equal(sub[s:e][:, [0, 2]], full[s:e][:, [0, 2]])
     assert np.all(np.isnan(sub[:s])) and np.all(np.isnan(sub[s:e, 1]))
+
+
+def test_gdpa_magnitude_bounds_output():
+    x, q, k, v, _ = _mk([5, 9], [7, 4], act="silu", bias_kind="bucket")
+    for act in ["silu", "gelu_tanh"]:
+        out, _ = A.forward(q, k, v, x.q_off, x.kv_off, act=act, bias_kind="bucket", bias=x.bias)
+        mag = A.gdpa_magnitude(q, k, v, x.q_off, x.kv_off, act=act, bias_kind="bucket", bias=x.bias)
+        assert np.all(mag >= np.abs(out) - 1e-15)
+    # every term non-negative: Q = 0 and a positive scalar bias give act(c) > 0; V >= 0
+    q0 = np.zeros_like(q)
+    va = np.abs(v)
+    c = np.array([0.8, 1.5])
+    out, _ = A.forward(q0, k, va, x.q_off, x.kv_off, act="gelu_tanh", bias_kind="scalar", bias=c)
+    mag = A.gdpa_magnitude(q0, k, va, x.q_off, x.kv_off, act="gelu_tanh", bias_kind="scalar", bias=c)
+    np.testing.assert_allclose(mag, out, rtol=1e-14)
