@@ -56,7 +56,8 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdArgs a) {
 }
 
 // 4 rows x 8 dims of a [T, H, D] tensor: loaded so that one thread can store them both row-major
-// (4 x 16 bytes) and transposed (8 x 8 bytes).
+// (4 x 16 bytes) and transposed (8 x 8 bytes). Lanes take consecutive row groups (g fastest), so the
+// transposed 8-byte writes of a wave spread over all LDS banks.
 template <int D, int ROWS>
 struct Units {
   static constexpr int CPR = D / 8;
@@ -65,25 +66,22 @@ struct Units {
 };
 
 template <int D, int ROWS>
-__device__ __forceinline__ void load_units(Units<D, ROWS>& u, const uint16_t* base, int rs, int row0, int limit,
-                                           int tid) {
+__device__ __forceinline__ void load_units(Units<D, ROWS>& u, __amdgpu_buffer_rsrc_t src, int rs, int row0, int tid) {
   constexpr int CPR = D / 8, N = Units<D, ROWS>::N;
+  constexpr int G = ROWS / 4;
   if (N >= kThreads || tid < N) {
-    const int dg = tid % CPR, g = tid / CPR;
+    const int g = tid % G, dg = tid / G;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = row0 + 4 * g + j;
-      u.r[j] = row < limit ? load16(base + (size_t)row * rs + dg * 8) : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j) u.r[j] = buf_load16(src, (uint32_t)((row0 + 4 * g + j) * rs + dg * 8) * 2u);
   }
 }
 
 template <int D, int ROWS>
 __device__ __forceinline__ void store_units(const Units<D, ROWS>& u, __bf16* rowmajor, int RS, __bf16* trans, int TS,
                                             int tid) {
-  constexpr int CPR = D / 8, N = Units<D, ROWS>::N;
+  constexpr int N = Units<D, ROWS>::N, G = ROWS / 4;
   if (N >= kThreads || tid < N) {
-    const int dg = tid % CPR, g = tid / CPR;
+    const int g = tid % G, dg = tid / G;
     if (rowmajor) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&rowmajor[(4 * g + j) * RS + dg * 8]) = u.r[j];
@@ -103,6 +101,7 @@ struct alignas(16) DqSmem {
   __bf16 kt[D * TS];
   __bf16 v[kDqBN * RS];
   float tab[kBuckets];
+  float diag[4][kDiagLen];
 };
 
 template <int D, int ACT, int BIAS, bool CAUSAL>
@@ -122,24 +121,26 @@ void bwd_dq_kernel(BwdArgs a) {
   const int row0 = t * BM + wave * 32;
   const int qi = row0 + l32;
 
-  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid] * (SOFTMAX ? kLog2e : 1.0f);
+  const float inv_scale = 1.0f / a.scale;
+  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
+  const float acc0 = (BIAS == kBiasScalar && !SOFTMAX) ? bias_c * inv_scale : 0.0f;
 
   bf16x8 qf[NKB], df[NKB];
   {
-    const size_t off = (size_t)(qs + qi) * rs + h * D + hh * 8;
+    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+    const __amdgpu_buffer_rsrc_t gr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      uint4 w = qi < Lq ? load16(a.q + off + kb * 16) : make_uint4(0, 0, 0, 0);
-      uint4 g = qi < Lq ? load16(a.dout + off + kb * 16) : make_uint4(0, 0, 0, 0);
-      qf[kb] = __builtin_bit_cast(bf16x8, w);
-      df[kb] = __builtin_bit_cast(bf16x8, g);
+      const uint32_t off = (uint32_t)(qi * rs + kb * 16 + hh * 8) * 2u;
+      qf[kb] = as_bf16x8(buf_load16(qr, off));
+      df[kb] = as_bf16x8(buf_load16(gr, off));
     }
   }
-  float lse2 = __builtin_huge_valf(), dlt = 0.0f;
+  float nlse2 = kNegInf, dlt = 0.0f;  // -lse in log2 units; -inf makes every P of the row 0
   if (SOFTMAX && qi < Lq) {
     const float l = a.lse[(size_t)h * a.Tq + qs + qi];
-    lse2 = l == kNegInf ? __builtin_huge_valf() : (l - (BIAS == kBiasScalar ? bias_c : 0.0f)) * kLog2e;
+    nlse2 = l == kNegInf ? kNegInf : -(l - (BIAS == kBiasScalar ? bias_c : 0.0f)) * kLog2e;
     dlt = a.delta[(size_t)h * a.Tq + qs + qi];
   }
   const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
@@ -149,35 +150,46 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) qacc[db] = f32x16{};
 
-  const uint16_t* kbase = a.k + (size_t)ks * rs + h * D;
-  const uint16_t* vbase = a.v + (size_t)ks * rs + h * D;
+  const __amdgpu_buffer_rsrc_t kr = slice_rsrc(a.k + (size_t)ks * rs + h * D, Lkv, rs, D);
+  const __amdgpu_buffer_rsrc_t vr = slice_rsrc(a.v + (size_t)ks * rs + h * D, Lkv, rs, D);
   Units<D, kDqBN> uk, uv;
   if (k0 < k1) {
-    load_units<D, kDqBN>(uk, kbase, rs, k0 * BN, Lkv, tid);
-    load_units<D, kDqBN>(uv, vbase, rs, k0 * BN, Lkv, tid);
+    load_units<D, kDqBN>(uk, kr, rs, k0 * BN, tid);
+    load_units<D, kDqBN>(uv, vr, rs, k0 * BN, tid);
   }
   for (int kt = k0; kt < k1; ++kt) {
+    const int key0 = kt * BN;
     __syncthreads();
     store_units<D, kDqBN>(uk, sm.k, RS, sm.kt, TS, tid);
     store_units<D, kDqBN>(uv, sm.v, RS, nullptr, 0, tid);
+    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, row0 - key0 - (BN - 1), inv_scale, lane);
     __syncthreads();
     if (kt + 1 < k1) {
-      load_units<D, kDqBN>(uk, kbase, rs, (kt + 1) * BN, Lkv, tid);
-      load_units<D, kDqBN>(uv, vbase, rs, (kt + 1) * BN, Lkv, tid);
+      load_units<D, kDqBN>(uk, kr, rs, (kt + 1) * BN, tid);
+      load_units<D, kDqBN>(uv, vr, rs, (kt + 1) * BN, tid);
     }
-    const int key0 = kt * BN;
 
     f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-      sacc[sb] = f32x16{};
+      if (BIAS == kBiasBucket) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float* dv = &sm.diag[wave][63 - 32 * sb + l32 - 16 * c - 8 * hh];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sacc[sb][8 * c + j] = dv[-j];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sb][r] = acc0;
+      }
       pacc[sb] = f32x16{};
-      const __bf16* kr = &sm.k[(32 * sb + kappa(l32)) * RS + hh * 8];
-      const __bf16* vr = &sm.v[(32 * sb + kappa(l32)) * RS + hh * 8];
+      const __bf16* kp = &sm.k[(32 * sb + kappa(l32)) * RS + hh * 8];
+      const __bf16* vp = &sm.v[(32 * sb + kappa(l32)) * RS + hh * 8];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        sacc[sb] = mfma32(lds_load8(kr + kb * 16), qf[kb], sacc[sb]);
-        pacc[sb] = mfma32(lds_load8(vr + kb * 16), df[kb], pacc[sb]);
+        sacc[sb] = mfma32(lds_load8(kp + kb * 16), qf[kb], sacc[sb]);
+        pacc[sb] = mfma32(lds_load8(vp + kb * 16), df[kb], pacc[sb]);
       }
     }
 
@@ -187,21 +199,20 @@ void bwd_dq_kernel(BwdArgs a) {
     for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 32 * sb + acc_row(r, hh);
-        float x = sacc[sb][r] * smul;
-        if (BIAS == kBiasBucket) x += sm.tab[rel_bucket(qi - key)];
-        if (BIAS == kBiasScalar && !SOFTMAX) x += bias_c;
-        const bool masked = need_mask && (key >= Lkv || (CAUSAL && key > qi));
         float d;
         if (SOFTMAX) {
-          const float p = fast_exp2(x - lse2);
+          const float p = fast_exp2(__builtin_fmaf(sacc[sb][r], smul, nlse2));
           d = p * (pacc[sb][r] - dlt);
         } else {
           float f, g;
-          act_fwd_grad<ACT>(x, f, g);
+          act_fwd_grad<ACT>(sacc[sb][r] * smul, f, g);
           d = pacc[sb][r] * g * invL;
         }
-        ds[sb][r] = masked ? 0.0f : d;
+        if (need_mask) {
+          const int key = key0 + 32 * sb + acc_row(r, hh);
+          d = (key >= Lkv || (CAUSAL && key > qi)) ? 0.0f : d;
+        }
+        ds[sb][r] = d;
       }
     }
     bf16x8 dsb[4];
@@ -209,9 +220,9 @@ void bwd_dq_kernel(BwdArgs a) {
     for (int c = 0; c < 4; ++c) dsb[c] = pack8(&ds[c >> 1][8 * (c & 1)]);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const __bf16* kr = &sm.kt[(32 * db + l32) * TS + 8 * hh];
+      const __bf16* kp = &sm.kt[(32 * db + l32) * TS + 8 * hh];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qacc[db] = mfma32(lds_load8(kr + 16 * c), dsb[c], qacc[db]);
+      for (int c = 0; c < 4; ++c) qacc[db] = mfma32(lds_load8(kp + 16 * c), dsb[c], qacc[db]);
     }
   }
 
@@ -248,6 +259,7 @@ struct alignas(16) KvSmem {
   float lse2[kKvBM];
   float dlt[kKvBM];
   float tab[kBuckets];
+  float diag[4][kDiagLen];
 };
 
 template <int D, int ACT, int BIAS, bool CAUSAL>
@@ -267,18 +279,20 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int key_w = kt * BN + wave * 32;  // first key of this wave
   const int kj = key_w + l32;
 
-  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid] * (SOFTMAX ? kLog2e : 1.0f);
+  const float inv_scale = 1.0f / a.scale;
+  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
+  const float acc0 = (BIAS == kBiasScalar && !SOFTMAX) ? bias_c * inv_scale : 0.0f;
 
   bf16x8 kf[NKB], vf[NKB];
   {
-    const size_t off = (size_t)(ks + kj) * rs + h * D + hh * 8;
+    const __amdgpu_buffer_rsrc_t kr = slice_rsrc(a.k + (size_t)ks * rs + h * D, Lkv, rs, D);
+    const __amdgpu_buffer_rsrc_t vr = slice_rsrc(a.v + (size_t)ks * rs + h * D, Lkv, rs, D);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      uint4 w = kj < Lkv ? load16(a.k + off + kb * 16) : make_uint4(0, 0, 0, 0);
-      uint4 x = kj < Lkv ? load16(a.v + off + kb * 16) : make_uint4(0, 0, 0, 0);
-      kf[kb] = __builtin_bit_cast(bf16x8, w);
-      vf[kb] = __builtin_bit_cast(bf16x8, x);
+      const uint32_t off = (uint32_t)(kj * rs + kb * 16 + hh * 8) * 2u;
+      kf[kb] = as_bf16x8(buf_load16(kr, off));
+      vf[kb] = as_bf16x8(buf_load16(vr, off));
     }
   }
   const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
@@ -292,28 +306,29 @@ void bwd_dkdv_kernel(BwdArgs a) {
     dv[db] = f32x16{};
   }
 
-  const uint16_t* qbase = a.q + (size_t)qs * rs + h * D;
-  const uint16_t* gbase = a.dout + (size_t)qs * rs + h * D;
+  const __amdgpu_buffer_rsrc_t qsr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+  const __amdgpu_buffer_rsrc_t gsr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
   Units<D, kKvBM> uq, ug;
   float pl = 0.0f, pd = 0.0f;
   auto load_stats = [&](int qt) {
     if (SOFTMAX && tid < BM) {
       const int q = qt * BM + tid;
-      pl = __builtin_huge_valf();
+      pl = kNegInf;  // -lse in log2 units; -inf makes P of rows past the end 0
       pd = 0.0f;
       if (q < Lq) {
         const float l = a.lse[(size_t)h * a.Tq + qs + q];
-        pl = l == kNegInf ? __builtin_huge_valf() : (l - lse_shift) * kLog2e;
+        pl = l == kNegInf ? kNegInf : -(l - lse_shift) * kLog2e;
         pd = a.delta[(size_t)h * a.Tq + qs + q];
       }
     }
   };
   if (q0 < q1) {
-    load_units<D, kKvBM>(uq, qbase, rs, q0 * BM, Lq, tid);
-    load_units<D, kKvBM>(ug, gbase, rs, q0 * BM, Lq, tid);
+    load_units<D, kKvBM>(uq, qsr, rs, q0 * BM, tid);
+    load_units<D, kKvBM>(ug, gsr, rs, q0 * BM, tid);
     load_stats(q0);
   }
   for (int qt = q0; qt < q1; ++qt) {
+    const int qrow0 = qt * BM;
     __syncthreads();
     store_units<D, kKvBM>(uq, sm.q, RS, sm.qt, TS, tid);
     store_units<D, kKvBM>(ug, sm.g, RS, sm.gt, TS, tid);
@@ -321,83 +336,88 @@ void bwd_dkdv_kernel(BwdArgs a) {
       sm.lse2[tid] = pl;
       sm.dlt[tid] = pd;
     }
+    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, qrow0 - key_w - 31, inv_scale, lane);
     __syncthreads();
     if (qt + 1 < q1) {
-      load_units<D, kKvBM>(uq, qbase, rs, (qt + 1) * BM, Lq, tid);
-      load_units<D, kKvBM>(ug, gbase, rs, (qt + 1) * BM, Lq, tid);
+      load_units<D, kKvBM>(uq, qsr, rs, (qt + 1) * BM, tid);
+      load_units<D, kKvBM>(ug, gsr, rs, (qt + 1) * BM, tid);
       load_stats(qt + 1);
     }
-    const int qrow0 = qt * BM;
 
-    // S = Q K^T and dP = dO V^T for 64 queries x this wave's 32 keys: lane column = key kj,
-    // register r of block qb = query qrow0 + 32 qb + acc_row(r, hh).
-    f32x16 sacc[2], pacc[2];
+    // Two 32-query blocks, one after the other (keeps the score temporaries of one block live):
+    // S = Q K^T and dP = dO V^T with lane column = key kj and register r = query
+    // qrow0 + 32 qb + acc_row(r, hh); then dV += P^T dO and dK += dS^T Q over those 32 queries.
+    const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      sacc[qb] = f32x16{};
-      pacc[qb] = f32x16{};
-      const __bf16* qr = &sm.q[(32 * qb + kappa(l32)) * RS + hh * 8];
-      const __bf16* gr = &sm.g[(32 * qb + kappa(l32)) * RS + hh * 8];
+      f32x16 sacc, pacc = f32x16{};
+      if (BIAS == kBiasBucket) {
+        // d = qi - kj = (qrow0 - key_w - 31) + (31 + 32 qb + 16 c + 8 hh + j - l32)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float* dvp = &sm.diag[wave][31 + 32 * qb + 16 * c + 8 * hh - l32];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sacc[8 * c + j] = dvp[j];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = acc0;
+      }
+      const __bf16* qp = &sm.q[(32 * qb + kappa(l32)) * RS + hh * 8];
+      const __bf16* gp = &sm.g[(32 * qb + kappa(l32)) * RS + hh * 8];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        sacc[qb] = mfma32(lds_load8(qr + kb * 16), kf[kb], sacc[qb]);
-        pacc[qb] = mfma32(lds_load8(gr + kb * 16), vf[kb], pacc[qb]);
+        sacc = mfma32(lds_load8(qp + kb * 16), kf[kb], sacc);
+        pacc = mfma32(lds_load8(gp + kb * 16), vf[kb], pacc);
       }
-    }
 
-    const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0);
-    float p[2][16], ds[2][16];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int c8 = 0; c8 < 2; ++c8) {
         const int rbase = 32 * qb + 16 * c8 + 8 * hh;  // 8 consecutive query rows of this lane
-        float l8[8], d8[8];
+        float l8[8], d8[8], pv[8], dsv[8];
         if (SOFTMAX) {
-          float4 x0 = *reinterpret_cast<const float4*>(&sm.lse2[rbase]);
-          float4 x1 = *reinterpret_cast<const float4*>(&sm.lse2[rbase + 4]);
-          float4 y0 = *reinterpret_cast<const float4*>(&sm.dlt[rbase]);
-          float4 y1 = *reinterpret_cast<const float4*>(&sm.dlt[rbase + 4]);
+          const float4 x0 = *reinterpret_cast<const float4*>(&sm.lse2[rbase]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&sm.lse2[rbase + 4]);
+          const float4 y0 = *reinterpret_cast<const float4*>(&sm.dlt[rbase]);
+          const float4 y1 = *reinterpret_cast<const float4*>(&sm.dlt[rbase + 4]);
           l8[0] = x0.x; l8[1] = x0.y; l8[2] = x0.z; l8[3] = x0.w; l8[4] = x1.x; l8[5] = x1.y; l8[6] = x1.z; l8[7] = x1.w;
           d8[0] = y0.x; d8[1] = y0.y; d8[2] = y0.z; d8[3] = y0.w; d8[4] = y1.x; d8[5] = y1.y; d8[6] = y1.z; d8[7] = y1.w;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int r = 8 * c8 + j;
-          const int qi = qrow0 + rbase + j;
-          float x = sacc[qb][r] * smul;
-          if (BIAS == kBiasBucket) x += sm.tab[rel_bucket(qi - kj)];
-          if (BIAS == kBiasScalar && !SOFTMAX) x += bias_c;
-          const bool masked = (need_mask && (kj >= Lkv || (CAUSAL && kj > qi))) || (!SOFTMAX && qi >= Lq);
-          float pv, dv_;
+          float pj, dj;
           if (SOFTMAX) {
-            pv = fast_exp2(x - l8[j]);
-            dv_ = pv * (pacc[qb][r] - d8[j]);
+            pj = fast_exp2(__builtin_fmaf(sacc[r], smul, l8[j]));
+            dj = pj * (pacc[r] - d8[j]);
           } else {
             float f, g;
-            act_fwd_grad<ACT>(x, f, g);
-            pv = f * invL;
-            dv_ = pacc[qb][r] * g * invL;
+            act_fwd_grad<ACT>(sacc[r] * smul, f, g);
+            pj = f * invL;
+            dj = pacc[r] * g * invL;
           }
-          p[qb][r] = masked ? 0.0f : pv;
-          ds[qb][r] = masked ? 0.0f : dv_;
+          if (need_mask || !SOFTMAX) {
+            const int qi = qrow0 + rbase + j;
+            const bool masked = (need_mask && (kj >= Lkv || (CAUSAL && kj > qi))) || (!SOFTMAX && qi >= Lq);
+            pj = masked ? 0.0f : pj;
+            dj = masked ? 0.0f : dj;
+          }
+          pv[j] = pj;
+          dsv[j] = dj;
         }
+        pb[c8] = pack8(pv);
+        dsb[c8] = pack8(dsv);
       }
-    }
-    bf16x8 pb[4], dsb[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      pb[c] = pack8(&p[c >> 1][8 * (c & 1)]);
-      dsb[c] = pack8(&ds[c >> 1][8 * (c & 1)]);
-    }
+      for (int db = 0; db < NDB; ++db) {
+        const __bf16* gtp = &sm.gt[(32 * db + l32) * TS + 32 * qb + 8 * hh];
+        const __bf16* qtp = &sm.qt[(32 * db + l32) * TS + 32 * qb + 8 * hh];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const __bf16* gr = &sm.gt[(32 * db + l32) * TS + 8 * hh];
-      const __bf16* qr = &sm.qt[(32 * db + l32) * TS + 8 * hh];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        dv[db] = mfma32(lds_load8(gr + 16 * c), pb[c], dv[db]);
-        dk[db] = mfma32(lds_load8(qr + 16 * c), dsb[c], dk[db]);
+        for (int c8 = 0; c8 < 2; ++c8) {
+          dv[db] = mfma32(lds_load8(gtp + 16 * c8), pb[c8], dv[db]);
+          dk[db] = mfma32(lds_load8(qtp + 16 * c8), dsb[c8], dk[db]);
+        }
       }
     }
   }

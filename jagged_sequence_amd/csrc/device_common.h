@@ -61,10 +61,9 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // Relative-distance bucket: exact below 16, then four equal-width buckets per octave, capped at 63.
 __device__ __forceinline__ int rel_bucket(int d) {
   d = d < 0 ? -d : d;
-  if (d < 16) return d;
-  int e = 31 - __builtin_clz(d);
-  int b = 16 + 4 * (e - 4) + ((d >> (e - 2)) & 3);
-  return b < 63 ? b : 63;
+  const int e = 31 - __builtin_clz(d | 16);  // floor(log2 d) for d >= 16; the select below covers d < 16
+  const int b = 16 + 4 * (e - 4) + ((d >> (e - 2)) & 3);
+  return d < 16 ? d : (b < 63 ? b : 63);
 }
 
 // Score activations for GDPA. sigma(z) = 1 / (1 + 2^(-z log2 e)); SiLU(x) = x sigma(x);
@@ -111,6 +110,42 @@ __device__ __forceinline__ void store4(void* base, size_t idx, float a, float b,
 }
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Buffer resource over the rows of one (sequence, head) slice of a [T, H, D] bf16 tensor: `base`
+// points at row 0 of the slice, rows are `rs` elements apart and `rows` of them are valid. Loads
+// past the last valid row fall outside the resource's byte range and return zeros, so tails of
+// jagged sequences need no branch and never read a neighbouring sequence.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const uint16_t* base, int rows, int rs, int D) {
+  const uint32_t bytes = rows > 0 ? (uint32_t)((rows - 1) * rs + D) * 2u : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes at byte offset `off` of a buffer resource (zeros when out of range).
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+  u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
+
+// Keeps the compiler from moving LDS accesses of one wave across this point; the hardware
+// executes one wave's LDS instructions in order, so a wave may then read what it just wrote.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Per-wave diagonal bias vector. The relative-position bias of a 32-query x 64-key wave tile
+// depends only on d = i - j, which takes 95 consecutive values there. Each wave writes
+// vec[t] = T[bucket(|d0 + t|)] * mul for t in [0, 95) (two entries per lane) and then loads every
+// score's bias with plain LDS reads, no per-score bucket arithmetic.
+constexpr int kDiagLen = 96;
+__device__ __forceinline__ void fill_diag(float* vec, const float* tab, int d0, float mul, int lane) {
+  vec[lane] = tab[rel_bucket(d0 + lane)] * mul;
+  if (lane < kDiagLen - 64) vec[64 + lane] = tab[rel_bucket(d0 + 64 + lane)] * mul;
+}
 
 // Pack element e (0..7) of four 8-element bf16 rows into 4 consecutive bf16 (a column slice).
 __device__ __forceinline__ uint2 column4(const uint4 (&r)[4], int e) {

@@ -23,6 +23,7 @@ struct alignas(16) FwdSmem {
   __bf16 k[kFwdBN * KS];
   __bf16 vt[D * VS];
   float tab[kBuckets];
+  float diag[4][kDiagLen];
 };
 
 template <int D>
@@ -32,23 +33,21 @@ struct KvRegs {
   uint4 v[4];                                           // 4 keys x 8 dims, stored transposed
 };
 
+// Global -> registers for one 64-key tile. Rows past the sequence end read as zeros.
 template <int D>
-__device__ __forceinline__ void load_kv(KvRegs<D>& r, const uint16_t* kb, const uint16_t* vb, int rs, int key0,
-                                        int Lkv, int tid) {
+__device__ __forceinline__ void load_kv(KvRegs<D>& r, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int rs,
+                                        int key0, int tid) {
   constexpr int CPR = D / 8;
 #pragma unroll
   for (int u = 0; u < KvRegs<D>::KCH; ++u) {
-    int c = tid + kThreads * u, row = c / CPR, col = c % CPR, key = key0 + row;
-    r.k[u] = key < Lkv ? load16(kb + (size_t)key * rs + col * 8) : make_uint4(0, 0, 0, 0);
+    const int c = tid + kThreads * u, row = c / CPR, col = c % CPR;
+    r.k[u] = buf_load16(kr, (uint32_t)((key0 + row) * rs + col * 8) * 2u);
   }
-  constexpr int UNITS = (kFwdBN / 4) * CPR;
+  constexpr int UNITS = (kFwdBN / 4) * CPR, G = kFwdBN / 4;
   if (UNITS >= kThreads || tid < UNITS) {
-    int dg = tid % CPR, kg = tid / CPR;
+    const int kg = tid % G, dg = tid / G;  // key groups fastest: transposed LDS writes hit distinct banks
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int key = key0 + 4 * kg + j;
-      r.v[j] = key < Lkv ? load16(vb + (size_t)key * rs + dg * 8) : make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j) r.v[j] = buf_load16(vr, (uint32_t)((key0 + 4 * kg + j) * rs + dg * 8) * 2u);
   }
 }
 
@@ -57,17 +56,22 @@ __device__ __forceinline__ void store_kv(const KvRegs<D>& r, FwdSmem<D>& sm, int
   constexpr int CPR = D / 8, KS = FwdSmem<D>::KS, VS = FwdSmem<D>::VS;
 #pragma unroll
   for (int u = 0; u < KvRegs<D>::KCH; ++u) {
-    int c = tid + kThreads * u, row = c / CPR, col = c % CPR;
+    const int c = tid + kThreads * u, row = c / CPR, col = c % CPR;
     *reinterpret_cast<uint4*>(&sm.k[row * KS + col * 8]) = r.k[u];
   }
-  constexpr int UNITS = (kFwdBN / 4) * CPR;
+  constexpr int UNITS = (kFwdBN / 4) * CPR, G = kFwdBN / 4;
   if (UNITS >= kThreads || tid < UNITS) {
-    int dg = tid % CPR, kg = tid / CPR;
+    const int kg = tid % G, dg = tid / G;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       *reinterpret_cast<uint2*>(&sm.vt[(dg * 8 + e) * VS + 4 * kg]) = column4(r.v, e);
   }
 }
+
+// Softmax keeps a running row maximum m and rescales O and l only when a tile's maximum exceeds m
+// by more than 2^kLazy: otherwise probabilities are taken against the stale m (bounded by 2^kLazy,
+// exact in fp32 and as relative-precision bf16 operands), which skips most rescales.
+constexpr float kLazy = 8.0f;
 
 template <int D, int ACT, int BIAS, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
@@ -85,18 +89,18 @@ void fwd_kernel(FwdArgs a) {
   const int rs = a.H * D;
   const int row0 = t * BM + wave * 32;
   const int qi = row0 + l32;
+  const float inv_scale = 1.0f / a.scale;
 
-  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid] * (SOFTMAX ? kLog2e : 1.0f);
+  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
+  // the bias enters as the accumulator's initial value, in units of the unscaled score
+  const float acc0 = (BIAS == kBiasScalar && !SOFTMAX) ? bias_c * inv_scale : 0.0f;
 
   bf16x8 qf[NKB];
   {
-    const uint16_t* qp = a.q + (size_t)(qs + qi) * rs + h * D + hh * 8;
+    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      uint4 w = qi < Lq ? load16(qp + kb * 16) : make_uint4(0, 0, 0, 0);
-      qf[kb] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int kb = 0; kb < NKB; ++kb) qf[kb] = as_bf16x8(buf_load16(qr, (uint32_t)(qi * rs + kb * 16 + hh * 8) * 2u));
   }
 
   f32x16 o[NDB];
@@ -105,83 +109,99 @@ void fwd_kernel(FwdArgs a) {
   float m_run = kNegInf, l_run = 0.0f;
   const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
 
-  const uint16_t* kbase = a.k + (size_t)ks * rs + h * D;
-  const uint16_t* vbase = a.v + (size_t)ks * rs + h * D;
+  const __amdgpu_buffer_rsrc_t kr = slice_rsrc(a.k + (size_t)ks * rs + h * D, Lkv, rs, D);
+  const __amdgpu_buffer_rsrc_t vr = slice_rsrc(a.v + (size_t)ks * rs + h * D, Lkv, rs, D);
   KvRegs<D> pf;
-  if (k0 < k1) load_kv<D>(pf, kbase, vbase, rs, k0 * BN, Lkv, tid);
+  if (k0 < k1) load_kv<D>(pf, kr, vr, rs, k0 * BN, tid);
 
   for (int kt = k0; kt < k1; ++kt) {
+    const int key0 = kt * BN;
     __syncthreads();
     store_kv<D>(pf, sm, tid);
+    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, row0 - key0 - (BN - 1), inv_scale, lane);
     __syncthreads();
-    if (kt + 1 < k1) load_kv<D>(pf, kbase, vbase, rs, (kt + 1) * BN, Lkv, tid);
-    const int key0 = kt * BN;
+    if (kt + 1 < k1) load_kv<D>(pf, kr, vr, rs, (kt + 1) * BN, tid);
 
+    // S^T tile: lane = query qi, register r of block sb = key key0 + 32 sb + acc_row(r, hh).
     f32x16 sacc[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-      sacc[sb] = f32x16{};
-      const __bf16* kr = &sm.k[(32 * sb + kappa(l32)) * KS + hh * 8];
+      if (BIAS == kBiasBucket) {
+        // d = qi - key = (row0 - key0 - 63) + (63 - 32 sb + l32 - 16 c - 8 hh - j)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) sacc[sb] = mfma32(lds_load8(kr + kb * 16), qf[kb], sacc[sb]);
+        for (int c = 0; c < 2; ++c) {
+          const float* dv = &sm.diag[wave][63 - 32 * sb + l32 - 16 * c - 8 * hh];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sacc[sb][8 * c + j] = dv[-j];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sb][r] = acc0;
+      }
+      const __bf16* kp = &sm.k[(32 * sb + kappa(l32)) * KS + hh * 8];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sacc[sb] = mfma32(lds_load8(kp + kb * 16), qf[kb], sacc[sb]);
     }
 
     const bool need_mask = (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
-    float s[2][16];
+    if (need_mask) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 32 * sb + acc_row(r, hh);
-        float x = sacc[sb][r] * smul;
-        if (BIAS == kBiasBucket) x += sm.tab[rel_bucket(qi - key)];
-        if (BIAS == kBiasScalar && !SOFTMAX) x += bias_c;
-        const bool masked = need_mask && (key >= Lkv || (CAUSAL && key > qi));
-        if (SOFTMAX) {
-          s[sb][r] = masked ? kNegInf : x;
-        } else {
-          s[sb][r] = masked ? 0.0f : act_fwd<ACT>(x);
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * sb + acc_row(r, hh);
+          const bool masked = key >= Lkv || (CAUSAL && key > qi);
+          sacc[sb][r] = masked ? (SOFTMAX ? kNegInf : __builtin_nanf("")) : sacc[sb][r];
         }
-      }
     }
 
+    float p[2][16];
     if (SOFTMAX) {
       float mx = kNegInf;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == kNegInf ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * smul;
+      if (__ballot(mx > m_run + kLazy)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == kNegInf ? 0.0f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m_run = m_new;
+      }
+      const float nm = m_run == kNegInf ? 0.0f : -m_run;
       float lsum = 0.0f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(s[sb][r] - m_use);
-          s[sb][r] = p;
-          lsum += p;
+          const float e = fast_exp2(__builtin_fmaf(sacc[sb][r], smul, nm));
+          p[sb][r] = e;
+          lsum += e;
         }
-      l_run = l_run * alpha + lsum;
-      if (__ballot(alpha != 1.0f)) {
+      l_run += lsum;
+    } else {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
-      m_run = m_new;
+        for (int r = 0; r < 16; ++r) {
+          const float x = sacc[sb][r];
+          p[sb][r] = x != x ? 0.0f : act_fwd<ACT>(x * smul);  // masked scores carry NaN
+        }
     }
 
     bf16x8 pb[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) pb[c] = pack8(&s[c >> 1][8 * (c & 1)]);
+    for (int c = 0; c < 4; ++c) pb[c] = pack8(&p[c >> 1][8 * (c & 1)]);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const __bf16* vr = &sm.vt[(32 * db + l32) * VS + 8 * hh];
+      const __bf16* vp = &sm.vt[(32 * db + l32) * VS + 8 * hh];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[db] = mfma32(lds_load8(vr + 16 * c), pb[c], o[db]);
+      for (int c = 0; c < 4; ++c) o[db] = mfma32(lds_load8(vp + 16 * c), pb[c], o[db]);
     }
   }
 
