@@ -11,6 +11,7 @@
 //   GDPA:    P = act(s) / Lkv,   dP = <dO_i, v_j>, dS = dP act'(s) / Lkv
 //   dV_j += P dO_i,  dK_j += scale dS q_i,  dQ_i += scale dS k_j
 #include "device_common.h"
+#include "tile_lds.h"
 
 namespace jfa {
 namespace {
@@ -452,6 +453,207 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// D = 128 dK/dV with a two-stage LDS ring: Q and dO tiles are loaded straight into LDS (swizzled
+// row-major, no staging registers) one tile ahead of the compute, one barrier per tile; the Q^T and
+// dO^T operands of dK += dS^T Q and dV += P^T dO come from transposing LDS reads.
+struct alignas(16) KvSmem2 {
+  unsigned char qg[2][2][kKvBM * kRowBytes];  // [stage][0 = Q, 1 = dO]
+  float lse2[2][kKvBM];                       // -lse in log2 units (softmax)
+  float dlt[2][kKvBM];
+  float tab[kBuckets];
+  float diag[4][kDiagLen];
+};
+
+template <int ACT, int BIAS, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel2(BwdArgs a) {
+  constexpr int D = 128, BM = kKvBM, BN = kKvBN, NKB = D / 16, NDB = D / 32;
+  constexpr bool SOFTMAX = ACT == kSoftmax;
+  __shared__ KvSmem2 sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t* it = a.kv_items + (size_t)blockIdx.x * kItemInts;
+  const int b = it[0], h = it[1], kt = it[2], q0 = it[3], q1 = it[4], slot = it[5];
+  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
+  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const int rs = a.H * D;
+  const int key_w = kt * BN + wave * 32;  // first key of this wave
+  const int kj = key_w + l32;
+
+  const float inv_scale = 1.0f / a.scale;
+  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
+  const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
+  const float acc0 = (BIAS == kBiasScalar && !SOFTMAX) ? bias_c * inv_scale : 0.0f;
+
+  bf16x8 kf[NKB], vf[NKB];
+  {
+    const __amdgpu_buffer_rsrc_t kr = slice_rsrc(a.k + (size_t)ks * rs + h * D, Lkv, rs, D);
+    const __amdgpu_buffer_rsrc_t vr = slice_rsrc(a.v + (size_t)ks * rs + h * D, Lkv, rs, D);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const uint32_t off = (uint32_t)(kj * rs + kb * 16 + hh * 8) * 2u;
+      kf[kb] = as_bf16x8(buf_load16(kr, off));
+      vf[kb] = as_bf16x8(buf_load16(vr, off));
+    }
+  }
+  const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
+  const float invL = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
+  const float lse_shift = (SOFTMAX && BIAS == kBiasScalar) ? bias_c : 0.0f;
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  const __amdgpu_buffer_rsrc_t qsr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+  const __amdgpu_buffer_rsrc_t gsr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
+  const TileLoader ld = make_loader64(wave, lane, rs);
+  const uint32_t raddr = row_operand_base(kappa(l32), hh);
+  uint32_t T[2];
+  tr_operand_bases(lane, T);
+
+  float pl = kNegInf, pd = 0.0f;  // statistics of query row tid of the next tile (softmax)
+  auto load_stats = [&](int qt) {
+    if (SOFTMAX && tid < BM) {
+      const int q = qt * BM + tid;
+      pl = kNegInf;  // -lse in log2 units; -inf makes P of rows past the end 0
+      pd = 0.0f;
+      if (q < Lq) {
+        const float l = a.lse[(size_t)h * a.Tq + qs + q];
+        pl = l == kNegInf ? kNegInf : -(l - lse_shift) * kLog2e;
+        pd = a.delta[(size_t)h * a.Tq + qs + q];
+      }
+    }
+  };
+  if (q0 < q1) {
+    load_tile64(ld, qsr, q0 * BM, rs, sm.qg[0][0], wave);
+    load_tile64(ld, gsr, q0 * BM, rs, sm.qg[0][1], wave);
+    load_stats(q0);
+  }
+  for (int qt = q0; qt < q1; ++qt) {
+    const int qrow0 = qt * BM;
+    const int st = (qt - q0) & 1;
+    if (SOFTMAX && tid < BM) {
+      sm.lse2[st][tid] = pl;
+      sm.dlt[st][tid] = pd;
+    }
+    wait_vm();
+    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, qrow0 - key_w - 31, inv_scale, lane);
+    __syncthreads();
+    if (qt + 1 < q1) {
+      load_tile64(ld, qsr, (qt + 1) * BM, rs, sm.qg[st ^ 1][0], wave);
+      load_tile64(ld, gsr, (qt + 1) * BM, rs, sm.qg[st ^ 1][1], wave);
+      load_stats(qt + 1);
+    }
+    const unsigned char* Qt = sm.qg[st][0];
+    const unsigned char* Gt = sm.qg[st][1];
+    const float* lse2 = sm.lse2[st];
+    const float* dltv = sm.dlt[st];
+
+    const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 sacc, pacc = f32x16{};
+      if (BIAS == kBiasBucket) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float* dvp = &sm.diag[wave][31 + 32 * qb + 16 * c + 8 * hh - l32];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sacc[8 * c + j] = dvp[j];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = acc0;
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint32_t off = (raddr ^ (uint32_t)(kb << 5)) + qb * 32 * kRowBytes;
+        sacc = mfma32(lds_read16(Qt, off), kf[kb], sacc);
+        pacc = mfma32(lds_read16(Gt, off), vf[kb], pacc);
+      }
+
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int c8 = 0; c8 < 2; ++c8) {
+        const int rbase = 32 * qb + 16 * c8 + 8 * hh;  // 8 consecutive query rows of this lane
+        float l8[8], d8[8], pv[8], dsv[8];
+        if (SOFTMAX) {
+          const float4 x0 = *reinterpret_cast<const float4*>(&lse2[rbase]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&lse2[rbase + 4]);
+          const float4 y0 = *reinterpret_cast<const float4*>(&dltv[rbase]);
+          const float4 y1 = *reinterpret_cast<const float4*>(&dltv[rbase + 4]);
+          l8[0] = x0.x; l8[1] = x0.y; l8[2] = x0.z; l8[3] = x0.w; l8[4] = x1.x; l8[5] = x1.y; l8[6] = x1.z; l8[7] = x1.w;
+          d8[0] = y0.x; d8[1] = y0.y; d8[2] = y0.z; d8[3] = y0.w; d8[4] = y1.x; d8[5] = y1.y; d8[6] = y1.z; d8[7] = y1.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = 8 * c8 + j;
+          float pj, dj;
+          if (SOFTMAX) {
+            pj = fast_exp2(__builtin_fmaf(sacc[r], smul, l8[j]));
+            dj = pj * (pacc[r] - d8[j]);
+          } else {
+            float f, g;
+            act_fwd_grad<ACT>(sacc[r] * smul, f, g);
+            pj = f * invL;
+            dj = pacc[r] * g * invL;
+          }
+          if (need_mask || !SOFTMAX) {
+            const int qi = qrow0 + rbase + j;
+            const bool masked = (need_mask && (kj >= Lkv || (CAUSAL && kj > qi))) || (!SOFTMAX && qi >= Lq);
+            pj = masked ? 0.0f : pj;
+            dj = masked ? 0.0f : dj;
+          }
+          pv[j] = pj;
+          dsv[j] = dj;
+        }
+        pb[c8] = pack8(pv);
+        dsb[c8] = pack8(dsv);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int c8 = 0; c8 < 2; ++c8) {
+          const uint32_t base = (uint32_t)((32 * qb + 16 * c8) * kRowBytes);
+          const uint32_t o0 = base + (T[0] ^ (uint32_t)(64 * db)), o1 = base + (T[1] ^ (uint32_t)(64 * db));
+          dv[db] = mfma32(lds_read_tr(Gt, o0, o1), pb[c8], dv[db]);
+          dk[db] = mfma32(lds_read_tr(Qt, o0, o1), dsb[c8], dk[db]);
+        }
+    }
+  }
+
+  if (slot < 0) {
+    if (kj < Lkv) {
+      const size_t base = ((size_t)(ks + kj) * a.H + h) * D;
+      const float sc = a.scale;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const size_t i = base + 32 * db + 8 * g + 4 * hh;
+          store4(a.dk, i, dk[db][4 * g] * sc, dk[db][4 * g + 1] * sc, dk[db][4 * g + 2] * sc, dk[db][4 * g + 3] * sc,
+                 a.grad_f32);
+          store4(a.dv, i, dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3], a.grad_f32);
+        }
+    }
+  } else {
+    const size_t prow = (size_t)slot * BN + wave * 32 + l32;
+    float* pk = a.part_dk + prow * D;
+    float* pvp = a.part_dv + prow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i = 32 * db + 8 * g + 4 * hh;
+        *reinterpret_cast<float4*>(pk + i) = make_float4(dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]);
+        *reinterpret_cast<float4*>(pvp + i) = make_float4(dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
+      }
+  }
+}
+
 // ---------------------------------------------------------------- fixed-order partial sums
 // One workgroup per split group (b, h, tile, slot0, R); 2 threads per row, D/2 columns each.
 template <int D>
@@ -513,6 +715,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dispatch
+// D = 128 runs the LDS-ring kernels; D = 64 the register-staged ones.
+template <int D, int ACT, int BIAS, bool CAUSAL>
+constexpr auto dkdv_select = D == 128 ? &bwd_dkdv_kernel2<ACT, BIAS, CAUSAL> : &bwd_dkdv_kernel<D, ACT, BIAS, CAUSAL>;
+
 
 #define JFA_DISPATCH_MODES(KERNEL, m, n, s, a)                                                          \
   [&]() -> hipError_t {                                                                                 \
@@ -565,7 +771,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n, hipStream_t s)
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  return JFA_DISPATCH_MODES(bwd_dkdv_kernel, m, n, s, a);
+  return JFA_DISPATCH_MODES(dkdv_select, m, n, s, a);
 }
 
 hipError_t launch_bwd_reduce_dq(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
@@ -598,7 +804,7 @@ int occupancy_dkdv(const Modes& m) {
   int n = 0;
   hipError_t e = m.D == 64
                      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dkdv_kernel<64, kSoftmax, kBiasBucket, true>, kThreads, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dkdv_kernel<128, kSoftmax, kBiasBucket, true>, kThreads, 0);
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dkdv_kernel2<kSoftmax, kBiasBucket, true>, kThreads, 0);
   return (e == hipSuccess && n > 0) ? n : 1;
 }
 

@@ -12,6 +12,7 @@
 // The query of lane l is column l%32 of every accumulator, so row statistics reduce inside the
 // lane plus one exchange with lane l^32.
 #include "device_common.h"
+#include "tile_lds.h"
 
 namespace jfa {
 namespace {
@@ -241,6 +242,192 @@ void fwd_kernel(FwdArgs a) {
   }
 }
 
+// D = 128 forward with a two-stage LDS ring: K and V tiles are loaded straight into LDS
+// (swizzled row-major, no staging registers) one tile ahead of the compute, with one barrier per
+// tile; V^T operands come from transposing LDS reads of the row-major V tile.
+struct alignas(16) FwdSmem2 {
+  unsigned char kv[2][2][kFwdBN * kRowBytes];  // [stage][0 = K, 1 = V]
+  float tab[kBuckets];
+  float diag[4][kDiagLen];
+};
+
+template <int ACT, int BIAS, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void fwd_kernel2(FwdArgs a) {
+  constexpr int D = 128, BM = kFwdBM, BN = kFwdBN, NKB = D / 16, NDB = D / 32;
+  constexpr bool SOFTMAX = ACT == kSoftmax;
+  __shared__ FwdSmem2 sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t* it = a.items + (size_t)blockIdx.x * kItemInts;
+  const int b = it[0], h = it[1], t = it[2], k0 = it[3], k1 = it[4], slot = it[5];
+  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
+  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const int rs = a.H * D;
+  const int row0 = t * BM + wave * 32;
+  const int qi = row0 + l32;
+  const float inv_scale = 1.0f / a.scale;
+
+  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
+  const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
+  const float acc0 = (BIAS == kBiasScalar && !SOFTMAX) ? bias_c * inv_scale : 0.0f;
+
+  bf16x8 qf[NKB];
+  {
+    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) qf[kb] = as_bf16x8(buf_load16(qr, (uint32_t)(qi * rs + kb * 16 + hh * 8) * 2u));
+  }
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  float m_run = kNegInf, l_run = 0.0f;
+  const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
+
+  const __amdgpu_buffer_rsrc_t kr = slice_rsrc(a.k + (size_t)ks * rs + h * D, Lkv, rs, D);
+  const __amdgpu_buffer_rsrc_t vr = slice_rsrc(a.v + (size_t)ks * rs + h * D, Lkv, rs, D);
+  const TileLoader ld = make_loader64(wave, lane, rs);
+  const uint32_t kaddr = row_operand_base(kappa(l32), hh);  // K row kappa(l32) (+ 32 sb rows)
+  uint32_t T[2];
+  tr_operand_bases(lane, T);
+
+  if (k0 < k1) {
+    load_tile64(ld, kr, k0 * BN, rs, sm.kv[0][0], wave);
+    load_tile64(ld, vr, k0 * BN, rs, sm.kv[0][1], wave);
+  }
+  for (int kt = k0; kt < k1; ++kt) {
+    const int key0 = kt * BN;
+    const int st = (kt - k0) & 1;
+    wait_vm();
+    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, row0 - key0 - (BN - 1), inv_scale, lane);
+    __syncthreads();
+    if (kt + 1 < k1) {
+      load_tile64(ld, kr, (kt + 1) * BN, rs, sm.kv[st ^ 1][0], wave);
+      load_tile64(ld, vr, (kt + 1) * BN, rs, sm.kv[st ^ 1][1], wave);
+    }
+    const unsigned char* Kt = sm.kv[st][0];
+    const unsigned char* Vt = sm.kv[st][1];
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      if (BIAS == kBiasBucket) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float* dv = &sm.diag[wave][63 - 32 * sb + l32 - 16 * c - 8 * hh];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sacc[sb][8 * c + j] = dv[-j];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sb][r] = acc0;
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        sacc[sb] = mfma32(lds_read16(Kt, (kaddr ^ (uint32_t)(kb << 5)) + sb * 32 * kRowBytes), qf[kb], sacc[sb]);
+    }
+
+    const bool need_mask = (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
+    if (need_mask) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * sb + acc_row(r, hh);
+          const bool masked = key >= Lkv || (CAUSAL && key > qi);
+          sacc[sb][r] = masked ? (SOFTMAX ? kNegInf : __builtin_nanf("")) : sacc[sb][r];
+        }
+    }
+
+    float p[2][16];
+    if (SOFTMAX) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * smul;
+      if (__ballot(mx > m_run + kLazy)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == kNegInf ? 0.0f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m_run = m_new;
+      }
+      const float nm = m_run == kNegInf ? 0.0f : -m_run;
+      float lsum = 0.0f;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(__builtin_fmaf(sacc[sb][r], smul, nm));
+          p[sb][r] = e;
+          lsum += e;
+        }
+      l_run += lsum;
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = sacc[sb][r];
+          p[sb][r] = x != x ? 0.0f : act_fwd<ACT>(x * smul);
+        }
+    }
+
+    bf16x8 pb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pb[c] = pack8(&p[c >> 1][8 * (c & 1)]);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t base = (uint32_t)(c * 16 * kRowBytes);
+        o[db] = mfma32(lds_read_tr(Vt, base + (T[0] ^ (uint32_t)(64 * db)), base + (T[1] ^ (uint32_t)(64 * db))), pb[c],
+                       o[db]);
+      }
+  }
+
+  float inv;
+  float l_tot = 0.0f;
+  if (SOFTMAX) {
+    l_tot = l_run + __shfl_xor(l_run, 32);
+    inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  } else {
+    inv = (slot < 0 && Lkv > 0) ? 1.0f / (float)Lkv : 1.0f;
+  }
+  if (slot < 0) {
+    if (qi < Lq) {
+      const size_t base = ((size_t)(qs + qi) * a.H + h) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(a.out, base + 32 * db + 8 * g + 4 * hh, o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
+                 o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv, a.out_f32);
+      if (SOFTMAX && hh == 0)
+        a.lse[(size_t)h * a.Tq + qs + qi] =
+            l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 + (BIAS == kBiasScalar ? bias_c : 0.0f) : kNegInf;
+    }
+  } else {
+    const int prow = wave * 32 + l32;
+    float* po = a.part_o + ((size_t)slot * BM + prow) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * g + 4 * hh) =
+            make_float4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+    if (SOFTMAX && hh == 0)
+      a.part_lse[(size_t)slot * BM + prow] = l_tot > 0.0f ? m_run + fast_log2(l_tot) : kNegInf;
+  }
+}
+
 // Merge the pieces of split items in fixed order r = 0..R-1:
 //   softmax: lse* = log2 sum_r 2^lse_r,  O = sum_r 2^(lse_r - lse*) O_r   (O_r normalised per piece)
 //   GDPA:    O = (sum_r O_r) / Lkv
@@ -306,7 +493,10 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
 
 template <int D, int ACT, int BIAS, bool CAUSAL>
 hipError_t fwd_launch_t(const FwdArgs& a, int n, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_kernel<D, ACT, BIAS, CAUSAL>), dim3(n), dim3(kThreads), 0, s, a);
+  if (D == 128)
+    hipLaunchKernelGGL((fwd_kernel2<ACT, BIAS, CAUSAL>), dim3(n), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, ACT, BIAS, CAUSAL>), dim3(n), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -369,7 +559,7 @@ int occupancy_forward(const Modes& m) {
   if (m.D == 64)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<64, kSoftmax, kBiasBucket, true>, kThreads, 0);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<128, kSoftmax, kBiasBucket, true>, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel2<kSoftmax, kBiasBucket, true>, kThreads, 0);
   return (e == hipSuccess && n > 0) ? n : 1;
 }
 

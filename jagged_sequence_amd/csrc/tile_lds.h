@@ -1,0 +1,95 @@
+// Row-major bf16 tiles in LDS for D = 128, filled straight from global memory and read either
+// row-wise (16-byte MFMA operands) or transposed (ds_read_b64_tr_b16).
+//
+// A tile row is 128 bf16 = 256 bytes = 16 chunks of 16 bytes, rows packed with no padding. Chunk c of
+// row r is stored at chunk position c ^ swz(r), swz(r) = ((r & 3) << 2) | ((r >> 2) & 3), a bijection
+// of r mod 16. With it, (a) the 16 lanes of a quarter-wave that read one logical chunk of 16
+// different rows hit 16 different bank groups, and (b) a transposing read, which touches 4
+// consecutive rows x 4 consecutive chunks per half-wave, also covers all banks exactly once.
+//
+// Loads use buffer_load ... lds: lane i of a wave writes 16 bytes at (wave-uniform LDS base) + 16 i,
+// so one instruction fills 4 rows (1 KB); rows past the jagged end are out of the buffer range and
+// arrive as zeros. No registers are used for staging.
+#pragma once
+
+#include "device_common.h"
+
+namespace jfa {
+
+constexpr int kRowBytes = 256;  // D = 128 bf16
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+__device__ __forceinline__ lds_ptr_t to_lds(const void* p) { return (lds_ptr_t)p; }
+
+// Byte offsets (within the slice) and LDS row for instruction u of a wave filling a tile of
+// `rows_per_wave` rows: lane covers row 4 u + lane/16 of the wave's rows and the logical chunk that
+// lands at physical position lane % 16.
+struct TileLoader {
+  uint32_t voff[4];  // per u: row_in_tile * rs * 2 + logical chunk * 16 (without the tile's first row)
+};
+
+// Each wave fills rows [16 wave, 16 wave + 16) of a 64-row tile with 4 instructions.
+__device__ __forceinline__ TileLoader make_loader64(int wave, int lane, int rs) {
+  TileLoader t;
+  const int q = lane >> 4, p = lane & 15;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 16 * wave + 4 * u + q;  // row within the tile; r & 15 = 4 u + q
+    const int c = p ^ swz(r);
+    t.voff[u] = (uint32_t)(r * rs * 2 + c * 16);
+  }
+  return t;
+}
+
+// Issue the loads of a 64-row tile whose first row is `row0` of the slice into LDS at `tile`.
+__device__ __forceinline__ void load_tile64(const TileLoader& t, __amdgpu_buffer_rsrc_t src, int row0, int rs,
+                                            unsigned char* tile, int wave) {
+  const uint32_t base = (uint32_t)(row0 * rs * 2);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, to_lds(tile + (16 * wave + 4 * u) * kRowBytes), 16, base + t.voff[u],
+                                             0, 0, 0);
+}
+
+// Wait for this wave's outstanding global loads (including loads into LDS).
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Row operand: lane reads logical chunk (2 kb + hh) of tile row `r`: byte address
+// r * 256 + (((2 kb + hh) ^ swz(r)) << 4) = (r * 256 + ((hh ^ swz(r)) << 4)) ^ (kb << 5).
+__device__ __forceinline__ uint32_t row_operand_base(int r, int hh) {
+  return (uint32_t)(r * kRowBytes + ((hh ^ swz(r)) << 4));
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const unsigned char* tile, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(tile + off);
+}
+
+// Transposed operand of a 32x32x16 MFMA from a k-major tile (row = contraction index, column = m):
+// lane l receives X[k0 + 8 (l/32) + 4 half + 0..3][m0 + l % 32] for half = 0, 1 (8 values). Within
+// each 16-lane group, lane s supplies the address of X[k0 + 8 (g/2) + 4 half + s/4][m0 + 16 (g%2) + 4 (s%4)],
+// g = lane / 16. For m0 = 32 db and k0 a multiple of 16 the byte address is
+// 256 k0 + (T[half] ^ (64 db)) with the lane constant T computed here.
+__device__ __forceinline__ void tr_operand_bases(int lane, uint32_t (&T)[2]) {
+  const int g = lane >> 4, s = lane & 15;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int rr = 8 * (g >> 1) + 4 * half + (s >> 2);  // row within the 16-row group
+    const int col = 16 * (g & 1) + 4 * (s & 3);         // column within the 32-column block
+    const int c = col >> 3, w = col & 7;
+    T[half] = (uint32_t)(rr * kRowBytes + ((c ^ swz(rr)) << 4) + 2 * w);
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_read_tr(const unsigned char* tile, uint32_t off0, uint32_t off1) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + off0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + off1));
+  typedef __attribute__((ext_vector_type(8))) short s16x8;
+  const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+}  // namespace jfa
