@@ -249,6 +249,164 @@ void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// D = 128 dQ with a two-stage LDS ring: K and V tiles are loaded straight into LDS (swizzled
+// row-major) one tile ahead of the compute; K^T for dQ += dS K comes from transposing LDS reads.
+struct alignas(16) DqSmem2 {
+  unsigned char kv[2][2][kDqBN * kRowBytes];  // [stage][0 = K, 1 = V]
+  float tab[kBuckets];
+  float diag[4][kDiagLen];
+};
+
+template <int ACT, int BIAS, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel2(BwdArgs a) {
+  constexpr int D = 128, BM = kDqBM, BN = kDqBN, NKB = D / 16, NDB = D / 32;
+  constexpr bool SOFTMAX = ACT == kSoftmax;
+  __shared__ DqSmem2 sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t* it = a.dq_items + (size_t)blockIdx.x * kItemInts;
+  const int b = it[0], h = it[1], t = it[2], k0 = it[3], k1 = it[4], slot = it[5];
+  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
+  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const int rs = a.H * D;
+  const int row0 = t * BM + wave * 32;
+  const int qi = row0 + l32;
+
+  const float inv_scale = 1.0f / a.scale;
+  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
+  const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
+  const float acc0 = (BIAS == kBiasScalar && !SOFTMAX) ? bias_c * inv_scale : 0.0f;
+
+  bf16x8 qf[NKB], df[NKB];
+  {
+    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+    const __amdgpu_buffer_rsrc_t gr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const uint32_t off = (uint32_t)(qi * rs + kb * 16 + hh * 8) * 2u;
+      qf[kb] = as_bf16x8(buf_load16(qr, off));
+      df[kb] = as_bf16x8(buf_load16(gr, off));
+    }
+  }
+  float nlse2 = kNegInf, dlt = 0.0f;  // -lse in log2 units; -inf makes every P of the row 0
+  if (SOFTMAX && qi < Lq) {
+    const float l = a.lse[(size_t)h * a.Tq + qs + qi];
+    nlse2 = l == kNegInf ? kNegInf : -(l - (BIAS == kBiasScalar ? bias_c : 0.0f)) * kLog2e;
+    dlt = a.delta[(size_t)h * a.Tq + qs + qi];
+  }
+  const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
+  const float invL = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
+
+  f32x16 qacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) qacc[db] = f32x16{};
+
+  const __amdgpu_buffer_rsrc_t kr = slice_rsrc(a.k + (size_t)ks * rs + h * D, Lkv, rs, D);
+  const __amdgpu_buffer_rsrc_t vr = slice_rsrc(a.v + (size_t)ks * rs + h * D, Lkv, rs, D);
+  const TileLoader ld = make_loader64(wave, lane, rs);
+  const uint32_t raddr = row_operand_base(kappa(l32), hh);
+  uint32_t T[2];
+  tr_operand_bases(lane, T);
+
+  if (k0 < k1) {
+    load_tile64(ld, kr, k0 * BN, rs, sm.kv[0][0], wave);
+    load_tile64(ld, vr, k0 * BN, rs, sm.kv[0][1], wave);
+  }
+  for (int kt = k0; kt < k1; ++kt) {
+    const int key0 = kt * BN;
+    const int st = (kt - k0) & 1;
+    wait_vm();
+    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, row0 - key0 - (BN - 1), inv_scale, lane);
+    __syncthreads();
+    if (kt + 1 < k1) {
+      load_tile64(ld, kr, (kt + 1) * BN, rs, sm.kv[st ^ 1][0], wave);
+      load_tile64(ld, vr, (kt + 1) * BN, rs, sm.kv[st ^ 1][1], wave);
+    }
+    const unsigned char* Kt = sm.kv[st][0];
+    const unsigned char* Vt = sm.kv[st][1];
+
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      if (BIAS == kBiasBucket) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float* dv = &sm.diag[wave][63 - 32 * sb + l32 - 16 * c - 8 * hh];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sacc[sb][8 * c + j] = dv[-j];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[sb][r] = acc0;
+      }
+      pacc[sb] = f32x16{};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint32_t off = (raddr ^ (uint32_t)(kb << 5)) + sb * 32 * kRowBytes;
+        sacc[sb] = mfma32(lds_read16(Kt, off), qf[kb], sacc[sb]);
+        pacc[sb] = mfma32(lds_read16(Vt, off), df[kb], pacc[sb]);
+      }
+    }
+
+    const bool need_mask = (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
+    float ds[2][16];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float d;
+        if (SOFTMAX) {
+          const float p = fast_exp2(__builtin_fmaf(sacc[sb][r], smul, nlse2));
+          d = p * (pacc[sb][r] - dlt);
+        } else {
+          float f, g;
+          act_fwd_grad<ACT>(sacc[sb][r] * smul, f, g);
+          d = pacc[sb][r] * g * invL;
+        }
+        if (need_mask) {
+          const int key = key0 + 32 * sb + acc_row(r, hh);
+          d = (key >= Lkv || (CAUSAL && key > qi)) ? 0.0f : d;
+        }
+        ds[sb][r] = d;
+      }
+    }
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dsb[c] = pack8(&ds[c >> 1][8 * (c & 1)]);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t base = (uint32_t)(c * 16 * kRowBytes);
+        qacc[db] = mfma32(lds_read_tr(Kt, base + (T[0] ^ (uint32_t)(64 * db)), base + (T[1] ^ (uint32_t)(64 * db))),
+                          dsb[c], qacc[db]);
+      }
+  }
+
+  if (slot < 0) {
+    if (qi < Lq) {
+      const size_t base = ((size_t)(qs + qi) * a.H + h) * D;
+      const float sc = a.scale;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(a.dq, base + 32 * db + 8 * g + 4 * hh, qacc[db][4 * g] * sc, qacc[db][4 * g + 1] * sc,
+                 qacc[db][4 * g + 2] * sc, qacc[db][4 * g + 3] * sc, a.grad_f32);
+    }
+  } else {
+    float* po = a.part_dq + ((size_t)slot * BM + wave * 32 + l32) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * g + 4 * hh) =
+            make_float4(qacc[db][4 * g], qacc[db][4 * g + 1], qacc[db][4 * g + 2], qacc[db][4 * g + 3]);
+  }
+}
+
 // ---------------------------------------------------------------- dK/dV, key-tile parallel
 template <int D>
 struct alignas(16) KvSmem {
@@ -718,6 +876,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_dkdv_kernel(BwdArgs a) {
 // D = 128 runs the LDS-ring kernels; D = 64 the register-staged ones.
 template <int D, int ACT, int BIAS, bool CAUSAL>
 constexpr auto dkdv_select = D == 128 ? &bwd_dkdv_kernel2<ACT, BIAS, CAUSAL> : &bwd_dkdv_kernel<D, ACT, BIAS, CAUSAL>;
+template <int D, int ACT, int BIAS, bool CAUSAL>
+constexpr auto dq_select = D == 128 ? &bwd_dq_kernel2<ACT, BIAS, CAUSAL> : &bwd_dq_kernel<D, ACT, BIAS, CAUSAL>;
 
 
 #define JFA_DISPATCH_MODES(KERNEL, m, n, s, a)                                                          \
@@ -766,7 +926,7 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, const Modes& m, hipStream_t s
 
 hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  return JFA_DISPATCH_MODES(bwd_dq_kernel, m, n, s, a);
+  return JFA_DISPATCH_MODES(dq_select, m, n, s, a);
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
@@ -796,7 +956,7 @@ int occupancy_dq(const Modes& m) {
   int n = 0;
   hipError_t e = m.D == 64
                      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dq_kernel<64, kSoftmax, kBiasBucket, true>, kThreads, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dq_kernel<128, kSoftmax, kBiasBucket, true>, kThreads, 0);
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dq_kernel2<kSoftmax, kBiasBucket, true>, kThreads, 0);
   return (e == hipSuccess && n > 0) ? n : 1;
 }
 
