@@ -13,7 +13,8 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libjfa.so")
+# JFA_LIBRARY selects another build of the same library (for A/B measurements of kernel variants)
+LIB_PATH = os.environ.get("JFA_LIBRARY") or os.path.join(_HERE, "libjfa.so")
 
 JFA_OK = 0
 STATUS_NAMES = {0: "JFA_OK", 1: "JFA_ERR_NULL_ARG", 2: "JFA_ERR_BAD_OFFSETS", 3: "JFA_ERR_BAD_SHAPE",

@@ -10,6 +10,8 @@
 //   softmax: P = exp(s - lse_i), dP = <dO_i, v_j>, dS = P (dP - Delta_i), Delta_i = <dO_i, O_i>
 //   GDPA:    P = act(s) / Lkv,   dP = <dO_i, v_j>, dS = dP act'(s) / Lkv
 //   dV_j += P dO_i,  dK_j += scale dS q_i,  dQ_i += scale dS k_j
+#include <type_traits>
+
 #include "device_common.h"
 #include "tile_lds.h"
 
@@ -711,76 +713,89 @@ void bwd_dkdv_kernel2(BwdArgs a) {
     const float* lse2 = sm.lse2[st];
     const float* dltv = sm.dlt[st];
 
-    const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0);
+    // One 64-query step as straight-line code (no branch inside), instantiated for tiles that need
+    // masking and for interior tiles, so the scheduler can overlap one block's softmax arithmetic
+    // with the other block's matrix products.
+    auto step = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      f32x16 sacc[2], pacc[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 sacc, pacc = f32x16{};
-      if (BIAS == kBiasBucket) {
+      for (int qb = 0; qb < 2; ++qb) {
+        if (BIAS == kBiasBucket) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const float* dvp = &sm.diag[wave][31 + 32 * qb + 16 * c + 8 * hh - l32];
+          for (int c = 0; c < 2; ++c) {
+            const float* dvp = &sm.diag[wave][31 + 32 * qb + 16 * c + 8 * hh - l32];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) sacc[8 * c + j] = dvp[j];
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = acc0;
-      }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const uint32_t off = (raddr ^ (uint32_t)(kb << 5)) + qb * 32 * kRowBytes;
-        sacc = mfma32(lds_read16(Qt, off), kf[kb], sacc);
-        pacc = mfma32(lds_read16(Gt, off), vf[kb], pacc);
-      }
-
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int c8 = 0; c8 < 2; ++c8) {
-        const int rbase = 32 * qb + 16 * c8 + 8 * hh;  // 8 consecutive query rows of this lane
-        float l8[8], d8[8], pv[8], dsv[8];
-        if (SOFTMAX) {
-          const float4 x0 = *reinterpret_cast<const float4*>(&lse2[rbase]);
-          const float4 x1 = *reinterpret_cast<const float4*>(&lse2[rbase + 4]);
-          const float4 y0 = *reinterpret_cast<const float4*>(&dltv[rbase]);
-          const float4 y1 = *reinterpret_cast<const float4*>(&dltv[rbase + 4]);
-          l8[0] = x0.x; l8[1] = x0.y; l8[2] = x0.z; l8[3] = x0.w; l8[4] = x1.x; l8[5] = x1.y; l8[6] = x1.z; l8[7] = x1.w;
-          d8[0] = y0.x; d8[1] = y0.y; d8[2] = y0.z; d8[3] = y0.w; d8[4] = y1.x; d8[5] = y1.y; d8[6] = y1.z; d8[7] = y1.w;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 8 * c8 + j;
-          float pj, dj;
-          if (SOFTMAX) {
-            pj = fast_exp2(__builtin_fmaf(sacc[r], smul, l8[j]));
-            dj = pj * (pacc[r] - d8[j]);
-          } else {
-            float f, g;
-            act_fwd_grad<ACT>(sacc[r] * smul, f, g);
-            pj = f * invL;
-            dj = pacc[r] * g * invL;
+            for (int j = 0; j < 8; ++j) sacc[qb][8 * c + j] = dvp[j];
           }
-          if (need_mask || !SOFTMAX) {
-            const int qi = qrow0 + rbase + j;
-            const bool masked = (need_mask && (kj >= Lkv || (CAUSAL && kj > qi))) || (!SOFTMAX && qi >= Lq);
-            pj = masked ? 0.0f : pj;
-            dj = masked ? 0.0f : dj;
-          }
-          pv[j] = pj;
-          dsv[j] = dj;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[qb][r] = acc0;
         }
-        pb[c8] = pack8(pv);
-        dsb[c8] = pack8(dsv);
+        pacc[qb] = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const uint32_t off = (raddr ^ (uint32_t)(kb << 5)) + qb * 32 * kRowBytes;
+          sacc[qb] = mfma32(lds_read16(Qt, off), kf[kb], sacc[qb]);
+          pacc[qb] = mfma32(lds_read16(Gt, off), vf[kb], pacc[qb]);
+        }
       }
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int qb = 0; qb < 2; ++qb) {
+        bf16x8 pb[2], dsb[2];
 #pragma unroll
         for (int c8 = 0; c8 < 2; ++c8) {
-          const uint32_t base = (uint32_t)((32 * qb + 16 * c8) * kRowBytes);
-          const uint32_t o0 = base + (T[0] ^ (uint32_t)(64 * db)), o1 = base + (T[1] ^ (uint32_t)(64 * db));
-          dv[db] = mfma32(lds_read_tr(Gt, o0, o1), pb[c8], dv[db]);
-          dk[db] = mfma32(lds_read_tr(Qt, o0, o1), dsb[c8], dk[db]);
+          const int rbase = 32 * qb + 16 * c8 + 8 * hh;  // 8 consecutive query rows of this lane
+          float l8[8], d8[8], pv[8], dsv[8];
+          if (SOFTMAX) {
+            const float4 x0 = *reinterpret_cast<const float4*>(&lse2[rbase]);
+            const float4 x1 = *reinterpret_cast<const float4*>(&lse2[rbase + 4]);
+            const float4 y0 = *reinterpret_cast<const float4*>(&dltv[rbase]);
+            const float4 y1 = *reinterpret_cast<const float4*>(&dltv[rbase + 4]);
+            l8[0] = x0.x; l8[1] = x0.y; l8[2] = x0.z; l8[3] = x0.w; l8[4] = x1.x; l8[5] = x1.y; l8[6] = x1.z; l8[7] = x1.w;
+            d8[0] = y0.x; d8[1] = y0.y; d8[2] = y0.z; d8[3] = y0.w; d8[4] = y1.x; d8[5] = y1.y; d8[6] = y1.z; d8[7] = y1.w;
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int r = 8 * c8 + j;
+            float pj, dj;
+            if (SOFTMAX) {
+              pj = fast_exp2(__builtin_fmaf(sacc[qb][r], smul, l8[j]));
+              dj = pj * (pacc[qb][r] - d8[j]);
+            } else {
+              float f, g;
+              act_fwd_grad<ACT>(sacc[qb][r] * smul, f, g);
+              pj = f * invL;
+              dj = pacc[qb][r] * g * invL;
+            }
+            if (MASK || !SOFTMAX) {
+              const int qi = qrow0 + rbase + j;
+              const bool masked = (MASK && (kj >= Lkv || (CAUSAL && kj > qi))) || (!SOFTMAX && qi >= Lq);
+              pj = masked ? 0.0f : pj;
+              dj = masked ? 0.0f : dj;
+            }
+            pv[j] = pj;
+            dsv[j] = dj;
+          }
+          pb[c8] = pack8(pv);
+          dsb[c8] = pack8(dsv);
         }
-    }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int c8 = 0; c8 < 2; ++c8) {
+            const uint32_t base = (uint32_t)((32 * qb + 16 * c8) * kRowBytes);
+            const uint32_t o0 = base + (T[0] ^ (uint32_t)(64 * db)), o1 = base + (T[1] ^ (uint32_t)(64 * db));
+            dv[db] = mfma32(lds_read_tr(Gt, o0, o1), pb[c8], dv[db]);
+            dk[db] = mfma32(lds_read_tr(Qt, o0, o1), dsb[c8], dk[db]);
+          }
+      }
+    };
+    const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0);
+    if (need_mask)
+      step(std::true_type{});
+    else
+      step(std::false_type{});
   }
 
   if (slot < 0) {
