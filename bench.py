@@ -32,9 +32,9 @@ DEFAULT_WORKLOAD = "causal_bucket"
 # FLOPs each kernel must execute per visible pair and head (its own matrix products):
 #   forward: S = QK^T, O = PV; dK/dV: S, dP = dO V^T, dV = P^T dO, dK = dS^T Q; dQ: S, dP, dQ = dS K
 KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dkdv": 8, "dq": 6}
-KERNEL_SOURCES = {"forward": ["fwd.hip", "device_common.h", "jfa_internal.h"],
-                  "dkdv": ["bwd.hip", "device_common.h", "jfa_internal.h"],
-                  "dq": ["bwd.hip", "device_common.h", "jfa_internal.h"]}
+KERNEL_SOURCES = {"forward": ["fwd.hip", "device_common.h", "tile_lds.h", "jfa_internal.h"],
+                  "dkdv": ["bwd.hip", "device_common.h", "tile_lds.h", "jfa_internal.h"],
+                  "dq": ["bwd.hip", "device_common.h", "tile_lds.h", "jfa_internal.h"]}
 
 
 def source_hash(kernel: str) -> str:
@@ -122,6 +122,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 3 device-to-device copies of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU only "
@@ -139,6 +141,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n}), flush=True)
+        return 0
     w = ji.WORKLOADS[args.workload]
     x = ji.workload_inputs(args.workload)
     causal = w.mask == "causal"
