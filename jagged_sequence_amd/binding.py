@@ -11,6 +11,10 @@ import os
 from typing import Optional
 
 import numpy as np
+# torch must be loaded before libjfa.so: the library's libamdhip64 dependency then resolves to the HIP
+# runtime torch already carries, so one runtime owns the device, the streams and the pointers that
+# torch hands to the library. Loading the library first would bring in a second runtime.
+import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # JFA_LIBRARY selects another build of the same library (for A/B measurements of kernel variants)
@@ -86,7 +90,6 @@ def _ptr(t) -> Optional[int]:
 
 
 def _stream_handle(stream) -> Optional[int]:
-    import torch
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream
@@ -167,7 +170,6 @@ class Plan:
 
     # ------------------------------------------------------------------ compute
     def _workspace(self, nbytes: int, ws):
-        import torch
         if nbytes == 0:
             return None
         if ws is None:
@@ -176,7 +178,6 @@ class Plan:
 
     def forward(self, q, k, v, q_offsets, kv_offsets, bias=None, out=None, lse=None, workspace=None, stream=None):
         """Forward pass; returns (out, lse). Tensors are torch device tensors in the ABI layouts."""
-        import torch
         if out is None:
             out = torch.empty((self.Tq, self.H, self.D), device=q.device,
                               dtype=torch.float32 if self.out_dtype == "f32" else torch.bfloat16)
@@ -192,7 +193,6 @@ class Plan:
     def backward(self, q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq=None, dk=None, dv=None,
                  workspace=None, stream=None):
         """Backward pass; returns (dq, dk, dv)."""
-        import torch
         gdt = torch.float32 if self.grad_dtype == "f32" else torch.bfloat16
         if dq is None:
             dq = torch.empty((self.Tq, self.H, self.D), device=q.device, dtype=gdt)
