@@ -613,19 +613,34 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
-// D = 128 dK/dV with a two-stage LDS ring: Q and dO tiles are loaded straight into LDS (swizzled
-// row-major, no staging registers) one tile ahead of the compute, one barrier per tile; the Q^T and
-// dO^T operands of dK += dS^T Q and dV += P^T dO come from transposing LDS reads.
+// D = 128 dK/dV with wave pairs. An 8-wave workgroup owns 128 keys; waves p and p + 4 share keys
+// 32 p .. 32 p + 31 and sit on the same SIMD. Wave p (A) holds K and accumulates dV: S = Q K^T,
+// P = softmax probabilities (or act(S)/Lkv), dV += P^T dO. Wave p + 4 (B) holds V and accumulates dK:
+// dP = dO V^T, dS = P (dP - Delta) (or dP act'(S)/Lkv), dK += dS^T Q. P (and act'(S)/Lkv) pass from
+// A to B through LDS between two barriers. Each wave keeps one operand and one accumulator set, so
+// two waves fit per SIMD and A's exponentials overlap B's matrix products. Q and dO tiles are loaded
+// straight into a two-stage LDS ring (swizzled row-major, no staging registers) one tile ahead of the
+// compute; the Q^T and dO^T operands come from transposing LDS reads.
 struct alignas(16) KvSmem2 {
   unsigned char qg[2][2][kKvBM * kRowBytes];  // [stage][0 = Q, 1 = dO]
   float lse2[2][kKvBM];                       // -lse in log2 units (softmax)
   float dlt[2][kKvBM];
+  uint4 xch[4][2][2][2][64];                  // [pair][0 = P, 1 = act'/Lkv][q block][8-row half][lane]: 8 bf16
   float tab[kBuckets];
   float diag[4][kDiagLen];
 };
 
+__device__ __forceinline__ void unpack8(uint4 w, float (&x)[8]) {
+  const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = __builtin_bit_cast(float, v[j] << 16);
+    x[2 * j + 1] = __builtin_bit_cast(float, v[j] & 0xffff0000u);
+  }
+}
+
 template <int ACT, int BIAS, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel2(BwdArgs a) {
   constexpr int D = 128, BM = kKvBM, BN = kKvBN, NKB = D / 16, NDB = D / 32;
   constexpr bool SOFTMAX = ACT == kSoftmax;
@@ -633,12 +648,14 @@ void bwd_dkdv_kernel2(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
+  const bool isB = wave >= 4;
   const int32_t* it = a.kv_items + (size_t)blockIdx.x * kItemInts;
   const int b = it[0], h = it[1], kt = it[2], q0 = it[3], q1 = it[4], slot = it[5];
   const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
   const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
   const int rs = a.H * D;
-  const int key_w = kt * BN + wave * 32;  // first key of this wave
+  const int key_w = kt * BN + pair * 32;  // first key of this pair
   const int kj = key_w + l32;
 
   const float inv_scale = 1.0f / a.scale;
@@ -646,31 +663,23 @@ void bwd_dkdv_kernel2(BwdArgs a) {
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
   const float acc0 = (BIAS == kBiasScalar && !SOFTMAX) ? bias_c * inv_scale : 0.0f;
 
-  bf16x8 kf[NKB], vf[NKB];
+  bf16x8 frag[NKB];  // A: K fragment, B: V fragment (B operand, lane = key)
   {
-    const __amdgpu_buffer_rsrc_t kr = slice_rsrc(a.k + (size_t)ks * rs + h * D, Lkv, rs, D);
-    const __amdgpu_buffer_rsrc_t vr = slice_rsrc(a.v + (size_t)ks * rs + h * D, Lkv, rs, D);
+    const __amdgpu_buffer_rsrc_t fr = slice_rsrc((isB ? a.v : a.k) + (size_t)ks * rs + h * D, Lkv, rs, D);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const uint32_t off = (uint32_t)(kj * rs + kb * 16 + hh * 8) * 2u;
-      kf[kb] = as_bf16x8(buf_load16(kr, off));
-      vf[kb] = as_bf16x8(buf_load16(vr, off));
-    }
+    for (int kb = 0; kb < NKB; ++kb) frag[kb] = as_bf16x8(buf_load16(fr, (uint32_t)(kj * rs + kb * 16 + hh * 8) * 2u));
   }
   const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
   const float invL = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
   const float lse_shift = (SOFTMAX && BIAS == kBiasScalar) ? bias_c : 0.0f;
 
-  f32x16 dk[NDB], dv[NDB];
+  f32x16 acc[NDB];  // A: dV, B: dK (unscaled)
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
-  }
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   const __amdgpu_buffer_rsrc_t qsr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
   const __amdgpu_buffer_rsrc_t gsr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
-  const TileLoader ld = make_loader64(wave, lane, rs);
+  const TileLoader ld = make_loader64_w8(wave, lane, rs);
   const uint32_t raddr = row_operand_base(kappa(l32), hh);
   uint32_t T[2];
   tr_operand_bases(lane, T);
@@ -689,8 +698,8 @@ void bwd_dkdv_kernel2(BwdArgs a) {
     }
   };
   if (q0 < q1) {
-    load_tile64(ld, qsr, q0 * BM, rs, sm.qg[0][0], wave);
-    load_tile64(ld, gsr, q0 * BM, rs, sm.qg[0][1], wave);
+    load_tile64_w8(ld, qsr, q0 * BM, rs, sm.qg[0][0], wave);
+    load_tile64_w8(ld, gsr, q0 * BM, rs, sm.qg[0][1], wave);
     load_stats(q0);
   }
   for (int qt = q0; qt < q1; ++qt) {
@@ -701,83 +710,124 @@ void bwd_dkdv_kernel2(BwdArgs a) {
       sm.dlt[st][tid] = pd;
     }
     wait_vm();
-    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, qrow0 - key_w - 31, inv_scale, lane);
+    if (BIAS == kBiasBucket && !isB) fill_diag(sm.diag[pair], sm.tab, qrow0 - key_w - 31, inv_scale, lane);
     __syncthreads();
     if (qt + 1 < q1) {
-      load_tile64(ld, qsr, (qt + 1) * BM, rs, sm.qg[st ^ 1][0], wave);
-      load_tile64(ld, gsr, (qt + 1) * BM, rs, sm.qg[st ^ 1][1], wave);
+      load_tile64_w8(ld, qsr, (qt + 1) * BM, rs, sm.qg[st ^ 1][0], wave);
+      load_tile64_w8(ld, gsr, (qt + 1) * BM, rs, sm.qg[st ^ 1][1], wave);
       load_stats(qt + 1);
     }
     const unsigned char* Qt = sm.qg[st][0];
     const unsigned char* Gt = sm.qg[st][1];
-    const float* lse2 = sm.lse2[st];
-    const float* dltv = sm.dlt[st];
+    const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0);
 
-    // One 64-query step as straight-line code (no branch inside), instantiated for tiles that need
-    // masking and for interior tiles, so the scheduler can overlap one block's softmax arithmetic
-    // with the other block's matrix products.
-    auto step = [&](auto mask_tag) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      f32x16 sacc[2], pacc[2];
+    f32x16 pacc[2];    // B: dP of both query blocks
+    if (!isB) {
+      // ---- A, phase 1: S = Q K^T, probabilities, hand-off to B
+      auto phase1 = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        if (BIAS == kBiasBucket) {
+        for (int qb = 0; qb < 2; ++qb) {
+          f32x16 sacc;
+          if (BIAS == kBiasBucket) {
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const float* dvp = &sm.diag[wave][31 + 32 * qb + 16 * c + 8 * hh - l32];
+            for (int c = 0; c < 2; ++c) {
+              const float* dvp = &sm.diag[pair][31 + 32 * qb + 16 * c + 8 * hh - l32];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sacc[qb][8 * c + j] = dvp[j];
-          }
-        } else {
+              for (int j = 0; j < 8; ++j) sacc[8 * c + j] = dvp[j];
+            }
+          } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[qb][r] = acc0;
-        }
-        pacc[qb] = f32x16{};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const uint32_t off = (raddr ^ (uint32_t)(kb << 5)) + qb * 32 * kRowBytes;
-          sacc[qb] = mfma32(lds_read16(Qt, off), kf[kb], sacc[qb]);
-          pacc[qb] = mfma32(lds_read16(Gt, off), vf[kb], pacc[qb]);
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        bf16x8 pb[2], dsb[2];
-#pragma unroll
-        for (int c8 = 0; c8 < 2; ++c8) {
-          const int rbase = 32 * qb + 16 * c8 + 8 * hh;  // 8 consecutive query rows of this lane
-          float l8[8], d8[8], pv[8], dsv[8];
-          if (SOFTMAX) {
-            const float4 x0 = *reinterpret_cast<const float4*>(&lse2[rbase]);
-            const float4 x1 = *reinterpret_cast<const float4*>(&lse2[rbase + 4]);
-            const float4 y0 = *reinterpret_cast<const float4*>(&dltv[rbase]);
-            const float4 y1 = *reinterpret_cast<const float4*>(&dltv[rbase + 4]);
-            l8[0] = x0.x; l8[1] = x0.y; l8[2] = x0.z; l8[3] = x0.w; l8[4] = x1.x; l8[5] = x1.y; l8[6] = x1.z; l8[7] = x1.w;
-            d8[0] = y0.x; d8[1] = y0.y; d8[2] = y0.z; d8[3] = y0.w; d8[4] = y1.x; d8[5] = y1.y; d8[6] = y1.z; d8[7] = y1.w;
+            for (int r = 0; r < 16; ++r) sacc[r] = acc0;
           }
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int r = 8 * c8 + j;
-            float pj, dj;
+          for (int kb = 0; kb < NKB; ++kb)
+            sacc = mfma32(lds_read16(Qt, (raddr ^ (uint32_t)(kb << 5)) + qb * 32 * kRowBytes), frag[kb], sacc);
+#pragma unroll
+          for (int c8 = 0; c8 < 2; ++c8) {
+            const int rbase = 32 * qb + 16 * c8 + 8 * hh;  // 8 consecutive query rows of this lane
+            float pv[8], gv[8];
             if (SOFTMAX) {
-              pj = fast_exp2(__builtin_fmaf(sacc[qb][r], smul, l8[j]));
-              dj = pj * (pacc[qb][r] - d8[j]);
+              const float* ls = sm.lse2[st];
+              const float4 x0 = *reinterpret_cast<const float4*>(&ls[rbase]);
+              const float4 x1 = *reinterpret_cast<const float4*>(&ls[rbase + 4]);
+              const float l8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+              for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(__builtin_fmaf(sacc[8 * c8 + j], smul, l8[j]));
             } else {
-              float f, g;
-              act_fwd_grad<ACT>(sacc[qb][r] * smul, f, g);
-              pj = f * invL;
-              dj = pacc[qb][r] * g * invL;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                float f, g;
+                act_fwd_grad<ACT>(sacc[8 * c8 + j] * smul, f, g);
+                pv[j] = f * invL;
+                gv[j] = g * invL;
+              }
             }
             if (MASK || !SOFTMAX) {
-              const int qi = qrow0 + rbase + j;
-              const bool masked = (MASK && (kj >= Lkv || (CAUSAL && kj > qi))) || (!SOFTMAX && qi >= Lq);
-              pj = masked ? 0.0f : pj;
-              dj = masked ? 0.0f : dj;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const int qi = qrow0 + rbase + j;
+                const bool masked = (MASK && (kj >= Lkv || (CAUSAL && kj > qi))) || (!SOFTMAX && qi >= Lq);
+                pv[j] = masked ? 0.0f : pv[j];
+                if (!SOFTMAX) gv[j] = masked ? 0.0f : gv[j];
+              }
             }
-            pv[j] = pj;
-            dsv[j] = dj;
+            sm.xch[pair][0][qb][c8][lane] = __builtin_bit_cast(uint4, pack8(pv));
+            if (!SOFTMAX) sm.xch[pair][1][qb][c8][lane] = __builtin_bit_cast(uint4, pack8(gv));
           }
-          pb[c8] = pack8(pv);
+        }
+      };
+      if (need_mask)
+        phase1(std::true_type{});
+      else
+        phase1(std::false_type{});
+    } else {
+      // ---- B, phase 1: dP = dO V^T
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        pacc[qb] = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          pacc[qb] = mfma32(lds_read16(Gt, (raddr ^ (uint32_t)(kb << 5)) + qb * 32 * kRowBytes), frag[kb], pacc[qb]);
+      }
+    }
+    __syncthreads();
+    if (!isB) {
+      // ---- A, phase 2: dV += P^T dO (P read back from the hand-off buffer)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int c8 = 0; c8 < 2; ++c8) {
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, sm.xch[pair][0][qb][c8][lane]);
+          const uint32_t base = (uint32_t)((32 * qb + 16 * c8) * kRowBytes);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = mfma32(lds_read_tr(Gt, base + (T[0] ^ (uint32_t)(64 * db)), base + (T[1] ^ (uint32_t)(64 * db))),
+                             pb, acc[db]);
+        }
+    } else {
+      // ---- B, phase 2: dS, dK += dS^T Q
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int c8 = 0; c8 < 2; ++c8) {
+          float pv[8], dsv[8];
+          unpack8(sm.xch[pair][0][qb][c8][lane], pv);
+          if (SOFTMAX) {
+            const int rbase = 32 * qb + 16 * c8 + 8 * hh;
+            const float* dl = sm.dlt[st];
+            const float4 y0 = *reinterpret_cast<const float4*>(&dl[rbase]);
+            const float4 y1 = *reinterpret_cast<const float4*>(&dl[rbase + 4]);
+            const float d8[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dsv[j] = pv[j] * (pacc[qb][8 * c8 + j] - d8[j]);
+          } else {
+            float gv[8];
+            unpack8(sm.xch[pair][1][qb][c8][lane], gv);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dsv[j] = pacc[qb][8 * c8 + j] * gv[j];
+          }
           dsb[c8] = pack8(dsv);
         }
 #pragma unroll
@@ -785,45 +835,34 @@ void bwd_dkdv_kernel2(BwdArgs a) {
 #pragma unroll
           for (int c8 = 0; c8 < 2; ++c8) {
             const uint32_t base = (uint32_t)((32 * qb + 16 * c8) * kRowBytes);
-            const uint32_t o0 = base + (T[0] ^ (uint32_t)(64 * db)), o1 = base + (T[1] ^ (uint32_t)(64 * db));
-            dv[db] = mfma32(lds_read_tr(Gt, o0, o1), pb[c8], dv[db]);
-            dk[db] = mfma32(lds_read_tr(Qt, o0, o1), dsb[c8], dk[db]);
+            acc[db] = mfma32(lds_read_tr(Qt, base + (T[0] ^ (uint32_t)(64 * db)), base + (T[1] ^ (uint32_t)(64 * db))),
+                             dsb[c8], acc[db]);
           }
       }
-    };
-    const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0);
-    if (need_mask)
-      step(std::true_type{});
-    else
-      step(std::false_type{});
+    }
   }
 
+  // Accumulator register r of d-block db: dimension 32 db + 8 (r/4) + 4 hh + r%4, key kj.
+  const float sc = isB ? a.scale : 1.0f;
   if (slot < 0) {
     if (kj < Lkv) {
+      void* dst = isB ? a.dk : a.dv;
       const size_t base = ((size_t)(ks + kj) * a.H + h) * D;
-      const float sc = a.scale;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const size_t i = base + 32 * db + 8 * g + 4 * hh;
-          store4(a.dk, i, dk[db][4 * g] * sc, dk[db][4 * g + 1] * sc, dk[db][4 * g + 2] * sc, dk[db][4 * g + 3] * sc,
-                 a.grad_f32);
-          store4(a.dv, i, dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3], a.grad_f32);
-        }
+        for (int g = 0; g < 4; ++g)
+          store4(dst, base + 32 * db + 8 * g + 4 * hh, acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc,
+                 acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc, a.grad_f32);
     }
   } else {
-    const size_t prow = (size_t)slot * BN + wave * 32 + l32;
-    float* pk = a.part_dk + prow * D;
-    float* pvp = a.part_dv + prow * D;
+    float* pp = (isB ? a.part_dk : a.part_dv) + ((size_t)slot * BN + pair * 32 + l32) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int i = 32 * db + 8 * g + 4 * hh;
-        *reinterpret_cast<float4*>(pk + i) = make_float4(dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]);
-        *reinterpret_cast<float4*>(pvp + i) = make_float4(dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]);
-      }
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(pp + 32 * db + 8 * g + 4 * hh) =
+            make_float4(acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]);
   }
 }
 
@@ -889,6 +928,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dispatch
 // D = 128 runs the LDS-ring kernels; D = 64 the register-staged ones.
+constexpr int kDkdvThreads128 = 512;
 template <int D, int ACT, int BIAS, bool CAUSAL>
 constexpr auto dkdv_select = D == 128 ? &bwd_dkdv_kernel2<ACT, BIAS, CAUSAL> : &bwd_dkdv_kernel<D, ACT, BIAS, CAUSAL>;
 template <int D, int ACT, int BIAS, bool CAUSAL>
@@ -898,7 +938,7 @@ constexpr auto dq_select = D == 128 ? &bwd_dq_kernel2<ACT, BIAS, CAUSAL> : &bwd_
 #define JFA_DISPATCH_MODES(KERNEL, m, n, s, a)                                                          \
   [&]() -> hipError_t {                                                                                 \
     auto go = [&](auto kern) {                                                                          \
-      hipLaunchKernelGGL(kern, dim3(n), dim3(kThreads), 0, s, a);                                       \
+      hipLaunchKernelGGL(kern, dim3(n), dim3(block), 0, s, a);                                          \
       return hipGetLastError();                                                                         \
     };                                                                                                  \
     if (m.D == 64) {                                                                                    \
@@ -941,11 +981,13 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a, const Modes& m, hipStream_t s
 
 hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  const int block = kThreads;
   return JFA_DISPATCH_MODES(dq_select, m, n, s, a);
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  const int block = m.D == 128 ? kDkdvThreads128 : kThreads;
   return JFA_DISPATCH_MODES(dkdv_select, m, n, s, a);
 }
 
@@ -979,7 +1021,8 @@ int occupancy_dkdv(const Modes& m) {
   int n = 0;
   hipError_t e = m.D == 64
                      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dkdv_kernel<64, kSoftmax, kBiasBucket, true>, kThreads, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dkdv_kernel2<kSoftmax, kBiasBucket, true>, kThreads, 0);
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dkdv_select<128, kSoftmax, kBiasBucket, true>,
+                                                                    kDkdvThreads128, 0);
   return (e == hipSuccess && n > 0) ? n : 1;
 }
 

@@ -55,6 +55,29 @@ __device__ __forceinline__ void load_tile64(const TileLoader& t, __amdgpu_buffer
                                              0, 0, 0);
 }
 
+// Each of 8 waves fills rows [8 wave, 8 wave + 8) of a 64-row tile with 2 instructions.
+__device__ __forceinline__ TileLoader make_loader64_w8(int wave, int lane, int rs) {
+  TileLoader t;
+  const int q = lane >> 4, p = lane & 15;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = 8 * wave + 4 * u + q;
+    const int c = p ^ swz(r);
+    t.voff[u] = (uint32_t)(r * rs * 2 + c * 16);
+  }
+  t.voff[2] = t.voff[3] = 0;
+  return t;
+}
+
+__device__ __forceinline__ void load_tile64_w8(const TileLoader& t, __amdgpu_buffer_rsrc_t src, int row0, int rs,
+                                               unsigned char* tile, int wave) {
+  const uint32_t base = (uint32_t)(row0 * rs * 2);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, to_lds(tile + (8 * wave + 4 * u) * kRowBytes), 16, base + t.voff[u],
+                                             0, 0, 0);
+}
+
 // Wait for this wave's outstanding global loads (including loads into LDS).
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0); }
 
