@@ -316,18 +316,20 @@ void bwd_dq_kernel2(BwdArgs a) {
     load_tile64(ld, kr, k0 * BN, rs, sm.kv[0][0], wave);
     load_tile64(ld, vr, k0 * BN, rs, sm.kv[0][1], wave);
   }
-  for (int kt = k0; kt < k1; ++kt) {
+  // One kv tile; ST (compile-time) is the ring stage holding it.
+  auto tile = [&](const int kt, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
     const int key0 = kt * BN;
-    const int st = (kt - k0) & 1;
     wait_vm();
-    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, row0 - key0 - (BN - 1), inv_scale, lane);
+    // Bias of score (qi, key) at diag[31 - l32 + key - key0], ascending in register order.
+    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, key0 - row0 - 31, inv_scale, lane);
     __syncthreads();
     if (kt + 1 < k1) {
-      load_tile64(ld, kr, (kt + 1) * BN, rs, sm.kv[st ^ 1][0], wave);
-      load_tile64(ld, vr, (kt + 1) * BN, rs, sm.kv[st ^ 1][1], wave);
+      load_tile64(ld, kr, (kt + 1) * BN, rs, sm.kv[ST ^ 1][0], wave);
+      load_tile64(ld, vr, (kt + 1) * BN, rs, sm.kv[ST ^ 1][1], wave);
     }
-    const unsigned char* Kt = sm.kv[st][0];
-    const unsigned char* Vt = sm.kv[st][1];
+    const unsigned char* Kt = sm.kv[ST][0];
+    const unsigned char* Vt = sm.kv[ST][1];
 
     f32x16 sacc[2], pacc[2];
 #pragma unroll
@@ -335,9 +337,9 @@ void bwd_dq_kernel2(BwdArgs a) {
       if (BIAS == kBiasBucket) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const float* dv = &sm.diag[wave][63 - 32 * sb + l32 - 16 * c - 8 * hh];
+          const float* dv = &sm.diag[wave][31 - l32 + 32 * sb + 16 * c + 8 * hh];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) sacc[sb][8 * c + j] = dv[-j];
+          for (int j = 0; j < 8; ++j) sacc[sb][8 * c + j] = dv[j];
         }
       } else {
 #pragma unroll
@@ -367,12 +369,17 @@ void bwd_dq_kernel2(BwdArgs a) {
           act_fwd_grad<ACT>(sacc[sb][r] * smul, f, g);
           d = pacc[sb][r] * g * invL;
         }
-        if (need_mask) {
-          const int key = key0 + 32 * sb + acc_row(r, hh);
-          d = (key >= Lkv || (CAUSAL && key > qi)) ? 0.0f : d;
-        }
         ds[sb][r] = d;
       }
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * sb + acc_row(r, hh);
+          ds[sb][r] = (key >= Lkv || (CAUSAL && key > qi)) ? 0.0f : ds[sb][r];
+        }
     }
     bf16x8 dsb[4];
 #pragma unroll
@@ -385,6 +392,10 @@ void bwd_dq_kernel2(BwdArgs a) {
         qacc[db] = mfma32(lds_read_tr(Kt, base + (T[0] ^ (uint32_t)(64 * db)), base + (T[1] ^ (uint32_t)(64 * db))),
                           dsb[c], qacc[db]);
       }
+  };
+  for (int kt = k0; kt < k1; kt += 2) {
+    tile(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < k1) tile(kt + 1, std::integral_constant<int, 1>{});
   }
 
   if (slot < 0) {

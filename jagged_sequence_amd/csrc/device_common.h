@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "jfa_internal.h"
 
@@ -47,6 +48,21 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
     r[j + 1] = p[1];
   }
   return r;
+}
+
+// acc + the sum of the 32 bf16 values in p (v_dot2c_f32_bf16 against (1, 1): two values per
+// instruction, fp32 accumulation).
+__device__ __forceinline__ float rowsum_bf16(const bf16x8 (&p)[4], float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float acc2 = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < 8; j += 4) {
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[c][j], p[c][j + 1]}, one, acc, false);
+      acc2 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[c][j + 2], p[c][j + 3]}, one, acc2, false);
+    }
+  return acc + acc2;
 }
 
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {

@@ -297,18 +297,22 @@ void fwd_kernel2(FwdArgs a) {
     load_tile64(ld, kr, k0 * BN, rs, sm.kv[0][0], wave);
     load_tile64(ld, vr, k0 * BN, rs, sm.kv[0][1], wave);
   }
-  for (int kt = k0; kt < k1; ++kt) {
+  // One kv tile. ST is the ring stage holding tile kt (compile-time, so every LDS address is a
+  // loop-invariant register plus an immediate offset).
+  auto tile = [&](const int kt, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
     const int key0 = kt * BN;
-    const int st = (kt - k0) & 1;
     wait_vm();
-    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, row0 - key0 - (BN - 1), inv_scale, lane);
+    // Bias of score (qi, key) sits at diag[qi - key + 31 - (row0 - key0)] = diag[31 - l32 + key - key0]:
+    // ascending in the accumulator's register order.
+    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, key0 - row0 - 31, inv_scale, lane);
     __syncthreads();
     if (kt + 1 < k1) {
-      load_tile64(ld, kr, (kt + 1) * BN, rs, sm.kv[st ^ 1][0], wave);
-      load_tile64(ld, vr, (kt + 1) * BN, rs, sm.kv[st ^ 1][1], wave);
+      load_tile64(ld, kr, (kt + 1) * BN, rs, sm.kv[ST ^ 1][0], wave);
+      load_tile64(ld, vr, (kt + 1) * BN, rs, sm.kv[ST ^ 1][1], wave);
     }
-    const unsigned char* Kt = sm.kv[st][0];
-    const unsigned char* Vt = sm.kv[st][1];
+    const unsigned char* Kt = sm.kv[ST][0];
+    const unsigned char* Vt = sm.kv[ST][1];
 
     f32x16 sacc[2];
 #pragma unroll
@@ -316,9 +320,9 @@ void fwd_kernel2(FwdArgs a) {
       if (BIAS == kBiasBucket) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const float* dv = &sm.diag[wave][63 - 32 * sb + l32 - 16 * c - 8 * hh];
+          const float* dv = &sm.diag[wave][31 - l32 + 32 * sb + 16 * c + 8 * hh];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) sacc[sb][8 * c + j] = dv[-j];
+          for (int j = 0; j < 8; ++j) sacc[sb][8 * c + j] = dv[j];
         }
       } else {
 #pragma unroll
@@ -360,16 +364,10 @@ void fwd_kernel2(FwdArgs a) {
         m_run = m_new;
       }
       const float nm = m_run == kNegInf ? 0.0f : -m_run;
-      float lsum = 0.0f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(__builtin_fmaf(sacc[sb][r], smul, nm));
-          p[sb][r] = e;
-          lsum += e;
-        }
-      l_run += lsum;
+        for (int r = 0; r < 16; ++r) p[sb][r] = fast_exp2(__builtin_fmaf(sacc[sb][r], smul, nm));
     } else {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -383,6 +381,8 @@ void fwd_kernel2(FwdArgs a) {
     bf16x8 pb[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) pb[c] = pack8(&p[c >> 1][8 * (c & 1)]);
+    // The row sum adds the bf16 weights the P V product uses, two per instruction.
+    if (SOFTMAX) l_run = rowsum_bf16(pb, l_run);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -391,6 +391,10 @@ void fwd_kernel2(FwdArgs a) {
         o[db] = mfma32(lds_read_tr(Vt, base + (T[0] ^ (uint32_t)(64 * db)), base + (T[1] ^ (uint32_t)(64 * db))), pb[c],
                        o[db]);
       }
+  };
+  for (int kt = k0; kt < k1; kt += 2) {
+    tile(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < k1) tile(kt + 1, std::integral_constant<int, 1>{});
   }
 
   float inv;
