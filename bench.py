@@ -122,6 +122,8 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--dbias", action="store_true",
+                    help="also compute the bias gradient in every backward pass (a learned bias needs it)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -173,12 +175,15 @@ def main() -> int:
     dq = torch.empty_like(out)
     dk = torch.empty((x.k.shape[0], w.H, w.D), dtype=odt, device="cuda")
     dv = torch.empty_like(dk)
+    want_db = args.dbias and bias is not None and w.backward
+    db = torch.empty(bias.shape, dtype=torch.float32, device="cuda") if want_db else None
     stream = torch.cuda.current_stream()
 
     def step():
         plan.forward(q, k, v, qo, ko, bias, out=out, lse=lse, workspace=ws_f, stream=stream)
         if w.backward:
-            plan.backward(q, k, v, qo, ko, bias, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b, stream=stream)
+            plan.backward(q, k, v, qo, ko, bias, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws_b, stream=stream,
+                          dbias=db)
 
     for _ in range(args.warmup):
         step()
@@ -226,7 +231,8 @@ def main() -> int:
         "data": "synthetic (seeded jagged lengths and N(0,1) bf16 values; no dataset)",
         "config": {"workload": args.workload, "B": w.B, "H": w.H, "D": w.D, "mask": w.mask, "act": w.act,
                    "bias": w.bias, "tokens_q": int(x.q_off[-1]), "tokens_kv": int(x.kv_off[-1]),
-                   "visible_pairs_x_heads": int(pairs), "out_dtype": args.out_dtype, "description": w.description},
+                   "visible_pairs_x_heads": int(pairs), "out_dtype": args.out_dtype, "bias_gradient": bool(want_db),
+                   "description": w.description},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "plan_ms": round(plan_ms, 3),
         "kernels": {kk: {"avg_ms": round(vv["avg_ms"], 5), "per_step": vv["launches_per_step"]}

@@ -107,9 +107,17 @@ jfa_status jfa_forward(jfa_plan_t plan, const void* q, const void* k, const void
                        void* out, float* lse, void* workspace, size_t workspace_bytes,
                        jfa_stream_t stream);
 
-/* Backward pass: gradients of <out, dout> with respect to q, k and v. `out` and `lse` are the
- * forward results (softmax only; they may be NULL for GDPA). `dbias` must be NULL: the bias
- * gradient is not provided by this build (JFA_ERR_UNSUPPORTED otherwise). */
+/* Backward pass: gradients of <out, dout> with respect to q, k and v, and optionally the bias.
+ * `out` and `lse` are the forward results (softmax only; they may be NULL for GDPA).
+ * `dbias` is NULL (no bias gradient) or a device fp32 array of the bias shape, [H] for
+ * JFA_BIAS_HEAD_SCALAR and [H][64] for JFA_BIAS_REL_BUCKET64 (16-byte aligned), that receives
+ * dL/dbias: for the table, entry (h, u) is the sum of dS over the visible scores of head h whose
+ * relative distance |i - j| falls in bucket u; for the scalar, the sum of dS over all visible
+ * scores of head h (exactly 0 under softmax, which is invariant to a per-row shift). It is
+ * overwritten, not accumulated, and does not depend on launch timing (fixed-point sums).
+ * Requesting it without a bias returns JFA_ERR_UNSUPPORTED. The pages ask for custom attention
+ * bias together with an efficient backward pass (aihot.vn GEM page, section "Jagged Sequence
+ * Flash Attention"); a learned bias needs this gradient to train. */
 jfa_status jfa_backward(jfa_plan_t plan, const void* q, const void* k, const void* v,
                         const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias,
                         const void* out, const float* lse, const void* dout, void* dq, void* dk,
@@ -130,7 +138,8 @@ jfa_status jfa_plan_info(jfa_plan_t plan, int32_t* info, size_t n);
 
 /* Per-kernel timing with HIP events recorded around every launch of this plan (for
  * measurement; adds two event records per launch while on). Kernel ids: 0 forward,
- * 1 forward combine, 2 backward preprocess, 3 dK/dV, 4 dQ, 5 backward partial reduce.
+ * 1 forward combine, 2 backward preprocess, 3 dK/dV, 4 dQ, 5 backward partial reduce,
+ * 6 bias-gradient clear and finish.
  * jfa_timing_read waits for the recorded events and returns their summed time and count;
  * jfa_timing_enable(plan, 1) also clears previous records. Not thread safe. */
 jfa_status jfa_timing_enable(jfa_plan_t plan, int32_t enable);

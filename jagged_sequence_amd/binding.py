@@ -30,7 +30,7 @@ BIASES = {"none": 0, "scalar": 1, "bucket": 2}
 DTYPES = {"bf16": 0, "f32": 1}
 PLAN_HOST_ONLY = 0x1
 PLAN_NO_SPLIT = 0x2
-KERNELS = {"forward": 0, "combine": 1, "preprocess": 2, "dkdv": 3, "dq": 4, "reduce": 5}
+KERNELS = {"forward": 0, "combine": 1, "preprocess": 2, "dkdv": 3, "dq": 4, "reduce": 5, "dbias": 6}
 SYMBOLS = ["jfa_plan", "jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_plan_schedule", "jfa_plan_info",
            "jfa_timing_enable", "jfa_timing_read", "jfa_plan_destroy", "jfa_status_string", "jfa_last_error"]
 
@@ -191,8 +191,12 @@ class Plan:
         return out, lse
 
     def backward(self, q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq=None, dk=None, dv=None,
-                 workspace=None, stream=None):
-        """Backward pass; returns (dq, dk, dv)."""
+                 workspace=None, stream=None, dbias=None):
+        """Backward pass; returns (dq, dk, dv), or (dq, dk, dv, dbias) when ``dbias`` is given.
+
+        ``dbias`` is None (no bias gradient), True (allocate it) or an fp32 device tensor of the
+        bias shape that receives the gradient.
+        """
         gdt = torch.float32 if self.grad_dtype == "f32" else torch.bfloat16
         if dq is None:
             dq = torch.empty((self.Tq, self.H, self.D), device=q.device, dtype=gdt)
@@ -200,12 +204,17 @@ class Plan:
             dk = torch.empty((self.Tkv, self.H, self.D), device=q.device, dtype=gdt)
         if dv is None:
             dv = torch.empty((self.Tkv, self.H, self.D), device=q.device, dtype=gdt)
+        want_db = dbias is not None and dbias is not False
+        if dbias is True:
+            shape = (self.H, 64) if self.bias_kind == "bucket" else (self.H,)
+            dbias = torch.empty(shape, device=q.device, dtype=torch.float32)
         _, bwd_bytes = self.workspace_bytes()
         ws = self._workspace(bwd_bytes, workspace)
         _check(LIB.jfa_backward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias),
-                                _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), None, _ptr(ws),
+                                _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(dbias) if want_db else None, _ptr(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(), _stream_handle(stream)))
-        return dq, dk, dv
+        return (dq, dk, dv, dbias) if want_db else (dq, dk, dv)
 
 
 # ---------------------------------------------------------------------- C-named entry points
@@ -221,6 +230,6 @@ def jfa_forward(plan: Plan, q, k, v, q_offsets, kv_offsets, bias=None, out=None,
 
 
 def jfa_backward(plan: Plan, q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq=None, dk=None, dv=None,
-                 workspace=None, stream=None):
-    """``jfa_backward``: returns (dq, dk, dv)."""
-    return plan.backward(q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq, dk, dv, workspace, stream)
+                 workspace=None, stream=None, dbias=None):
+    """``jfa_backward``: returns (dq, dk, dv), plus dbias when it is requested."""
+    return plan.backward(q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq, dk, dv, workspace, stream, dbias)

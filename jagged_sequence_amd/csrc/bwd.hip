@@ -432,14 +432,17 @@ struct alignas(16) KvSmem {
   float dlt[kKvBM];
   float tab[kBuckets];
   float diag[4][kDiagLen];
+  unsigned long long dbh[4][kDbiasBins];  // per-wave bias-gradient bins (fixed point)
 };
 
-template <int D, int ACT, int BIAS, bool CAUSAL>
+template <int D, int ACT, int BIASX, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BM = kKvBM, BN = kKvBN, NKB = D / 16, NDB = D / 32;
   constexpr int RS = KvSmem<D>::RS, TS = KvSmem<D>::TS;
   constexpr bool SOFTMAX = ACT == kSoftmax;
+  constexpr int BIAS = BIASX & 3;
+  constexpr bool DBIAS = (BIASX & kBiasGrad) != 0;
   __shared__ KvSmem<D> sm;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
@@ -453,6 +456,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
   const float inv_scale = 1.0f / a.scale;
   if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
+  DbiasLane dbl;
+  if (DBIAS) sm.dbh[wave][lane] = 0ull;
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
   const float acc0 = (BIAS == kBiasScalar && !SOFTMAX) ? bias_c * inv_scale : 0.0f;
 
@@ -580,6 +585,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         }
         pb[c8] = pack8(pv);
         dsb[c8] = pack8(dsv);
+        if (DBIAS) dbl.add_run<BIAS == kBiasBucket>(sm.dbh[wave], qrow0 + rbase - kj, dsv);
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -591,6 +597,16 @@ void bwd_dkdv_kernel(BwdArgs a) {
           dk[db] = mfma32(lds_load8(qtp + 16 * c8), dsb[c8], dk[db]);
         }
       }
+    }
+  }
+
+  if (DBIAS) {
+    dbl.flush(sm.dbh[wave]);
+    wave_lds_fence();
+    constexpr int NB = BIAS == kBiasBucket ? kDbiasBins : 1;
+    if (lane < NB) {
+      const unsigned long long x = sm.dbh[wave][lane];
+      if (x) atomicAdd(a.dbias_acc + (size_t)h * NB + lane, x);
     }
   }
 
@@ -639,6 +655,7 @@ struct alignas(16) KvSmem2 {
   uint4 xch[4][2][2][2][64];                  // [pair][0 = P, 1 = act'/Lkv][q block][8-row half][lane]: 8 bf16
   float tab[kBuckets];
   float diag[4][kDiagLen];
+  unsigned long long dbh[4][kDbiasBins];      // per-B-wave bias-gradient bins (fixed point)
 };
 
 __device__ __forceinline__ void unpack8(uint4 w, float (&x)[8]) {
@@ -650,10 +667,12 @@ __device__ __forceinline__ void unpack8(uint4 w, float (&x)[8]) {
   }
 }
 
-template <int ACT, int BIAS, bool CAUSAL>
+template <int ACT, int BIASX, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel2(BwdArgs a) {
   constexpr int D = 128, BM = kKvBM, BN = kKvBN, NKB = D / 16, NDB = D / 32;
+  constexpr int BIAS = BIASX & 3;
+  constexpr bool DBIAS = (BIASX & kBiasGrad) != 0;
   constexpr bool SOFTMAX = ACT == kSoftmax;
   __shared__ KvSmem2 sm;
 
@@ -671,6 +690,8 @@ void bwd_dkdv_kernel2(BwdArgs a) {
 
   const float inv_scale = 1.0f / a.scale;
   if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
+  DbiasLane dbl;  // B waves: running bias-gradient sum of this lane
+  if (DBIAS && isB) sm.dbh[pair][lane] = 0ull;
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
   const float acc0 = (BIAS == kBiasScalar && !SOFTMAX) ? bias_c * inv_scale : 0.0f;
 
@@ -840,6 +861,7 @@ void bwd_dkdv_kernel2(BwdArgs a) {
             for (int j = 0; j < 8; ++j) dsv[j] = pacc[qb][8 * c8 + j] * gv[j];
           }
           dsb[c8] = pack8(dsv);
+          if (DBIAS) dbl.add_run<BIAS == kBiasBucket>(sm.dbh[pair], qrow0 + 32 * qb + 16 * c8 + 8 * hh - kj, dsv);
         }
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -850,6 +872,16 @@ void bwd_dkdv_kernel2(BwdArgs a) {
                              dsb[c8], acc[db]);
           }
       }
+    }
+  }
+
+  if (DBIAS && isB) {
+    dbl.flush(sm.dbh[pair]);
+    wave_lds_fence();
+    constexpr int NB = BIAS == kBiasBucket ? kDbiasBins : 1;
+    if (lane < NB) {
+      const unsigned long long x = sm.dbh[pair][lane];
+      if (x) atomicAdd(a.dbias_acc + (size_t)h * NB + lane, x);
     }
   }
 
@@ -937,11 +969,26 @@ __global__ __launch_bounds__(256) void bwd_reduce_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- bias gradient
+// The fixed-point accumulators are cleared by a kernel (not a memset) so that a captured graph
+// replays correctly; the finishing kernel converts them to fp32. Without a gradient variant of
+// the dK/dV kernel (softmax with a per-head scalar, whose exact gradient is 0) the cleared totals
+// come out as 0.
+__global__ __launch_bounds__(256) void bwd_dbias_clear_kernel(BwdArgs a, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) a.dbias_acc[i] = 0ull;
+}
+
+__global__ __launch_bounds__(256) void bwd_dbias_finish_kernel(BwdArgs a, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) a.dbias[i] = (float)((double)(long long)a.dbias_acc[i] * (1.0 / 4294967296.0));
+}
+
 // ---------------------------------------------------------------- dispatch
 // D = 128 runs the LDS-ring kernels; D = 64 the register-staged ones.
 constexpr int kDkdvThreads128 = 512;
-template <int D, int ACT, int BIAS, bool CAUSAL>
-constexpr auto dkdv_select = D == 128 ? &bwd_dkdv_kernel2<ACT, BIAS, CAUSAL> : &bwd_dkdv_kernel<D, ACT, BIAS, CAUSAL>;
+template <int D, int ACT, int BIASX, bool CAUSAL>
+constexpr auto dkdv_select = D == 128 ? &bwd_dkdv_kernel2<ACT, BIASX, CAUSAL> : &bwd_dkdv_kernel<D, ACT, BIASX, CAUSAL>;
 template <int D, int ACT, int BIAS, bool CAUSAL>
 constexpr auto dq_select = D == 128 ? &bwd_dq_kernel2<ACT, BIAS, CAUSAL> : &bwd_dq_kernel<D, ACT, BIAS, CAUSAL>;
 
@@ -976,6 +1023,24 @@ constexpr auto dq_select = D == 128 ? &bwd_dq_kernel2<ACT, BIAS, CAUSAL> : &bwd_
       return m.causal ? go(KERNEL<DD, AA, kBiasBucket, true>) : go(KERNEL<DD, AA, kBiasBucket, false>); \
   }
 
+// The dK/dV kernels also come in bias-gradient variants (bias | kBiasGrad).
+#define JFA_GO_CAUSAL(KERNEL, DD, AA, BB, m, go) \
+  return m.causal ? go(KERNEL<DD, AA, BB, true>) : go(KERNEL<DD, AA, BB, false>);
+#define JFA_DISPATCH_BIAS_GRAD(KERNEL, DD, AA, m, go)                                       \
+  switch (m.bias | (m.dbias && !(m.bias == kBiasScalar && AA == kSoftmax) ? kBiasGrad : 0)) { \
+    case kBiasNone: JFA_GO_CAUSAL(KERNEL, DD, AA, kBiasNone, m, go)                         \
+    case kBiasScalar: JFA_GO_CAUSAL(KERNEL, DD, AA, kBiasScalar, m, go)                     \
+    case kBiasBucket: JFA_GO_CAUSAL(KERNEL, DD, AA, kBiasBucket, m, go)                     \
+    case kBiasScalar | kBiasGrad: JFA_GO_CAUSAL(KERNEL, DD, AA, kBiasScalar | kBiasGrad, m, go) \
+    default: JFA_GO_CAUSAL(KERNEL, DD, AA, kBiasBucket | kBiasGrad, m, go)                  \
+  }
+#define JFA_DISPATCH_ACT_GRAD(KERNEL, DD, m, go)                                \
+  switch (m.act) {                                                              \
+    case kSoftmax: JFA_DISPATCH_BIAS_GRAD(KERNEL, DD, kSoftmax, m, go)          \
+    case kSilu: JFA_DISPATCH_BIAS_GRAD(KERNEL, DD, kSilu, m, go)                \
+    default: JFA_DISPATCH_BIAS_GRAD(KERNEL, DD, kGeluTanh, m, go)               \
+  }
+
 }  // namespace
 
 hipError_t launch_bwd_preprocess(const BwdArgs& a, const Modes& m, hipStream_t s) {
@@ -999,7 +1064,27 @@ hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n, hipStream_t s)
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int block = m.D == 128 ? kDkdvThreads128 : kThreads;
-  return JFA_DISPATCH_MODES(dkdv_select, m, n, s, a);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(n), dim3(block), 0, s, a);
+    return hipGetLastError();
+  };
+  if (m.D == 64) {
+    JFA_DISPATCH_ACT_GRAD(dkdv_select, 64, m, go)
+  } else {
+    JFA_DISPATCH_ACT_GRAD(dkdv_select, 128, m, go)
+  }
+}
+
+hipError_t launch_bwd_dbias_clear(const BwdArgs& a, const Modes& m, hipStream_t s) {
+  const int n = a.H * (m.bias == kBiasBucket ? kDbiasBins : 1);
+  hipLaunchKernelGGL(bwd_dbias_clear_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dbias_finish(const BwdArgs& a, const Modes& m, hipStream_t s) {
+  const int n = a.H * (m.bias == kBiasBucket ? kDbiasBins : 1);
+  hipLaunchKernelGGL(bwd_dbias_finish_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_reduce_dq(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {

@@ -163,6 +163,48 @@ __device__ __forceinline__ void fill_diag(float* vec, const float* tab, int d0, 
   if (lane < kDiagLen - 64) vec[64 + lane] = tab[rel_bucket(d0 + 64 + lane)] * mul;
 }
 
+// Bias gradient: dT[u] sums dS over the scores whose relative distance falls in bucket u (one bin
+// for the per-head scalar). Each lane keeps a running sum for its current bucket in registers;
+// when its bucket changes, the sum is added to this wave's bins as a 2^-32 fixed-point integer.
+// Integer addition is associative, so the bins and the global totals built from them do not depend
+// on the order in which lanes, waves or workgroups add: the result is deterministic.
+constexpr int kDbiasBins = 64;
+__device__ __forceinline__ unsigned long long to_fixed(float x) {
+  return (unsigned long long)__float2ll_rn(x * 4294967296.0f);  // exact scaling by 2^32
+}
+struct DbiasLane {
+  int u = -1;
+  float s = 0.0f;
+  __device__ __forceinline__ void flush(unsigned long long* bins) {
+    if (u >= 0 && s != 0.0f) atomicAdd(bins + u, to_fixed(s));
+    u = -1;
+    s = 0.0f;
+  }
+  __device__ __forceinline__ void add(unsigned long long* bins, int bucket, float v) {
+    if (bucket != u) {
+      flush(bins);
+      u = bucket;
+    }
+    s += v;
+  }
+  // Eight scores at relative distances d, d + 1, ..., d + 7 (one bucket unless the run crosses a
+  // bucket boundary or zero).
+  template <bool BUCKET>
+  __device__ __forceinline__ void add_run(unsigned long long* bins, int d, const float (&v)[8]) {
+    if (!BUCKET) {
+      add(bins, 0, ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7])));
+      return;
+    }
+    const int ulo = rel_bucket(d), uhi = rel_bucket(d + 7);
+    if ((d >= 0 || d + 7 <= 0) && ulo == uhi) {
+      add(bins, ulo, ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7])));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) add(bins, rel_bucket(d + j), v[j]);
+    }
+  }
+};
+
 // Pack element e (0..7) of four 8-element bf16 rows into 4 consecutive bf16 (a column slice).
 __device__ __forceinline__ uint2 column4(const uint4 (&r)[4], int e) {
   auto half = [&](const uint4& x) -> uint32_t {

@@ -144,7 +144,7 @@ struct jfa_plan_s {
   int device = -1;
   // workspace layout
   size_t ws_fwd = 0, off_part_lse = 0;
-  size_t ws_bwd = 0, off_delta = 0, off_part_dq = 0, off_part_dk = 0, off_part_dv = 0;
+  size_t ws_bwd = 0, off_delta = 0, off_part_dq = 0, off_part_dk = 0, off_part_dv = 0, off_dbias = 0;
   // timing
   bool timing = false;
   struct Rec {
@@ -300,6 +300,8 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   o += align256((size_t)P->lists[kKv].nslots * kKvBN * D * 4);
   P->off_part_dv = o;
   o += align256((size_t)P->lists[kKv].nslots * kKvBN * D * 4);
+  P->off_dbias = o;  // fixed-point bias-gradient totals, used when the caller asks for dbias
+  if (P->modes.bias != kBiasNone) o += align256((size_t)P->H * (P->modes.bias == kBiasBucket ? kBuckets : 1) * 8);
   P->ws_bwd = o;
   if (P->lists[kFwd].nslots == 0) P->ws_fwd = 0;
 
@@ -397,14 +399,14 @@ jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* 
   if (!P) return fail(JFA_ERR_NULL_ARG, "plan is NULL");
   if (P->flags & JFA_PLAN_HOST_ONLY) return fail(JFA_ERR_HOST_ONLY, "plan was built host-only");
   const bool softmax = P->modes.act == kSoftmax;
-  if (dbias) return fail(JFA_ERR_UNSUPPORTED, "the bias gradient is not provided; pass dbias = NULL");
+  if (dbias && P->modes.bias == kBiasNone) return fail(JFA_ERR_UNSUPPORTED, "dbias requested without a bias");
   if (!q || !k || !v || !q_offsets || !kv_offsets || !dout || !dq || !dk || !dv)
     return fail(JFA_ERR_NULL_ARG, "a tensor or offsets pointer is NULL");
   if (P->modes.bias != kBiasNone && !bias) return fail(JFA_ERR_NULL_ARG, "bias is NULL");
   if (softmax && (!out || !lse)) return fail(JFA_ERR_NULL_ARG, "out and lse are required for softmax");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv) || (out && !aligned16(out)) || (lse && !aligned16(lse)) || (bias && !aligned16(bias)) ||
-      !aligned16(workspace))
+      (dbias && !aligned16(dbias)) || !aligned16(workspace))
     return fail(JFA_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
   if (workspace_bytes < P->ws_bwd || (P->ws_bwd > 0 && !workspace))
     return fail(JFA_ERR_WORKSPACE, "backward workspace needs " + std::to_string(P->ws_bwd) + " bytes");
@@ -430,6 +432,8 @@ jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* 
   a.part_dq = ws ? reinterpret_cast<float*>(ws + P->off_part_dq) : nullptr;
   a.part_dk = ws ? reinterpret_cast<float*>(ws + P->off_part_dk) : nullptr;
   a.part_dv = ws ? reinterpret_cast<float*>(ws + P->off_part_dv) : nullptr;
+  a.dbias_acc = (ws && dbias) ? reinterpret_cast<unsigned long long*>(ws + P->off_dbias) : nullptr;
+  a.dbias = dbias;
   a.dq_items = P->lists[kDq].d_items;
   a.dq_groups = P->lists[kDq].d_groups;
   a.kv_items = P->lists[kKv].d_items;
@@ -440,7 +444,12 @@ jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* 
   a.scale = P->scale;
   a.out_f32 = P->out_f32;
   a.grad_f32 = P->grad_f32;
-  const Modes& m = P->modes;
+  Modes m = P->modes;
+  m.dbias = dbias ? 1 : 0;
+  if (dbias) {
+    st = timed(P, 6, s, [&] { return launch_bwd_dbias_clear(a, m, s); }, "bias-gradient clear launch");
+    if (st != JFA_OK) return st;
+  }
   if (softmax) {
     st = timed(P, 2, s, [&] { return launch_bwd_preprocess(a, m, s); }, "backward preprocess launch");
     if (st != JFA_OK) return st;
@@ -453,8 +462,11 @@ jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* 
     st = timed(P, 5, s, [&] { return launch_bwd_reduce_dq(a, m, (int)P->lists[kDq].n_groups(), s); }, "dQ reduce launch");
     if (st != JFA_OK) return st;
   }
-  if (P->lists[kKv].n_groups() > 0)
+  if (P->lists[kKv].n_groups() > 0) {
     st = timed(P, 5, s, [&] { return launch_bwd_reduce_dkdv(a, m, (int)P->lists[kKv].n_groups(), s); }, "dK/dV reduce launch");
+    if (st != JFA_OK) return st;
+  }
+  if (dbias) st = timed(P, 6, s, [&] { return launch_bwd_dbias_finish(a, m, s); }, "bias-gradient finish launch");
   return st;
 }
 

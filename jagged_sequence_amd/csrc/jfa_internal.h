@@ -58,6 +58,8 @@ struct BwdArgs {
   float* part_dq;  // [slots][kDqBM][D]
   float* part_dk;  // [slots][kKvBN][D]
   float* part_dv;  // [slots][kKvBN][D]
+  unsigned long long* dbias_acc;  // [H][bins] bias-gradient sums in 2^-32 fixed point (two's complement)
+  float* dbias;                   // [H][bins] output (bins = 64 for the bucket table, 1 for the scalar)
   const int32_t* dq_items;
   const int32_t* dq_groups;
   const int32_t* kv_items;
@@ -75,7 +77,12 @@ struct Modes {
   int act;
   int bias;
   int causal;
+  int dbias;  // the bias gradient is requested
 };
+
+// Bias template argument of the dK/dV kernels: kBiasScalar / kBiasBucket, plus kBiasGrad when the
+// kernel also accumulates the bias gradient.
+constexpr int kBiasGrad = 4;
 
 // Launchers (defined next to their kernels). Each returns the hipGetLastError() of its launch.
 hipError_t launch_forward(const FwdArgs& a, const Modes& m, int n_items, hipStream_t s);
@@ -85,6 +92,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n_items, hipStr
 hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n_items, hipStream_t s);
 hipError_t launch_bwd_reduce_dq(const BwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
 hipError_t launch_bwd_reduce_dkdv(const BwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
+hipError_t launch_bwd_dbias_clear(const BwdArgs& a, const Modes& m, hipStream_t s);
+hipError_t launch_bwd_dbias_finish(const BwdArgs& a, const Modes& m, hipStream_t s);
 
 // Resident workgroups per CU of each kernel for the given modes (occupancy query).
 int occupancy_forward(const Modes& m);

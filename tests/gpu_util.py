@@ -41,7 +41,7 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 
 
 def run_gpu(x: ji.Inputs, *, out_dtype="f32", grad_dtype="f32", num_slots=0, no_split=False, backward=True,
-            scale=0.0):
+            scale=0.0, dbias=False):
     plan = J.Plan(x.q_off, x.kv_off, x.H, x.D, mask=x.mask, act=x.act, bias=x.bias_kind, out_dtype=out_dtype,
                   grad_dtype=grad_dtype, num_slots=num_slots, no_split=no_split, scale=scale)
     q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
@@ -52,7 +52,11 @@ def run_gpu(x: ji.Inputs, *, out_dtype="f32", grad_dtype="f32", num_slots=0, no_
     res = {"plan": plan, "out": out, "lse": lse}
     if backward:
         do = to_dev(x.do)
-        dq, dk, dv = plan.backward(q, k, v, qo, ko, bias, out, lse, do)
+        if dbias:
+            dq, dk, dv, db = plan.backward(q, k, v, qo, ko, bias, out, lse, do, dbias=True)
+            res["dbias"] = db
+        else:
+            dq, dk, dv = plan.backward(q, k, v, qo, ko, bias, out, lse, do)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return res
@@ -68,8 +72,8 @@ def oracle(x: ji.Inputs, *, backward=True, seqs=None, heads=None):
     if x.act != "softmax":
         res["mag"] = A.gdpa_magnitude(q, k, v, x.q_off, x.kv_off, **kw)
     if backward:
-        dq, dk, dv, _ = A.backward(q, k, v, x.q_off, x.kv_off, f(x.do), **kw)
-        res.update(dq=dq, dk=dk, dv=dv)
+        dq, dk, dv, db = A.backward(q, k, v, x.q_off, x.kv_off, f(x.do), **kw)
+        res.update(dq=dq, dk=dk, dv=dv, dbias=db)
     return res
 
 
