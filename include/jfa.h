@@ -125,11 +125,17 @@ jfa_status jfa_backward(jfa_plan_t plan, const void* q, const void* k, const voi
                         jfa_stream_t stream);
 
 /* Work lists, for inspection and tests. `which`: 0 forward items, 1 forward split groups,
- * 2 dQ items, 3 dQ split groups, 4 dK/dV items, 5 dK/dV split groups. Items are 6 int32 each
- * (b, h, tile, lo, hi, slot): query-tile lists own query tile `tile` and cover key tiles
- * [lo, hi); the dK/dV list owns key tile `tile` and covers query tiles [lo, hi); slot is the
- * partial-result slot of a split piece or -1. Groups are 5 int32 each (b, h, tile, slot0, R).
- * Writes min(count, cap) records and sets *count to the total number of records. */
+ * 2 dQ items, 3 dQ split groups, 4 dK/dV items, 5 dK/dV split groups (longest first), and
+ * 6 forward, 7 dQ, 8 dK/dV items in dispatch order: the order in which the kernels' workgroups
+ * take them. Workgroup p runs on XCD p % 8, so the dispatch order keeps all items of a
+ * (sequence, head) group on one XCD's L2 (groups assigned longest first to the least-loaded XCD;
+ * each XCD takes its groups longest first, a group's items together in list order). Items are 6
+ * int32 each (b, h, tile, lo, hi, slot): query-tile lists own query tile `tile` and cover key
+ * tiles [lo, hi); the dK/dV list owns key tile `tile` and covers query tiles [lo, hi); slot is
+ * the partial-result slot of a split piece or -1. Groups are 5 int32 each (b, h, tile, slot0,
+ * R). The pages place the post-padding bottleneck in tile scheduling and load balance (vibekk.com
+ * GEM page, section on moving from padding to jagged kernels). Writes min(count, cap) records
+ * and sets *count to the total number of records. */
 jfa_status jfa_plan_schedule(jfa_plan_t plan, int32_t which, int32_t* out, size_t cap, size_t* count);
 
 /* Tile geometry and slot counts the plan used: writes up to `n` of

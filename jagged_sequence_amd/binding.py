@@ -148,7 +148,7 @@ class Plan:
     def schedule(self, which: int) -> np.ndarray:
         n = ctypes.c_size_t()
         _check(LIB.jfa_plan_schedule(self._h, which, None, 0, ctypes.byref(n)))
-        per = 5 if which & 1 else 6
+        per = 5 if which in (1, 3, 5) else 6  # 6..8: items in dispatch order
         out = np.zeros(n.value * per, dtype=np.int32)
         _check(LIB.jfa_plan_schedule(self._h, which, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value,
                                      ctypes.byref(n)))

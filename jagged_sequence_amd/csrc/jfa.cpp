@@ -18,6 +18,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <map>
 #include <vector>
 
 #include "jfa.h"
@@ -44,6 +45,7 @@ enum ListId { kFwd = 0, kDq = 1, kKv = 2 };
 struct List {
   std::vector<int32_t> items;   // 6 ints per item: b, h, tile, lo, hi, slot
   std::vector<int32_t> groups;  // 5 ints per group: b, h, tile, slot0, R
+  std::vector<int> order;       // dispatch order: device item p is items[order[p]]
   int nslots = 0;
   int slots = 0;                // concurrency the split rule balanced for
   int32_t* d_items = nullptr;
@@ -91,6 +93,54 @@ void finish(const std::vector<Raw>& raw, int slots, bool split, List& out) {
   for (const Item& i : items) out.items.insert(out.items.end(), {i.b, i.h, i.t, i.lo, i.hi, i.slot});
   out.nslots = next;
   out.slots = slots;
+}
+
+
+
+// Dispatch order. The GPU hands workgroup p of a launch to XCD p % kXcds, and each of MI355X's eight
+// XCDs has its own L2. Items of one (b, h) group read the same K/V (query-tile lists) or Q/dO
+// (key-tile lists), so the order keeps a group on one XCD and its items together:
+//   groups (b, h) with cost = total item cost, sorted by cost descending, then (b, h) ascending;
+//   each group goes to the XCD with the least cost so far (lowest index on ties);
+//   XCD x's queue holds its items by group rank, then in list order;
+//   position p takes the next item of queue p % kXcds, or, once that queue is empty, of the queue
+//   with the most items left (lowest index on ties).
+// Longest groups first keeps the longest-first dispatch of the list within each XCD.
+constexpr int kXcds = 8;
+
+std::vector<int> dispatch_order(const List& L) {
+  const size_t n = L.n_items();
+  std::map<std::pair<int, int>, int64_t> cost;
+  for (size_t i = 0; i < n; ++i) cost[{L.items[i * 6], L.items[i * 6 + 1]}] += L.items[i * 6 + 4] - L.items[i * 6 + 3];
+  std::vector<std::pair<std::pair<int, int>, int64_t>> gs(cost.begin(), cost.end());  // (b, h) ascending
+  std::stable_sort(gs.begin(), gs.end(), [](const auto& x, const auto& y) { return x.second > y.second; });
+  std::map<std::pair<int, int>, std::pair<int, int>> where;  // (b, h) -> (xcd, rank)
+  std::vector<int64_t> load(kXcds, 0);
+  for (size_t g = 0; g < gs.size(); ++g) {
+    int x = 0;
+    for (int y = 1; y < kXcds; ++y)
+      if (load[y] < load[x]) x = y;
+    where[gs[g].first] = {x, (int)g};
+    load[x] += gs[g].second;
+  }
+  std::vector<std::vector<int>> q(kXcds);
+  for (size_t i = 0; i < n; ++i) q[where[{L.items[i * 6], L.items[i * 6 + 1]}].first].push_back((int)i);
+  auto rank = [&](int i) { return where[{L.items[(size_t)i * 6], L.items[(size_t)i * 6 + 1]}].second; };
+  for (auto& v : q) std::stable_sort(v.begin(), v.end(), [&](int x, int y) { return rank(x) < rank(y); });
+  std::vector<size_t> head(kXcds, 0);
+  std::vector<int> order;
+  order.reserve(n);
+  for (size_t p = 0; p < n; ++p) {
+    int x = (int)(p % kXcds);
+    if (head[x] == q[x].size()) {
+      int best = -1;
+      for (int y = 0; y < kXcds; ++y)
+        if (head[y] < q[y].size() && (best < 0 || q[y].size() - head[y] > q[best].size() - head[best])) best = y;
+      x = best;
+    }
+    order.push_back(q[x][head[x]++]);
+  }
+  return order;
 }
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -285,6 +335,7 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   query_tile_list(lq, lkv, P->H, causal, kFwdBM, kFwdBN, slots[kFwd], split, P->lists[kFwd]);
   query_tile_list(lq, lkv, P->H, causal, kDqBM, kDqBN, slots[kDq], split, P->lists[kDq]);
   key_tile_list(lq, lkv, P->H, causal, kKvBM, kKvBN, slots[kKv], split, P->lists[kKv]);
+  for (auto& L : P->lists) L.order = dispatch_order(L);
 
   // workspace layout
   const size_t D = P->D;
@@ -315,7 +366,7 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
     for (int l = 0; l < 3; ++l) {
       List& L = P->lists[l];
       offs[l][0] = pos;
-      for (size_t i = 0; i < L.n_items(); ++i, pos += 8) std::copy_n(&L.items[i * 6], 6, &host[pos]);
+      for (size_t i = 0; i < L.n_items(); ++i, pos += 8) std::copy_n(&L.items[(size_t)L.order[i] * 6], 6, &host[pos]);
       offs[l][1] = pos;
       for (size_t g = 0; g < L.n_groups(); ++g, pos += 8) std::copy_n(&L.groups[g * 5], 5, &host[pos]);
     }
@@ -472,7 +523,13 @@ jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* 
 
 jfa_status jfa_plan_schedule(jfa_plan_t P, int32_t which, int32_t* out, size_t cap, size_t* count) {
   if (!P || !count) return fail(JFA_ERR_NULL_ARG, "plan or count is NULL");
-  if (which < 0 || which > 5) return fail(JFA_ERR_UNSUPPORTED, "which must be 0..5");
+  if (which < 0 || which > 8) return fail(JFA_ERR_UNSUPPORTED, "which must be 0..8");
+  if (which >= 6) {  // items in dispatch order
+    const List& D = P->lists[which - 6];
+    *count = D.n_items();
+    for (size_t i = 0; i < std::min(*count, cap) && out; ++i) std::copy_n(&D.items[(size_t)D.order[i] * 6], 6, out + i * 6);
+    return JFA_OK;
+  }
   const List& L = P->lists[which / 2];
   const bool groups = (which & 1) != 0;
   const std::vector<int32_t>& v = groups ? L.groups : L.items;

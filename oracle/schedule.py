@@ -76,3 +76,43 @@ def key_tile_items(lq, lkv, H: int, causal: bool, BMq: int, BNk: int, slots: int
                 cost = max(0, n_q - first)
                 raw.append((b, h, kt, first, first + cost))
     return _finish(raw, slots, split)
+
+
+def dispatch_order(items, n_xcd: int = 8):
+    """The items of one list in the order the kernel's workgroups take them.
+
+    Workgroup p of a launch runs on XCD p mod n_xcd, and every XCD has its own L2, so items that
+    read the same sequence's K/V (or Q/dO) are kept on one XCD:
+      a group is (b, h); its cost is the sum of (hi - lo) over its items;
+      groups are ranked by cost, largest first, ties by (b, h) ascending;
+      in rank order each group joins the XCD with the smallest total cost so far (lowest index
+      on ties);
+      an XCD's queue holds its items by group rank, then by position in the list;
+      position p takes the next item of queue p mod n_xcd, or, when that queue is empty, of the
+      queue with the most items left (lowest index on ties).
+    """
+    cost = {}
+    for (b, h, _t, lo, hi, _s) in items:
+        cost[(b, h)] = cost.get((b, h), 0) + (hi - lo)
+    ranked = sorted(cost, key=lambda g: (-cost[g], g))
+    load = [0] * n_xcd
+    home, rank = {}, {}
+    for r, g in enumerate(ranked):
+        x = min(range(n_xcd), key=lambda y: (load[y], y))
+        home[g], rank[g] = x, r
+        load[x] += cost[g]
+    queues = [[] for _ in range(n_xcd)]
+    for i, it in enumerate(items):
+        queues[home[(it[0], it[1])]].append(i)
+    for q in queues:
+        q.sort(key=lambda i: (rank[(items[i][0], items[i][1])], i))
+    taken = [0] * n_xcd
+    out = []
+    for p in range(len(items)):
+        x = p % n_xcd
+        if taken[x] == len(queues[x]):
+            x = max((y for y in range(n_xcd) if taken[y] < len(queues[y])),
+                    key=lambda y: (len(queues[y]) - taken[y], -y))
+        out.append(items[queues[x][taken[x]]])
+        taken[x] += 1
+    return out

@@ -55,6 +55,10 @@ def _compare(plan, lq, lkv, H, causal, slots, split):
     for which, expect in enumerate([fi, fg, qi, qg, ki, kg]):
         got = plan.schedule(which)
         np.testing.assert_array_equal(got, np.array(expect, dtype=np.int32).reshape(got.shape), err_msg=str(which))
+    for which, lst in [(6, fi), (7, qi), (8, ki)]:
+        got = plan.schedule(which)
+        expect = S.dispatch_order(lst)
+        np.testing.assert_array_equal(got, np.array(expect, dtype=np.int32).reshape(got.shape), err_msg=str(which))
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
@@ -74,6 +78,33 @@ def test_workload_schedules_bit_exact(name):
     plan = _host_plan(lq, lkv, w.H, w.D, mask=w.mask, act=w.act, bias=w.bias)
     assert plan.info()["fwd_slots"] == 512
     _compare(plan, lq, lkv, w.H, w.mask == "causal", 512, True)
+
+
+@pytest.mark.parametrize("name", ["causal_bucket", "longtail"])
+def test_dispatch_order_keeps_groups_on_one_xcd(name):
+    """Dispatch order: a permutation of the list; position p runs on XCD p % 8; away from the tail
+    (where drained queues lend positions) every (b, h) group sits on a single XCD, and the XCD loads
+    differ by less than the largest group."""
+    w = ji.WORKLOADS[name]
+    lq, lkv = ji.lengths(w)
+    plan = _host_plan(lq, lkv, w.H, w.D, mask=w.mask, act=w.act, bias=w.bias)
+    for lw, dw in [(0, 6), (2, 7), (4, 8)]:
+        lst, disp = plan.schedule(lw), plan.schedule(dw)
+        key = lambda a: sorted(map(tuple, a.tolist()))
+        assert key(lst) == key(disp)
+        n = len(disp)
+        home = {}
+        body = n - 8 * 8  # positions before the last rounds
+        for p in range(max(0, body)):
+            b, h = int(disp[p][0]), int(disp[p][1])
+            assert home.setdefault((b, h), p % 8) == p % 8, (b, h)
+        gsize = {}
+        for b, h, _t, lo, hi, _s in lst.tolist():
+            gsize[(b, h)] = gsize.get((b, h), 0) + hi - lo
+        tot = [0] * 8
+        for p in range(n):
+            tot[p % 8] += disp[p][4] - disp[p][3]
+        assert max(tot) - min(tot) <= max(gsize.values()) + max(1, sum(gsize.values()) // 100)
 
 
 def test_workspace_sizes():
