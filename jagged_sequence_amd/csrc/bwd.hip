@@ -316,6 +316,8 @@ void bwd_dq_kernel2(BwdArgs a) {
     load_tile64(ld, kr, k0 * BN, rs, sm.kv[0][0], wave);
     load_tile64(ld, vr, k0 * BN, rs, sm.kv[0][1], wave);
   }
+  // Wave 0 wrote the bias table; every wave reads it in the first tile's diagonal fill.
+  if (BIAS == kBiasBucket) __syncthreads();
   // One kv tile; ST (compile-time) is the ring stage holding it.
   auto tile = [&](const int kt, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
@@ -734,6 +736,9 @@ void bwd_dkdv_kernel2(BwdArgs a) {
     load_tile64_w8(ld, gsr, q0 * BM, rs, sm.qg[0][1], wave);
     load_stats(q0);
   }
+  // Wave 0 wrote the bias table (and the B waves cleared their gradient bins); A waves read the
+  // table in the first tile's diagonal fill.
+  if (BIAS == kBiasBucket) __syncthreads();
   for (int qt = q0; qt < q1; ++qt) {
     const int qrow0 = qt * BM;
     const int st = (qt - q0) & 1;

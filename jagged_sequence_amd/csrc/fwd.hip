@@ -297,6 +297,8 @@ void fwd_kernel2(FwdArgs a) {
     load_tile64(ld, kr, k0 * BN, rs, sm.kv[0][0], wave);
     load_tile64(ld, vr, k0 * BN, rs, sm.kv[0][1], wave);
   }
+  // Wave 0 wrote the bias table; every wave reads it in the first tile's diagonal fill.
+  if (BIAS == kBiasBucket) __syncthreads();
   // One kv tile. ST is the ring stage holding tile kt (compile-time, so every LDS address is a
   // loop-invariant register plus an immediate offset).
   auto tile = [&](const int kt, auto st_tag) {
