@@ -650,15 +650,49 @@ void bwd_dkdv_kernel(BwdArgs a) {
 // two waves fit per SIMD and A's exponentials overlap B's matrix products. Q and dO tiles are loaded
 // straight into a two-stage LDS ring (swizzled row-major, no staging registers) one tile ahead of the
 // compute; the Q^T and dO^T operands come from transposing LDS reads.
-struct alignas(16) KvSmem2 {
-  unsigned char qg[2][2][kKvBM * kRowBytes];  // [stage][0 = Q, 1 = dO]
-  float lse2[2][kKvBM];                       // -lse in log2 units (softmax)
+template <bool ONEBAR, bool GDPA>
+struct alignas(16) KvSmem2;
+
+// Two barriers per tile: a two-stage Q/dO ring and one hand-off buffer.
+template <bool GDPA>
+struct alignas(16) KvSmem2<false, GDPA> {
+  static constexpr int NPG = GDPA ? 2 : 1;      // P, and act'/Lkv for GDPA
+  unsigned char qg[2][2][kKvBM * kRowBytes];    // [stage][0 = Q, 1 = dO]
+  float lse2[2][kKvBM];                         // -lse in log2 units (softmax)
   float dlt[2][kKvBM];
-  uint4 xch[4][2][2][2][64];                  // [pair][0 = P, 1 = act'/Lkv][q block][8-row half][lane]: 8 bf16
+  uint4 xch[1][4][NPG][2][2][64];               // [buffer][pair][P / act'][q block][8-row half][lane]: 8 bf16
   float tab[kBuckets];
   float diag[4][kDiagLen];
-  unsigned long long dbh[4][kDbiasBins];      // per-B-wave bias-gradient bins (fixed point)
+  unsigned long long dbh[4][kDbiasBins];        // per-B-wave bias-gradient bins (fixed point)
 };
+
+// One barrier per tile: a three-stage ring and three hand-off buffers (152 KB). The small arrays
+// come first so that their LDS offsets fit the immediates of ds_read / ds_read2; the ring stages
+// are reached through a wave-uniform base offset.
+template <bool GDPA>
+struct alignas(16) KvSmem2<true, GDPA> {
+  static constexpr int NPG = GDPA ? 2 : 1;
+  float diag[4][kDiagLen];  // first: the 8-byte pair reads of a lane's bias window share one base
+  float tab[kBuckets];
+  unsigned long long dbh[4][kDbiasBins];
+  float lse2[3][kKvBM];
+  float dlt[3][kKvBM];
+  uint4 xch[3][4][NPG][2][2][64];
+  unsigned char qg[3][2][kKvBM * kRowBytes];
+};
+
+// A wave-uniform value the compiler cannot fold into address immediates.
+__device__ __forceinline__ uint32_t uniform_opaque(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+// A per-lane value the compiler must treat as new at this point (so that what is derived from it
+// is recomputed here instead of being kept live across the loop).
+__device__ __forceinline__ int lane_opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 __device__ __forceinline__ void unpack8(uint4 w, float (&x)[8]) {
   const uint32_t v[4] = {w.x, w.y, w.z, w.w};
@@ -676,7 +710,11 @@ void bwd_dkdv_kernel2(BwdArgs a) {
   constexpr int BIAS = BIASX & 3;
   constexpr bool DBIAS = (BIASX & kBiasGrad) != 0;
   constexpr bool SOFTMAX = ACT == kSoftmax;
-  __shared__ KvSmem2 sm;
+  // Softmax hands over P only, so a third ring stage and three hand-off buffers fit in LDS and one
+  // barrier per query tile suffices; GDPA also hands over act'/Lkv and keeps two barriers per tile.
+  constexpr bool ONEBAR = SOFTMAX;
+  using Smem = KvSmem2<ONEBAR, !SOFTMAX>;
+  __shared__ Smem sm;
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -713,12 +751,11 @@ void bwd_dkdv_kernel2(BwdArgs a) {
 
   const __amdgpu_buffer_rsrc_t qsr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
   const __amdgpu_buffer_rsrc_t gsr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
-  const TileLoader ld = make_loader64_w8(wave, lane, rs);
   const uint32_t raddr = row_operand_base(kappa(l32), hh);
   uint32_t T[2];
   tr_operand_bases(lane, T);
 
-  float pl = kNegInf, pd = 0.0f;  // statistics of query row tid of the next tile (softmax)
+  float pl = kNegInf, pd = 0.0f;  // statistics of query row tid of a coming tile (softmax)
   auto load_stats = [&](int qt) {
     if (SOFTMAX && tid < BM) {
       const int q = qt * BM + tid;
@@ -731,37 +768,38 @@ void bwd_dkdv_kernel2(BwdArgs a) {
       }
     }
   };
-  if (q0 < q1) {
-    load_tile64_w8(ld, qsr, q0 * BM, rs, sm.qg[0][0], wave);
-    load_tile64_w8(ld, gsr, q0 * BM, rs, sm.qg[0][1], wave);
-    load_stats(q0);
-  }
-  // Wave 0 wrote the bias table (and the B waves cleared their gradient bins); A waves read the
-  // table in the first tile's diagonal fill.
-  if (BIAS == kBiasBucket) __syncthreads();
-  for (int qt = q0; qt < q1; ++qt) {
-    const int qrow0 = qt * BM;
-    const int st = (qt - q0) & 1;
+  auto write_stats = [&](int stg) {
     if (SOFTMAX && tid < BM) {
-      sm.lse2[st][tid] = pl;
-      sm.dlt[st][tid] = pd;
+      sm.lse2[stg][tid] = pl;
+      sm.dlt[stg][tid] = pd;
     }
-    wait_vm();
-    if (BIAS == kBiasBucket && !isB) fill_diag(sm.diag[pair], sm.tab, qrow0 - key_w - 31, inv_scale, lane);
-    __syncthreads();
-    if (qt + 1 < q1) {
-      load_tile64_w8(ld, qsr, (qt + 1) * BM, rs, sm.qg[st ^ 1][0], wave);
-      load_tile64_w8(ld, gsr, (qt + 1) * BM, rs, sm.qg[st ^ 1][1], wave);
-      load_stats(qt + 1);
-    }
-    const unsigned char* Qt = sm.qg[st][0];
-    const unsigned char* Gt = sm.qg[st][1];
-    const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0);
+  };
+  auto issue_tile = [&](int qt, int stg) {
+    // loader offsets recomputed per tile (two VALU each) rather than held in registers
+    const TileLoader ld = make_loader64_w8(wave, lane_opaque(lane), rs);
+    load_tile64_w8(ld, qsr, qt * BM, rs, sm.qg[stg][0], wave);
+    load_tile64_w8(ld, gsr, qt * BM, rs, sm.qg[stg][1], wave);
+  };
+  auto fill = [&](int qt) {
+    if (BIAS == kBiasBucket && !isB) fill_diag(sm.diag[pair], sm.tab, qt * BM - key_w - 31, inv_scale, lane);
+  };
 
-    f32x16 pacc[2];    // B: dP of both query blocks
+  auto stage_ptr = [&](auto st_tag, int which) -> const unsigned char* {
+    constexpr int ST = decltype(st_tag)::value;
+    if constexpr (ONEBAR)
+      return sm.qg[0][which] + uniform_opaque((uint32_t)(ST * 2 * kKvBM * kRowBytes));
+    else
+      return sm.qg[ST][which];
+  };
+
+  // ---- phase 1. A: S = Q K^T, probabilities, hand-off to B. B: dP = dO V^T.
+  auto phase1 = [&](const int qt, auto st_tag, auto xb_tag, f32x16 (&pacc)[2]) {
+    constexpr int ST = decltype(st_tag)::value, XB = decltype(xb_tag)::value;
+    const int qrow0 = qt * BM;
+    const unsigned char* Qt = stage_ptr(st_tag, 0);
+    const unsigned char* Gt = stage_ptr(st_tag, 1);
     if (!isB) {
-      // ---- A, phase 1: S = Q K^T, probabilities, hand-off to B
-      auto phase1 = [&](auto mask_tag) {
+      auto run = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -785,7 +823,7 @@ void bwd_dkdv_kernel2(BwdArgs a) {
             const int rbase = 32 * qb + 16 * c8 + 8 * hh;  // 8 consecutive query rows of this lane
             float pv[8], gv[8];
             if (SOFTMAX) {
-              const float* ls = sm.lse2[st];
+              const float* ls = sm.lse2[ST];
               const float4 x0 = *reinterpret_cast<const float4*>(&ls[rbase]);
               const float4 x1 = *reinterpret_cast<const float4*>(&ls[rbase + 4]);
               const float l8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -809,17 +847,16 @@ void bwd_dkdv_kernel2(BwdArgs a) {
                 if (!SOFTMAX) gv[j] = masked ? 0.0f : gv[j];
               }
             }
-            sm.xch[pair][0][qb][c8][lane] = __builtin_bit_cast(uint4, pack8(pv));
-            if (!SOFTMAX) sm.xch[pair][1][qb][c8][lane] = __builtin_bit_cast(uint4, pack8(gv));
+            sm.xch[XB][pair][0][qb][c8][lane] = __builtin_bit_cast(uint4, pack8(pv));
+            if (!SOFTMAX) sm.xch[XB][pair][Smem::NPG - 1][qb][c8][lane] = __builtin_bit_cast(uint4, pack8(gv));
           }
         }
       };
-      if (need_mask)
-        phase1(std::true_type{});
+      if ((key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0))
+        run(std::true_type{});
       else
-        phase1(std::false_type{});
+        run(std::false_type{});
     } else {
-      // ---- B, phase 1: dP = dO V^T
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         pacc[qb] = f32x16{};
@@ -828,14 +865,20 @@ void bwd_dkdv_kernel2(BwdArgs a) {
           pacc[qb] = mfma32(lds_read16(Gt, (raddr ^ (uint32_t)(kb << 5)) + qb * 32 * kRowBytes), frag[kb], pacc[qb]);
       }
     }
-    __syncthreads();
+  };
+
+  // ---- phase 2. A: dV += P^T dO (P read back from the hand-off buffer). B: dS, dK += dS^T Q.
+  auto phase2 = [&](const int qt, auto st_tag, auto xb_tag, const f32x16 (&pacc)[2]) {
+    constexpr int ST = decltype(st_tag)::value, XB = decltype(xb_tag)::value;
+    const int qrow0 = qt * BM;
+    const unsigned char* Qt = stage_ptr(st_tag, 0);
+    const unsigned char* Gt = stage_ptr(st_tag, 1);
     if (!isB) {
-      // ---- A, phase 2: dV += P^T dO (P read back from the hand-off buffer)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int c8 = 0; c8 < 2; ++c8) {
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, sm.xch[pair][0][qb][c8][lane]);
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, sm.xch[XB][pair][0][qb][c8][lane]);
           const uint32_t base = (uint32_t)((32 * qb + 16 * c8) * kRowBytes);
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
@@ -843,17 +886,16 @@ void bwd_dkdv_kernel2(BwdArgs a) {
                              pb, acc[db]);
         }
     } else {
-      // ---- B, phase 2: dS, dK += dS^T Q
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         bf16x8 dsb[2];
 #pragma unroll
         for (int c8 = 0; c8 < 2; ++c8) {
           float pv[8], dsv[8];
-          unpack8(sm.xch[pair][0][qb][c8][lane], pv);
+          unpack8(sm.xch[XB][pair][0][qb][c8][lane], pv);
           if (SOFTMAX) {
             const int rbase = 32 * qb + 16 * c8 + 8 * hh;
-            const float* dl = sm.dlt[st];
+            const float* dl = sm.dlt[ST];
             const float4 y0 = *reinterpret_cast<const float4*>(&dl[rbase]);
             const float4 y1 = *reinterpret_cast<const float4*>(&dl[rbase + 4]);
             const float d8[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
@@ -861,7 +903,7 @@ void bwd_dkdv_kernel2(BwdArgs a) {
             for (int j = 0; j < 8; ++j) dsv[j] = pv[j] * (pacc[qb][8 * c8 + j] - d8[j]);
           } else {
             float gv[8];
-            unpack8(sm.xch[pair][1][qb][c8][lane], gv);
+            unpack8(sm.xch[XB][pair][Smem::NPG - 1][qb][c8][lane], gv);
 #pragma unroll
             for (int j = 0; j < 8; ++j) dsv[j] = pacc[qb][8 * c8 + j] * gv[j];
           }
@@ -877,6 +919,78 @@ void bwd_dkdv_kernel2(BwdArgs a) {
                              dsb[c8], acc[db]);
           }
       }
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if constexpr (ONEBAR) {
+    // Tile t lives in ring stage and hand-off buffer (t - q0) % 3. Step t: phase 1 of t; wait for
+    // tile t+1 (loaded during step t-1) and publish its statistics; barrier; load tile t+2 into the
+    // stage tile t-1 used; phase 2 of t. Every wave is past phase 2 of t-1 when the barrier of step
+    // t releases, so the stage and buffers it overwrites are free, and A's phase 1 of t+1 may run
+    // while B still finishes phase 2 of t.
+    if (q0 < q1) {
+      issue_tile(q0, 0);
+      load_stats(q0);
+    }
+    if (q0 + 1 < q1) issue_tile(q0 + 1, 1);
+    wait_vm();
+    write_stats(0);
+    if (q0 + 1 < q1) load_stats(q0 + 1);
+    if (q0 < q1) fill(q0);
+    __syncthreads();  // also publishes wave 0's bias table
+    auto step = [&](const int qt, auto st_tag) {
+      constexpr int ST = decltype(st_tag)::value;
+      f32x16 pacc[2];
+      phase1(qt, st_tag, st_tag, pacc);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm();
+      if (qt + 1 < q1) write_stats((ST + 1) % 3);
+      __syncthreads();
+      if (qt + 2 < q1) {
+        issue_tile(qt + 2, (ST + 2) % 3);
+        load_stats(qt + 2);
+      }
+      phase2(qt, st_tag, st_tag, pacc);
+      if (qt + 1 < q1) fill(qt + 1);
+      // Keep the compiler from hoisting the next tile's loads into this phase (register pressure).
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int qt = q0; qt < q1; qt += 3) {
+      step(qt, I0{});
+      if (qt + 1 < q1) step(qt + 1, I1{});
+      if (qt + 2 < q1) step(qt + 2, I2{});
+    }
+  } else {
+    // Two barriers per tile: the first publishes the tile and retires the other stage, the second
+    // publishes the hand-off buffer.
+    if (q0 < q1) {
+      issue_tile(q0, 0);
+      load_stats(q0);
+    }
+    // Wave 0 wrote the bias table (and the B waves cleared their gradient bins); A waves read the
+    // table in the first tile's diagonal fill.
+    if (BIAS == kBiasBucket) __syncthreads();
+    auto step = [&](const int qt, auto st_tag) {
+      constexpr int ST = decltype(st_tag)::value;
+      write_stats(ST);
+      wait_vm();
+      fill(qt);
+      __syncthreads();
+      if (qt + 1 < q1) {
+        issue_tile(qt + 1, ST ^ 1);
+        load_stats(qt + 1);
+      }
+      f32x16 pacc[2];
+      phase1(qt, st_tag, I0{}, pacc);
+      __syncthreads();
+      phase2(qt, st_tag, I0{}, pacc);
+    };
+    for (int qt = q0; qt < q1; qt += 2) {
+      step(qt, I0{});
+      if (qt + 1 < q1) step(qt + 1, I1{});
     }
   }
 
