@@ -324,12 +324,17 @@ void bwd_dq_kernel2(BwdArgs a) {
     const int key0 = kt * BN;
     wait_vm();
     // Bias of score (qi, key) at diag[31 - l32 + key - key0], ascending in register order.
-    if (BIAS == kBiasBucket) fill_diag(sm.diag[wave], sm.tab, key0 - row0 - 31, inv_scale, lane);
+    if (BIAS == kBiasBucket && !(CAUSAL && key0 > row0 + 31))
+      fill_diag(sm.diag[wave], sm.tab, key0 - row0 - 31, inv_scale, lane);
     __syncthreads();
     if (kt + 1 < k1) {
       load_tile64(ld, kr, (kt + 1) * BN, rs, sm.kv[ST ^ 1][0], wave);
       load_tile64(ld, vr, (kt + 1) * BN, rs, sm.kv[ST ^ 1][1], wave);
     }
+    // Under the causal mask a tile whose first key lies past this wave's last query contributes
+    // nothing; the wave skips its work (it has taken part in the barrier and the loads above) and
+    // leaves the SIMD to the other workgroup's wave.
+    if (CAUSAL && key0 > row0 + 31) return;
     const unsigned char* Kt = sm.kv[ST][0];
     const unsigned char* Vt = sm.kv[ST][1];
 
