@@ -32,6 +32,25 @@ DEFAULT_WORKLOAD = "causal_bucket"
 # FLOPs each kernel must execute per visible pair and head (its own matrix products):
 #   forward: S = QK^T, O = PV; dK/dV: S, dP = dO V^T, dV = P^T dO, dK = dS^T Q; dQ: S, dP, dQ = dS K
 KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dkdv": 8, "dq": 6}
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # about 315
+
+
+def kernel_bytes(kernel: str, Tq: int, Tkv: int, H: int, D: int, out_bytes: int, softmax: bool) -> int:
+    """Algorithmic HBM bytes of one launch: every tensor the kernel must read or write, once.
+
+    bf16 inputs (2 bytes per element); outputs and gradients in the chosen dtype; lse and Delta fp32.
+    forward: read Q, K, V; write O (and lse). dK/dV: read Q, dO, K, V (lse, Delta); write dK, dV.
+    dQ: read Q, dO, K, V (lse, Delta); write dQ.
+    """
+    q, kv = Tq * H * D, Tkv * H * D
+    stats = 2 * Tq * H * 4 if softmax else 0
+    if kernel == "forward":
+        return 2 * (q + 2 * kv) + out_bytes * q + (Tq * H * 4 if softmax else 0)
+    if kernel == "dkdv":
+        return 2 * (2 * q + 2 * kv) + stats + out_bytes * 2 * kv
+    return 2 * (2 * q + 2 * kv) + stats + out_bytes * q
+
+
 KERNEL_SOURCES = {"forward": ["fwd.hip", "device_common.h", "tile_lds.h", "jfa_internal.h"],
                   "dkdv": ["bwd.hip", "device_common.h", "tile_lds.h", "jfa_internal.h"],
                   "dq": ["bwd.hip", "device_common.h", "tile_lds.h", "jfa_internal.h"]}
@@ -207,14 +226,24 @@ def main() -> int:
     value = (fw + bw) / (elapsed / args.steps) / 1e12
     pairs = visible_pairs(x.q_off, x.kv_off, causal) * w.H
 
-    # roofline of the dominant kernel (largest share of the timed region)
+    # roofline of the dominant kernel (largest share of the timed region): its algorithmic FLOPs and
+    # bytes per launch decide the bound (MFMA above the ridge point, HBM below it)
     dom = max((kk for kk in kernels if kk in KERNEL_FLOPS_PER_PAIR_D), key=lambda kk: kernels[kk]["total_ms"])
     per_launch_flops = KERNEL_FLOPS_PER_PAIR_D[dom] * w.D * pairs / kernels[dom]["launches_per_step"]
-    achieved = per_launch_flops / (kernels[dom]["avg_ms"] * 1e-3) / 1e12
+    out_b = 4 if args.out_dtype == "f32" else 2
+    per_launch_bytes = kernel_bytes(dom, int(x.q_off[-1]), int(x.kv_off[-1]), w.H, w.D, out_b, w.act == "softmax")
+    secs = kernels[dom]["avg_ms"] * 1e-3
     traffic = counter_traffic(dom, args.workload)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom,
-                "algorithmic_flops_per_launch": per_launch_flops}
+    if per_launch_flops / per_launch_bytes >= RIDGE_FLOP_PER_BYTE:
+        achieved = per_launch_flops / secs / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom,
+                    "algorithmic_flops_per_launch": per_launch_flops, "algorithmic_bytes_per_launch": per_launch_bytes}
+    else:
+        achieved = per_launch_bytes / secs / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom,
+                    "algorithmic_flops_per_launch": per_launch_flops, "algorithmic_bytes_per_launch": per_launch_bytes}
 
     line = {
         "metric": METRIC,
