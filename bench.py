@@ -3,7 +3,8 @@
 
 A step is one pass of the whole hot path over one batch: the forward pass (work-list driven
 forward kernel and, when the plan split items, the combine kernel) and the backward pass
-(Delta preprocess, dK/dV kernel, dQ kernel, partial reduces), all through the C ABI. The plan
+(dQ kernel, which also forms Delta = rowsum(dO * O), dK/dV kernel, partial reduces), all through
+the C ABI. The plan
 (offset validation and the longest-first work lists) is built once per batch of offsets before
 the timed region; its host time is reported as ``plan_ms``.
 

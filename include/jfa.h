@@ -144,8 +144,8 @@ jfa_status jfa_plan_info(jfa_plan_t plan, int32_t* info, size_t n);
 
 /* Per-kernel timing with HIP events recorded around every launch of this plan (for
  * measurement; adds two event records per launch while on). Kernel ids: 0 forward,
- * 1 forward combine, 2 backward preprocess, 3 dK/dV, 4 dQ, 5 backward partial reduce,
- * 6 bias-gradient clear and finish.
+ * 1 forward combine, 3 dK/dV, 4 dQ (which also computes rowsum(dO * O) for dK/dV), 5 backward
+ * partial reduce, 6 bias-gradient clear and finish (2 is not used).
  * jfa_timing_read waits for the recorded events and returns their summed time and count;
  * jfa_timing_enable(plan, 1) also clears previous records. Not thread safe. */
 jfa_status jfa_timing_enable(jfa_plan_t plan, int32_t enable);

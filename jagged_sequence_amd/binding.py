@@ -30,7 +30,7 @@ BIASES = {"none": 0, "scalar": 1, "bucket": 2}
 DTYPES = {"bf16": 0, "f32": 1}
 PLAN_HOST_ONLY = 0x1
 PLAN_NO_SPLIT = 0x2
-KERNELS = {"forward": 0, "combine": 1, "preprocess": 2, "dkdv": 3, "dq": 4, "reduce": 5, "dbias": 6}
+KERNELS = {"forward": 0, "combine": 1, "dkdv": 3, "dq": 4, "reduce": 5, "dbias": 6}
 SYMBOLS = ["jfa_plan", "jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_plan_schedule", "jfa_plan_info",
            "jfa_timing_enable", "jfa_timing_read", "jfa_plan_destroy", "jfa_status_string", "jfa_last_error"]
 

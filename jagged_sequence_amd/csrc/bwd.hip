@@ -19,24 +19,20 @@ namespace jfa {
 namespace {
 
 // ---------------------------------------------------------------- Delta_i = <dO_i, O_i>
-template <int D>
-__global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdArgs a) {
-  constexpr int TPR = D / 8;  // threads per (token, head) row, 8 elements each
-  const int rows = a.Tq * a.H;
-  const int row = blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
-  const int part = threadIdx.x % TPR;
+// Dot product of one lane's dO elements (NKB groups of 8: elements 16 kb + 0..7 from `base`) with the
+// same elements of the forward output (bf16 or fp32), in fp32.
+template <int NKB>
+__device__ __forceinline__ float row_dot_out(const BwdArgs& a, size_t base, const bf16x8 (&df)[NKB]) {
   float acc = 0.0f;
-  if (row < rows) {
-    const size_t base = (size_t)row * D + part * 8;
-    uint4 g = load16(a.dout + base);
-    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
     float o[8];
     if (a.out_f32) {
-      const float* op = reinterpret_cast<const float*>(a.out) + base;
-      float4 x0 = *reinterpret_cast<const float4*>(op), x1 = *reinterpret_cast<const float4*>(op + 4);
+      const float* op = reinterpret_cast<const float*>(a.out) + base + 16 * kb;
+      const float4 x0 = *reinterpret_cast<const float4*>(op), x1 = *reinterpret_cast<const float4*>(op + 4);
       o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w; o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
     } else {
-      uint4 x = load16(reinterpret_cast<const uint16_t*>(a.out) + base);
+      const uint4 x = load16(reinterpret_cast<const uint16_t*>(a.out) + base + 16 * kb);
       const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -45,17 +41,9 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc += __builtin_bit_cast(float, gw[j] << 16) * o[2 * j];
-      acc += __builtin_bit_cast(float, gw[j] & 0xffff0000u) * o[2 * j + 1];
-    }
+    for (int j = 0; j < 8; ++j) acc += (float)df[kb][j] * o[j];
   }
-#pragma unroll
-  for (int w = TPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
-  if (row < rows && part == 0) {
-    const int tok = row / a.H, h = row % a.H;
-    a.delta[(size_t)h * a.Tq + tok] = acc;
-  }
+  return acc;
 }
 
 // 4 rows x 8 dims of a [T, H, D] tensor: loaded so that one thread can store them both row-major
@@ -141,10 +129,17 @@ void bwd_dq_kernel(BwdArgs a) {
     }
   }
   float nlse2 = kNegInf, dlt = 0.0f;  // -lse in log2 units; -inf makes every P of the row 0
-  if (SOFTMAX && qi < Lq) {
-    const float l = a.lse[(size_t)h * a.Tq + qs + qi];
-    nlse2 = l == kNegInf ? kNegInf : -(l - (BIAS == kBiasScalar ? bias_c : 0.0f)) * kLog2e;
-    dlt = a.delta[(size_t)h * a.Tq + qs + qi];
+  if (SOFTMAX) {
+    // Delta_i = <dO_i, O_i>: this lane's half of the row, then the other half from lane ^ 32. The
+    // first piece of the query tile (k0 == 0) also stores it for the dK/dV kernel, which runs after.
+    float part = 0.0f;
+    if (qi < Lq) {
+      const float l = a.lse[(size_t)h * a.Tq + qs + qi];
+      nlse2 = l == kNegInf ? kNegInf : -(l - (BIAS == kBiasScalar ? bias_c : 0.0f)) * kLog2e;
+      part = row_dot_out<NKB>(a, ((size_t)(qs + qi) * a.H + h) * D + hh * 8, df);
+    }
+    dlt = part + __shfl_xor(part, 32);
+    if (k0 == 0 && hh == 0 && qi < Lq) a.delta[(size_t)h * a.Tq + qs + qi] = dlt;
   }
   const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
   const float invL = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
@@ -293,10 +288,17 @@ void bwd_dq_kernel2(BwdArgs a) {
     }
   }
   float nlse2 = kNegInf, dlt = 0.0f;  // -lse in log2 units; -inf makes every P of the row 0
-  if (SOFTMAX && qi < Lq) {
-    const float l = a.lse[(size_t)h * a.Tq + qs + qi];
-    nlse2 = l == kNegInf ? kNegInf : -(l - (BIAS == kBiasScalar ? bias_c : 0.0f)) * kLog2e;
-    dlt = a.delta[(size_t)h * a.Tq + qs + qi];
+  if (SOFTMAX) {
+    // Delta_i = <dO_i, O_i>: this lane's half of the row, then the other half from lane ^ 32. The
+    // first piece of the query tile (k0 == 0) also stores it for the dK/dV kernel, which runs after.
+    float part = 0.0f;
+    if (qi < Lq) {
+      const float l = a.lse[(size_t)h * a.Tq + qs + qi];
+      nlse2 = l == kNegInf ? kNegInf : -(l - (BIAS == kBiasScalar ? bias_c : 0.0f)) * kLog2e;
+      part = row_dot_out<NKB>(a, ((size_t)(qs + qi) * a.H + h) * D + hh * 8, df);
+    }
+    dlt = part + __shfl_xor(part, 32);
+    if (k0 == 0 && hh == 0 && qi < Lq) a.delta[(size_t)h * a.Tq + qs + qi] = dlt;
   }
   const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
   const float invL = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
@@ -1167,17 +1169,6 @@ constexpr auto dq_select = D == 128 ? &bwd_dq_kernel2<ACT, BIAS, CAUSAL> : &bwd_
 
 }  // namespace
 
-hipError_t launch_bwd_preprocess(const BwdArgs& a, const Modes& m, hipStream_t s) {
-  const long rows = (long)a.Tq * a.H;
-  if (rows <= 0) return hipSuccess;
-  const int per_block = kThreads / (m.D / 8);
-  const int grid = (int)((rows + per_block - 1) / per_block);
-  if (m.D == 64)
-    hipLaunchKernelGGL(bwd_preprocess_kernel<64>, dim3(grid), dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(bwd_preprocess_kernel<128>, dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

@@ -501,18 +501,15 @@ jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* 
     st = timed(P, 6, s, [&] { return launch_bwd_dbias_clear(a, m, s); }, "bias-gradient clear launch");
     if (st != JFA_OK) return st;
   }
-  if (softmax) {
-    st = timed(P, 2, s, [&] { return launch_bwd_preprocess(a, m, s); }, "backward preprocess launch");
-    if (st != JFA_OK) return st;
-  }
-  st = timed(P, 3, s, [&] { return launch_bwd_dkdv(a, m, (int)P->lists[kKv].n_items(), s); }, "dK/dV launch");
-  if (st != JFA_OK) return st;
+  // dQ first: it also computes Delta = rowsum(dO * O) (softmax) for the dK/dV kernel.
   st = timed(P, 4, s, [&] { return launch_bwd_dq(a, m, (int)P->lists[kDq].n_items(), s); }, "dQ launch");
   if (st != JFA_OK) return st;
   if (P->lists[kDq].n_groups() > 0) {
     st = timed(P, 5, s, [&] { return launch_bwd_reduce_dq(a, m, (int)P->lists[kDq].n_groups(), s); }, "dQ reduce launch");
     if (st != JFA_OK) return st;
   }
+  st = timed(P, 3, s, [&] { return launch_bwd_dkdv(a, m, (int)P->lists[kKv].n_items(), s); }, "dK/dV launch");
+  if (st != JFA_OK) return st;
   if (P->lists[kKv].n_groups() > 0) {
     st = timed(P, 5, s, [&] { return launch_bwd_reduce_dkdv(a, m, (int)P->lists[kKv].n_groups(), s); }, "dK/dV reduce launch");
     if (st != JFA_OK) return st;

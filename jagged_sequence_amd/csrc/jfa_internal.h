@@ -54,7 +54,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;    // [H][Tq] fp32 (softmax)
+  float* delta;    // [H][Tq] fp32 (softmax): Delta = rowsum(dO * O), written by the dQ kernel
   float* part_dq;  // [slots][kDqBM][D]
   float* part_dk;  // [slots][kKvBN][D]
   float* part_dv;  // [slots][kKvBN][D]
@@ -87,7 +87,6 @@ constexpr int kBiasGrad = 4;
 // Launchers (defined next to their kernels). Each returns the hipGetLastError() of its launch.
 hipError_t launch_forward(const FwdArgs& a, const Modes& m, int n_items, hipStream_t s);
 hipError_t launch_forward_combine(const FwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
-hipError_t launch_bwd_preprocess(const BwdArgs& a, const Modes& m, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n_items, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n_items, hipStream_t s);
 hipError_t launch_bwd_reduce_dq(const BwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
