@@ -135,7 +135,7 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
+        if h is not None and h.value and LIB is not None:  # LIB is None during interpreter shutdown
             LIB.jfa_plan_destroy(h)
             self._h = None
 

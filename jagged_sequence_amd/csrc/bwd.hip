@@ -657,34 +657,34 @@ void bwd_dkdv_kernel(BwdArgs a) {
 // two waves fit per SIMD and A's exponentials overlap B's matrix products. Q and dO tiles are loaded
 // straight into a two-stage LDS ring (swizzled row-major, no staging registers) one tile ahead of the
 // compute; the Q^T and dO^T operands come from transposing LDS reads.
-template <bool ONEBAR, bool GDPA>
+template <bool ONEBAR, bool GDPA, int NP>
 struct alignas(16) KvSmem2;
 
-// Two barriers per tile: a two-stage Q/dO ring and one hand-off buffer.
-template <bool GDPA>
-struct alignas(16) KvSmem2<false, GDPA> {
+// Two barriers per tile: a two-stage Q/dO ring and one hand-off buffer (NP wave pairs).
+template <bool GDPA, int NP>
+struct alignas(16) KvSmem2<false, GDPA, NP> {
   static constexpr int NPG = GDPA ? 2 : 1;      // P, and act'/Lkv for GDPA
   unsigned char qg[2][2][kKvBM * kRowBytes];    // [stage][0 = Q, 1 = dO]
   float lse2[2][kKvBM];                         // -lse in log2 units (softmax)
   float dlt[2][kKvBM];
-  uint4 xch[1][4][NPG][2][2][64];               // [buffer][pair][P / act'][q block][8-row half][lane]: 8 bf16
+  uint4 xch[1][NP][NPG][2][2][64];              // [buffer][pair][P / act'][q block][8-row half][lane]: 8 bf16
   float tab[kBuckets];
-  float diag[4][kDiagLen];
-  unsigned long long dbh[4][kDbiasBins];        // per-B-wave bias-gradient bins (fixed point)
+  float diag[NP][kDiagLen];
+  unsigned long long dbh[NP][kDbiasBins];       // per-B-wave bias-gradient bins (fixed point)
 };
 
 // One barrier per tile: a three-stage ring and three hand-off buffers (152 KB). The small arrays
 // come first so that their LDS offsets fit the immediates of ds_read / ds_read2; the ring stages
 // are reached through a wave-uniform base offset.
-template <bool GDPA>
-struct alignas(16) KvSmem2<true, GDPA> {
+template <bool GDPA, int NP>
+struct alignas(16) KvSmem2<true, GDPA, NP> {
   static constexpr int NPG = GDPA ? 2 : 1;
-  float diag[4][kDiagLen];  // first: the 8-byte pair reads of a lane's bias window share one base
+  float diag[NP][kDiagLen];  // first: the 8-byte pair reads of a lane's bias window share one base
   float tab[kBuckets];
-  unsigned long long dbh[4][kDbiasBins];
+  unsigned long long dbh[NP][kDbiasBins];
   float lse2[3][kKvBM];
   float dlt[3][kKvBM];
-  uint4 xch[3][4][NPG][2][2][64];
+  uint4 xch[3][NP][NPG][2][2][64];
   unsigned char qg[3][2][kKvBM * kRowBytes];
 };
 
@@ -710,23 +710,28 @@ __device__ __forceinline__ void unpack8(uint4 w, float (&x)[8]) {
   }
 }
 
-template <int ACT, int BIASX, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+// NP wave pairs per workgroup own NP x 32 keys: NP = 4 (128 keys, 8 waves, one workgroup per CU) in
+// general; NP = 2 (64 keys, 4 waves, two workgroups per CU, about 75 KB of LDS) when every sequence
+// has a single query tile, where an item is one latency-bound pass and two resident workgroups
+// overlap one's loads with the other's work.
+template <int ACT, int BIASX, bool CAUSAL, int NP>
+__global__ __attribute__((amdgpu_flat_work_group_size(NP * 128, NP * 128), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel2(BwdArgs a) {
-  constexpr int D = 128, BM = kKvBM, BN = kKvBN, NKB = D / 16, NDB = D / 32;
+  constexpr int D = 128, BM = kKvBM, BN = 32 * NP, NKB = D / 16, NDB = D / 32;
   constexpr int BIAS = BIASX & 3;
   constexpr bool DBIAS = (BIASX & kBiasGrad) != 0;
   constexpr bool SOFTMAX = ACT == kSoftmax;
   // Softmax hands over P only, so a third ring stage and three hand-off buffers fit in LDS and one
-  // barrier per query tile suffices; GDPA also hands over act'/Lkv and keeps two barriers per tile.
-  constexpr bool ONEBAR = SOFTMAX;
-  using Smem = KvSmem2<ONEBAR, !SOFTMAX>;
+  // barrier per query tile suffices; GDPA also hands over act'/Lkv and keeps two barriers per tile,
+  // as does the short form (NP = 2), whose items have a single query tile.
+  constexpr bool ONEBAR = SOFTMAX && NP == 4;
+  using Smem = KvSmem2<ONEBAR, !SOFTMAX, NP>;
   __shared__ Smem sm;
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pair = wave & 3;
-  const bool isB = wave >= 4;
+  const int pair = wave % NP;
+  const bool isB = wave >= NP;
   const int32_t* it = a.kv_items + (size_t)blockIdx.x * kItemInts;
   const int b = it[0], h = it[1], kt = it[2], q0 = it[3], q1 = it[4], slot = it[5];
   const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
@@ -783,9 +788,15 @@ void bwd_dkdv_kernel2(BwdArgs a) {
   };
   auto issue_tile = [&](int qt, int stg) {
     // loader offsets recomputed per tile (two VALU each) rather than held in registers
-    const TileLoader ld = make_loader64_w8(wave, lane_opaque(lane), rs);
-    load_tile64_w8(ld, qsr, qt * BM, rs, sm.qg[stg][0], wave);
-    load_tile64_w8(ld, gsr, qt * BM, rs, sm.qg[stg][1], wave);
+    if constexpr (NP == 4) {
+      const TileLoader ld = make_loader64_w8(wave, lane_opaque(lane), rs);
+      load_tile64_w8(ld, qsr, qt * BM, rs, sm.qg[stg][0], wave);
+      load_tile64_w8(ld, gsr, qt * BM, rs, sm.qg[stg][1], wave);
+    } else {
+      const TileLoader ld = make_loader64(wave, lane_opaque(lane), rs);
+      load_tile64(ld, qsr, qt * BM, rs, sm.qg[stg][0], wave);
+      load_tile64(ld, gsr, qt * BM, rs, sm.qg[stg][1], wave);
+    }
   };
   auto fill = [&](int qt) {
     if (BIAS == kBiasBucket && !isB) fill_diag(sm.diag[pair], sm.tab, qt * BM - key_w - 31, inv_scale, lane);
@@ -1066,13 +1077,14 @@ __global__ __launch_bounds__(256) void bwd_reduce_dq_kernel(BwdArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_dkdv_kernel(BwdArgs a) {
-  constexpr int BN = kKvBN, HALF = D / 2;
+  constexpr int HALF = D / 2;
+  const int BN = a.kv_bn;
   const int32_t* g = a.kv_groups + (size_t)blockIdx.x * kGroupInts;
   const int b = g[0], h = g[1], kt = g[2], slot0 = g[3], R = g[4];
   const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
   const int row = threadIdx.x >> 1, part = threadIdx.x & 1;
   const int kj = kt * BN + row;
-  if (kj >= Lkv) return;
+  if (row >= BN || kj >= Lkv) return;
   for (int which = 0; which < 2; ++which) {
     const float* src = which == 0 ? a.part_dk : a.part_dv;
     float acc[HALF];
@@ -1113,8 +1125,9 @@ __global__ __launch_bounds__(256) void bwd_dbias_finish_kernel(BwdArgs a, int n)
 // ---------------------------------------------------------------- dispatch
 // D = 128 runs the LDS-ring kernels; D = 64 the register-staged ones.
 constexpr int kDkdvThreads128 = 512;
-template <int D, int ACT, int BIASX, bool CAUSAL>
-constexpr auto dkdv_select = D == 128 ? &bwd_dkdv_kernel2<ACT, BIASX, CAUSAL> : &bwd_dkdv_kernel<D, ACT, BIASX, CAUSAL>;
+template <int D, int ACT, int BIASX, bool CAUSAL, int NP = 4>
+constexpr auto dkdv_select =
+    D == 128 ? &bwd_dkdv_kernel2<ACT, BIASX, CAUSAL, NP> : &bwd_dkdv_kernel<D, ACT, BIASX, CAUSAL>;
 template <int D, int ACT, int BIAS, bool CAUSAL>
 constexpr auto dq_select = D == 128 ? &bwd_dq_kernel2<ACT, BIAS, CAUSAL> : &bwd_dq_kernel<D, ACT, BIAS, CAUSAL>;
 
@@ -1150,7 +1163,10 @@ constexpr auto dq_select = D == 128 ? &bwd_dq_kernel2<ACT, BIAS, CAUSAL> : &bwd_
   }
 
 // The dK/dV kernels also come in bias-gradient variants (bias | kBiasGrad).
-#define JFA_GO_CAUSAL(KERNEL, DD, AA, BB, m, go) \
+#define JFA_GO_CAUSAL(KERNEL, DD, AA, BB, m, go)                                                   \
+  if constexpr (DD == 128 && AA == kSoftmax) {                                                     \
+    if (m.kv_short) return m.causal ? go(KERNEL<DD, AA, BB, true, 2>) : go(KERNEL<DD, AA, BB, false, 2>); \
+  }                                                                                                \
   return m.causal ? go(KERNEL<DD, AA, BB, true>) : go(KERNEL<DD, AA, BB, false>);
 #define JFA_DISPATCH_BIAS_GRAD(KERNEL, DD, AA, m, go)                                       \
   switch (m.bias | (m.dbias && !(m.bias == kBiasScalar && AA == kSoftmax) ? kBiasGrad : 0)) { \
@@ -1178,7 +1194,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n, hipStream_t s)
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  const int block = m.D == 128 ? kDkdvThreads128 : kThreads;
+  const int block = m.D == 128 ? (m.kv_short ? kDkdvThreads128 / 2 : kDkdvThreads128) : kThreads;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(n), dim3(block), 0, s, a);
     return hipGetLastError();
@@ -1232,8 +1248,10 @@ int occupancy_dkdv(const Modes& m) {
   int n = 0;
   hipError_t e = m.D == 64
                      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dkdv_kernel<64, kSoftmax, kBiasBucket, true>, kThreads, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, dkdv_select<128, kSoftmax, kBiasBucket, true>,
-                                                                    kDkdvThreads128, 0);
+                     : m.kv_short ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                        &n, dkdv_select<128, kSoftmax, kBiasScalar, false, 2>, kDkdvThreads128 / 2, 0)
+                                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                                        &n, dkdv_select<128, kSoftmax, kBiasBucket, true>, kDkdvThreads128, 0);
   return (e == hipSuccess && n > 0) ? n : 1;
 }
 

@@ -184,6 +184,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct jfa_plan_s {
   int B = 0, H = 0, D = 0, Tq = 0, Tkv = 0;
+  int kv_bn = kKvBN;  // keys per dK/dV item
   Modes modes{};
   float scale = 0.0f;
   int out_f32 = 0, grad_f32 = 0;
@@ -307,6 +308,13 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   P->Tq = P->q_off[P->B];
   P->Tkv = P->kv_off[P->B];
   P->modes = Modes{p.head_dim, p.act, p.bias, p.mask == JFA_MASK_CAUSAL ? 1 : 0};
+  {
+    int max_lq = 0;
+    for (int x : lq) max_lq = std::max(max_lq, x);
+    // softmax only: the GDPA hand-off (P and act'/Lkv) needs too much LDS for two workgroups per CU
+    P->modes.kv_short = (p.head_dim == 128 && p.act == kSoftmax && max_lq <= kKvBM) ? 1 : 0;
+  }
+  P->kv_bn = P->modes.kv_short ? kKvBNShort : kKvBN;
   P->scale = p.scale != 0.0f ? p.scale : 1.0f / std::sqrt((float)p.head_dim);
   P->out_f32 = p.out_dtype == JFA_F32;
   P->grad_f32 = p.grad_dtype == JFA_F32;
@@ -334,7 +342,7 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   const bool causal = P->modes.causal != 0;
   query_tile_list(lq, lkv, P->H, causal, kFwdBM, kFwdBN, slots[kFwd], split, P->lists[kFwd]);
   query_tile_list(lq, lkv, P->H, causal, kDqBM, kDqBN, slots[kDq], split, P->lists[kDq]);
-  key_tile_list(lq, lkv, P->H, causal, kKvBM, kKvBN, slots[kKv], split, P->lists[kKv]);
+  key_tile_list(lq, lkv, P->H, causal, kKvBM, P->kv_bn, slots[kKv], split, P->lists[kKv]);
   for (auto& L : P->lists) L.order = dispatch_order(L);
 
   // workspace layout
@@ -348,9 +356,9 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   P->off_part_dq = o;
   o += align256((size_t)P->lists[kDq].nslots * kDqBM * D * 4);
   P->off_part_dk = o;
-  o += align256((size_t)P->lists[kKv].nslots * kKvBN * D * 4);
+  o += align256((size_t)P->lists[kKv].nslots * P->kv_bn * D * 4);
   P->off_part_dv = o;
-  o += align256((size_t)P->lists[kKv].nslots * kKvBN * D * 4);
+  o += align256((size_t)P->lists[kKv].nslots * P->kv_bn * D * 4);
   P->off_dbias = o;  // fixed-point bias-gradient totals, used when the caller asks for dbias
   if (P->modes.bias != kBiasNone) o += align256((size_t)P->H * (P->modes.bias == kBiasBucket ? kBuckets : 1) * 8);
   P->ws_bwd = o;
@@ -495,6 +503,7 @@ jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* 
   a.scale = P->scale;
   a.out_f32 = P->out_f32;
   a.grad_f32 = P->grad_f32;
+  a.kv_bn = P->kv_bn;
   Modes m = P->modes;
   m.dbias = dbias ? 1 : 0;
   if (dbias) {
@@ -538,7 +547,7 @@ jfa_status jfa_plan_schedule(jfa_plan_t P, int32_t which, int32_t* out, size_t c
 
 jfa_status jfa_plan_info(jfa_plan_t P, int32_t* info, size_t n) {
   if (!P || !info) return fail(JFA_ERR_NULL_ARG, "plan or info is NULL");
-  const int32_t v[9] = {kFwdBM, kFwdBN, kDqBM, kDqBN, kKvBM, kKvBN, P->lists[kFwd].slots, P->lists[kDq].slots,
+  const int32_t v[9] = {kFwdBM, kFwdBN, kDqBM, kDqBN, kKvBM, P->kv_bn, P->lists[kFwd].slots, P->lists[kDq].slots,
                         P->lists[kKv].slots};
   std::copy_n(v, std::min<size_t>(n, 9), info);
   return JFA_OK;

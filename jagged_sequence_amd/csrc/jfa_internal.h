@@ -14,6 +14,9 @@ namespace jfa {
 constexpr int kFwdBM = 128, kFwdBN = 64;
 constexpr int kDqBM = 128, kDqBN = 64;
 constexpr int kKvBM = 64, kKvBN = 128;
+// When every sequence has at most kKvBM queries (one query tile), dK/dV items are latency bound;
+// softmax with D = 128 then uses half-width items (64 keys, 4-wave workgroups, two per CU).
+constexpr int kKvBNShort = 64;
 constexpr int kThreads = 256;
 constexpr int kItemInts = 8;   // device record: b, h, tile, lo, hi, slot, 0, 0
 constexpr int kGroupInts = 8;  // device record: b, h, tile, slot0, R, 0, 0, 0
@@ -70,6 +73,7 @@ struct BwdArgs {
   float scale;
   int out_f32;
   int grad_f32;
+  int kv_bn;  // keys per dK/dV item (kKvBN or kKvBNShort)
 };
 
 struct Modes {
@@ -77,7 +81,8 @@ struct Modes {
   int act;
   int bias;
   int causal;
-  int dbias;  // the bias gradient is requested
+  int dbias;     // the bias gradient is requested
+  int kv_short;  // dK/dV items of kKvBNShort keys (D = 128, every Lq <= kKvBM)
 };
 
 // Bias template argument of the dK/dV kernels: kBiasScalar / kBiasBucket, plus kBiasGrad when the

@@ -107,6 +107,18 @@ def test_dispatch_order_keeps_groups_on_one_xcd(name):
         assert max(tot) - min(tot) <= max(gsize.values()) + max(1, sum(gsize.values()) // 100)
 
 
+def test_short_query_problems_use_half_width_key_items():
+    # softmax, D = 128 and every sequence with at most 64 queries: 64-key dK/dV items
+    assert _host_plan([1, 64, 30], [500, 64, 7], 2, 128, mask="none").info()["kv_bn"] == 64
+    assert _host_plan([1, 64, 30], [1, 64, 30], 2, 128, mask="causal").info()["kv_bn"] == 64
+    assert _host_plan([1, 65, 30], [500, 65, 7], 2, 128, mask="none").info()["kv_bn"] == 128
+    assert _host_plan([1, 64, 30], [500, 64, 7], 2, 128, mask="none", act="silu").info()["kv_bn"] == 128
+    assert _host_plan([1, 64, 30], [500, 64, 7], 2, 64, mask="none").info()["kv_bn"] == 128
+    w = ji.WORKLOADS["target_attn"]
+    lq, lkv = ji.lengths(w)
+    assert _host_plan(lq, lkv, w.H, w.D, mask=w.mask, act=w.act, bias=w.bias).info()["kv_bn"] == 64
+
+
 def test_workspace_sizes():
     lq = [700, 129, 1]
     plan = _host_plan(lq, lq, 2, mask="causal", num_slots=16)

@@ -97,3 +97,15 @@ def test_dbias_full_causal_bucket_workload():
     ref = oracle(x)
     err = check_dbias(x, to_np(gpu["dbias"]), ref["dbias"])
     say(f"  dbias rel-L2 {err:.2e}")
+
+
+@pytest.mark.parametrize("bias", ["scalar", "bucket"])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_dbias_short_query_items(mask, bias):
+    """Softmax problems whose sequences all have at most 64 queries use the half-width dK/dV items."""
+    lq, lkv = ([1, 37, 64, 50], [1, 37, 64, 50]) if mask == "causal" else ([1, 37, 64, 5], [300, 64, 129, 1000])
+    x = ji.make_inputs(lq, lkv, 2, 128, wid=47, mask=mask, act="softmax", bias_kind=bias, bias_sigma=0.5)
+    say(f"case dbias short-query mask={mask} bias={bias}")
+    gpu = run_gpu(x, dbias=True)
+    assert gpu["plan"].info()["kv_bn"] == 64
+    check_dbias(x, to_np(gpu["dbias"]), oracle(x)["dbias"])

@@ -137,3 +137,32 @@ def test_full_size_workloads_sampled(name):
     ref = oracle(x, seqs=seqs)
     rep = compare(x, gpu, ref, seqs=seqs, out_bf16=True, plain=True)
     say(f"  {rep}")
+
+
+# Every sequence with at most 64 queries: softmax dK/dV runs in half-width items (64 keys, 4-wave
+# workgroups). Keys span several items with ragged tails.
+SHORT_Q = [1, 37, 64, 5]
+SHORT_KV = [300, 64, 129, 1000]
+SHORT_SELF = [1, 37, 64, 50]
+
+
+@pytest.mark.parametrize("mask", ["none", "causal"])
+@pytest.mark.parametrize("bias", ["none", "scalar", "bucket"])
+def test_short_query_items(mask, bias):
+    lq, lkv = (SHORT_SELF, SHORT_SELF) if mask == "causal" else (SHORT_Q, SHORT_KV)
+    x = ji.make_inputs(lq, lkv, 2, 128, wid=45, mask=mask, act="softmax", bias_kind=bias, bias_sigma=0.5)
+    say(f"case short-query mask={mask} bias={bias}")
+    gpu = run_gpu(x)
+    assert gpu["plan"].info()["kv_bn"] == 64
+    compare(x, gpu, oracle(x))
+
+
+def test_short_query_items_split():
+    x = ji.make_inputs(SHORT_Q, SHORT_KV, 2, 128, wid=46, mask="none", act="softmax", bias_kind="bucket",
+                       bias_sigma=0.5)
+    say("case short-query split")
+    g1 = run_gpu(x, num_slots=16)
+    # a half-width dK/dV item covers one query tile and is never split; the forward and dQ lists are
+    assert g1["plan"].info()["kv_bn"] == 64 and len(g1["plan"].schedule(5)) == 0
+    assert len(g1["plan"].schedule(1)) > 0 and len(g1["plan"].schedule(3)) > 0
+    compare(x, g1, oracle(x))
