@@ -767,23 +767,24 @@ void bwd_dkdv_kernel2(BwdArgs a) {
   uint32_t T[2];
   tr_operand_bases(lane, T);
 
-  float pl = kNegInf, pd = 0.0f;  // statistics of query row tid of a coming tile (softmax)
+  // Statistics of query row tid of a coming tile (softmax), loaded raw one step ahead and converted
+  // only when written to LDS, after the step's wait, so that no wait for them lands in between.
+  float pl = 0.0f, pd = 0.0f;
   auto load_stats = [&](int qt) {
     if (SOFTMAX && tid < BM) {
       const int q = qt * BM + tid;
-      pl = kNegInf;  // -lse in log2 units; -inf makes P of rows past the end 0
-      pd = 0.0f;
       if (q < Lq) {
-        const float l = a.lse[(size_t)h * a.Tq + qs + q];
-        pl = l == kNegInf ? kNegInf : -(l - lse_shift) * kLog2e;
+        pl = a.lse[(size_t)h * a.Tq + qs + q];
         pd = a.delta[(size_t)h * a.Tq + qs + q];
       }
     }
   };
-  auto write_stats = [&](int stg) {
+  auto write_stats = [&](int qt, int stg) {
     if (SOFTMAX && tid < BM) {
-      sm.lse2[stg][tid] = pl;
-      sm.dlt[stg][tid] = pd;
+      const bool in = qt * BM + tid < Lq;
+      // -lse in log2 units; -inf makes P of rows past the end (and of empty rows) 0
+      sm.lse2[stg][tid] = (in && pl != kNegInf) ? -(pl - lse_shift) * kLog2e : kNegInf;
+      sm.dlt[stg][tid] = in ? pd : 0.0f;
     }
   };
   auto issue_tile = [&](int qt, int stg) {
@@ -955,7 +956,7 @@ void bwd_dkdv_kernel2(BwdArgs a) {
     }
     if (q0 + 1 < q1) issue_tile(q0 + 1, 1);
     wait_vm();
-    write_stats(0);
+    write_stats(q0, 0);
     if (q0 + 1 < q1) load_stats(q0 + 1);
     if (q0 < q1) fill(q0);
     __syncthreads();  // also publishes wave 0's bias table
@@ -965,7 +966,7 @@ void bwd_dkdv_kernel2(BwdArgs a) {
       phase1(qt, st_tag, st_tag, pacc);
       __builtin_amdgcn_sched_barrier(0);
       wait_vm();
-      if (qt + 1 < q1) write_stats((ST + 1) % 3);
+      if (qt + 1 < q1) write_stats(qt + 1, (ST + 1) % 3);
       __syncthreads();
       if (qt + 2 < q1) {
         issue_tile(qt + 2, (ST + 2) % 3);
@@ -993,7 +994,7 @@ void bwd_dkdv_kernel2(BwdArgs a) {
     if (BIAS == kBiasBucket) __syncthreads();
     auto step = [&](const int qt, auto st_tag) {
       constexpr int ST = decltype(st_tag)::value;
-      write_stats(ST);
+      write_stats(qt, ST);
       wait_vm();
       fill(qt);
       __syncthreads();

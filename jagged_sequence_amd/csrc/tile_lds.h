@@ -10,6 +10,12 @@
 // Loads use buffer_load ... lds: lane i of a wave writes 16 bytes at (wave-uniform LDS base) + 16 i,
 // so one instruction fills 4 rows (1 KB); rows past the jagged end are out of the buffer range and
 // arrive as zeros. No registers are used for staging.
+//
+// The loads are issued as inline assembly, outside the compiler's view. The compiler cannot tell one
+// LDS tile from another, so for a load into LDS that it knows of it waits for the load to land
+// before the wave's next LDS read of any tile, which would expose the whole latency of the next
+// tile's prefetch. Hidden from it, the loads are waited for only where the kernels say so: every
+// consumer of a tile sits behind wait_vm() in each wave followed by a workgroup barrier.
 #pragma once
 
 #include "device_common.h"
@@ -45,14 +51,21 @@ __device__ __forceinline__ TileLoader make_loader64(int wave, int lane, int rs) 
   return t;
 }
 
+// One buffer_load_dwordx4 ... lds of 16 bytes per lane: lane i's bytes at `voff` of the buffer land
+// at LDS byte address `lds` + 16 i. M0 carries the wave-uniform LDS address (set by the compiler just
+// before); the s_nop covers the wait state required between an SALU write of M0 and the load reading it.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t src, uint32_t voff, const unsigned char* lds) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)to_lds(lds);
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "{m0}"(m0v), "v"(voff), "s"(src) : "memory");
+}
+
 // Issue the loads of a 64-row tile whose first row is `row0` of the slice into LDS at `tile`.
 __device__ __forceinline__ void load_tile64(const TileLoader& t, __amdgpu_buffer_rsrc_t src, int row0, int rs,
                                             unsigned char* tile, int wave) {
   const uint32_t base = (uint32_t)(row0 * rs * 2);
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, to_lds(tile + (16 * wave + 4 * u) * kRowBytes), 16, base + t.voff[u],
-                                             0, 0, 0);
+    dma16(src, base + t.voff[u], tile + (16 * wave + 4 * u) * kRowBytes);
 }
 
 // Each of 8 waves fills rows [8 wave, 8 wave + 8) of a 64-row tile with 2 instructions.
@@ -74,8 +87,7 @@ __device__ __forceinline__ void load_tile64_w8(const TileLoader& t, __amdgpu_buf
   const uint32_t base = (uint32_t)(row0 * rs * 2);
 #pragma unroll
   for (int u = 0; u < 2; ++u)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, to_lds(tile + (8 * wave + 4 * u) * kRowBytes), 16, base + t.voff[u],
-                                             0, 0, 0);
+    dma16(src, base + t.voff[u], tile + (8 * wave + 4 * u) * kRowBytes);
 }
 
 // Wait for this wave's outstanding global loads (including loads into LDS).
