@@ -96,7 +96,10 @@ typedef struct {
 jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t* plan_out);
 
 /* Device bytes of workspace each pass needs (0 when nothing is split and no scratch is used).
- * Either pointer may be NULL. */
+ * At head dim 128 the backward workspace always holds the dK/dV kernel's work-queue counters
+ * (256 bytes): that kernel keeps as many workgroups as the GPU holds at once and hands them the
+ * work items through per-XCD queues; the backward pass zeroes the counters itself before the
+ * kernel runs. Either pointer may be NULL. */
 jfa_status jfa_workspace_bytes(jfa_plan_t plan, size_t* fwd_bytes, size_t* bwd_bytes);
 
 /* Forward pass. `bias` may be NULL only without bias; `lse` may be NULL only for GDPA (it is

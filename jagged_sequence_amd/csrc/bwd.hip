@@ -12,6 +12,8 @@
 //   dV_j += P dO_i,  dK_j += scale dS q_i,  dQ_i += scale dS k_j
 #include <type_traits>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "tile_lds.h"
 
@@ -23,25 +25,38 @@ namespace {
 // same elements of the forward output (bf16 or fp32), in fp32.
 template <int NKB>
 __device__ __forceinline__ float row_dot_out(const BwdArgs& a, size_t base, const bf16x8 (&df)[NKB]) {
+  // The dtype branch sits outside the loops and every load is issued before the first use, so the
+  // row costs one memory round trip rather than one per 16-byte piece.
   float acc = 0.0f;
+  if (a.out_f32) {
+    const float* op = reinterpret_cast<const float*>(a.out) + base;
+    float4 x[NKB][2];
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    float o[8];
-    if (a.out_f32) {
-      const float* op = reinterpret_cast<const float*>(a.out) + base + 16 * kb;
-      const float4 x0 = *reinterpret_cast<const float4*>(op), x1 = *reinterpret_cast<const float4*>(op + 4);
-      o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w; o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
-    } else {
-      const uint4 x = load16(reinterpret_cast<const uint16_t*>(a.out) + base + 16 * kb);
-      const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        o[2 * j] = __builtin_bit_cast(float, xw[j] << 16);
-        o[2 * j + 1] = __builtin_bit_cast(float, xw[j] & 0xffff0000u);
-      }
+    for (int kb = 0; kb < NKB; ++kb) {
+      x[kb][0] = *reinterpret_cast<const float4*>(op + 16 * kb);
+      x[kb][1] = *reinterpret_cast<const float4*>(op + 16 * kb + 4);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc += (float)df[kb][j] * o[j];
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float o[8] = {x[kb][0].x, x[kb][0].y, x[kb][0].z, x[kb][0].w,
+                          x[kb][1].x, x[kb][1].y, x[kb][1].z, x[kb][1].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += (float)df[kb][j] * o[j];
+    }
+  } else {
+    const uint16_t* op = reinterpret_cast<const uint16_t*>(a.out) + base;
+    uint4 x[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) x[kb] = load16(op + 16 * kb);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const uint32_t xw[4] = {x[kb].x, x[kb].y, x[kb].z, x[kb].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc += (float)df[kb][2 * j] * __builtin_bit_cast(float, xw[j] << 16);
+        acc += (float)df[kb][2 * j + 1] * __builtin_bit_cast(float, xw[j] & 0xffff0000u);
+      }
+    }
   }
   return acc;
 }
@@ -104,10 +119,9 @@ void bwd_dq_kernel(BwdArgs a) {
   __shared__ DqSmem<D> sm;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
-  const int32_t* it = a.dq_items + (size_t)blockIdx.x * kItemInts;
-  const int b = it[0], h = it[1], t = it[2], k0 = it[3], k1 = it[4], slot = it[5];
-  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
-  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const WorkRec w = load_item(a.dq_items, blockIdx.x);
+  const int h = w.h, t = w.tile, k0 = w.lo, k1 = w.hi, slot = w.slot;
+  const int qs = w.qs, Lq = w.Lq, ks = w.ks, Lkv = w.Lkv;
   const int rs = a.H * D;
   const int row0 = t * BM + wave * 32;
   const int qi = row0 + l32;
@@ -263,18 +277,32 @@ void bwd_dq_kernel2(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int32_t* it = a.dq_items + (size_t)blockIdx.x * kItemInts;
-  const int b = it[0], h = it[1], t = it[2], k0 = it[3], k1 = it[4], slot = it[5];
-  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
-  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  // The dK/dV kernel, which runs after this one, takes its items from a queue whose counters
+  // start at zero.
+  if (blockIdx.x == 0 && threadIdx.x < kQueues && a.kv_queue) a.kv_queue[threadIdx.x] = 0;
+  const WorkRec w = load_item(a.dq_items, blockIdx.x);
+  const int h = w.h, t = w.tile, k0 = w.lo, k1 = w.hi, slot = w.slot;
+  const int qs = w.qs, Lq = w.Lq, ks = w.ks, Lkv = w.Lkv;
   const int rs = a.H * D;
   const int row0 = t * BM + wave * 32;
   const int qi = row0 + l32;
 
   const float inv_scale = 1.0f / a.scale;
-  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
+  // The bias table is written to LDS after the other prologue loads are issued (its round trip
+  // overlaps theirs).
+  const float tabv = (BIAS == kBiasBucket && tid < kBuckets) ? a.bias[h * kBuckets + tid] : 0.0f;
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
   const float acc0 = (BIAS == kBiasScalar && !SOFTMAX) ? bias_c * inv_scale : 0.0f;
+
+  // The first key tile is requested before anything else, so that its latency overlaps the
+  // fragment loads and the Delta computation below.
+  const __amdgpu_buffer_rsrc_t kr = slice_rsrc(a.k + (size_t)ks * rs + h * D, Lkv, rs, D);
+  const __amdgpu_buffer_rsrc_t vr = slice_rsrc(a.v + (size_t)ks * rs + h * D, Lkv, rs, D);
+  const TileLoader ld = make_loader64(wave, lane, rs);
+  if (k0 < k1) {
+    load_tile64(ld, kr, k0 * BN, rs, sm.kv[0][0], wave);
+    load_tile64(ld, vr, k0 * BN, rs, sm.kv[0][1], wave);
+  }
 
   bf16x8 qf[NKB], df[NKB];
   {
@@ -307,19 +335,15 @@ void bwd_dq_kernel2(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) qacc[db] = f32x16{};
 
-  const __amdgpu_buffer_rsrc_t kr = slice_rsrc(a.k + (size_t)ks * rs + h * D, Lkv, rs, D);
-  const __amdgpu_buffer_rsrc_t vr = slice_rsrc(a.v + (size_t)ks * rs + h * D, Lkv, rs, D);
-  const TileLoader ld = make_loader64(wave, lane, rs);
   const uint32_t raddr = row_operand_base(kappa(l32), hh);
   uint32_t T[2];
   tr_operand_bases(lane, T);
 
-  if (k0 < k1) {
-    load_tile64(ld, kr, k0 * BN, rs, sm.kv[0][0], wave);
-    load_tile64(ld, vr, k0 * BN, rs, sm.kv[0][1], wave);
+  // Wave 0 writes the bias table; every wave reads it in the first tile's diagonal fill.
+  if (BIAS == kBiasBucket) {
+    if (tid < kBuckets) sm.tab[tid] = tabv;
+    __syncthreads();
   }
-  // Wave 0 wrote the bias table; every wave reads it in the first tile's diagonal fill.
-  if (BIAS == kBiasBucket) __syncthreads();
   // One kv tile; ST (compile-time) is the ring stage holding it.
   auto tile = [&](const int kt, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
@@ -455,10 +479,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ KvSmem<D> sm;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
-  const int32_t* it = a.kv_items + (size_t)blockIdx.x * kItemInts;
-  const int b = it[0], h = it[1], kt = it[2], q0 = it[3], q1 = it[4], slot = it[5];
-  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
-  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const WorkRec w = load_item(a.kv_items, blockIdx.x);
+  const int h = w.h, kt = w.tile, q0 = w.lo, q1 = w.hi, slot = w.slot;
+  const int qs = w.qs, Lq = w.Lq, ks = w.ks, Lkv = w.Lkv;
   const int rs = a.H * D;
   const int key_w = kt * BN + wave * 32;  // first key of this wave
   const int kj = key_w + l32;
@@ -714,34 +737,50 @@ __device__ __forceinline__ void unpack8(uint4 w, float (&x)[8]) {
 // general; NP = 2 (64 keys, 4 waves, two workgroups per CU, about 75 KB of LDS) when every sequence
 // has a single query tile, where an item is one latency-bound pass and two resident workgroups
 // overlap one's loads with the other's work.
-template <int ACT, int BIASX, bool CAUSAL, int NP>
-__global__ __attribute__((amdgpu_flat_work_group_size(NP * 128, NP * 128), amdgpu_waves_per_eu(2, 2)))
-void bwd_dkdv_kernel2(BwdArgs a) {
+// Softmax hands over P only, so a third ring stage and three hand-off buffers fit in LDS and one
+// barrier per query tile suffices; GDPA also hands over act'/Lkv and keeps two barriers per tile,
+// as does the short form (NP = 2), whose items have a single query tile.
+template <int ACT, int NP>
+struct DkdvShape {
+  static constexpr bool ONEBAR = ACT == kSoftmax && NP == 4;
+  using Smem = KvSmem2<ONEBAR, ACT != kSoftmax, NP>;
+};
+
+// One dK/dV item (the key tile and query-tile range at position `item` of the list) by the whole
+// workgroup. Its first LDS access follows a barrier that every wave has passed after the previous
+// item's last LDS access.
+// `claim_next()` runs when the item's tile loop ends and `take_next(token)` after its epilogue, so
+// that the work queue's round trip overlaps the epilogue's stores.
+template <int ACT, int BIASX, bool CAUSAL, int NP, class Claim, class Take>
+__device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4))) BwdArgs& a,
+                                           typename DkdvShape<ACT, NP>::Smem& sm, int item, const int wave,
+                                           Claim claim_next, Take take_next) {
   constexpr int D = 128, BM = kKvBM, BN = 32 * NP, NKB = D / 16, NDB = D / 32;
   constexpr int BIAS = BIASX & 3;
   constexpr bool DBIAS = (BIASX & kBiasGrad) != 0;
   constexpr bool SOFTMAX = ACT == kSoftmax;
-  // Softmax hands over P only, so a third ring stage and three hand-off buffers fit in LDS and one
-  // barrier per query tile suffices; GDPA also hands over act'/Lkv and keeps two barriers per tile,
-  // as does the short form (NP = 2), whose items have a single query tile.
-  constexpr bool ONEBAR = SOFTMAX && NP == 4;
-  using Smem = KvSmem2<ONEBAR, !SOFTMAX, NP>;
-  __shared__ Smem sm;
+  constexpr bool ONEBAR = DkdvShape<ACT, NP>::ONEBAR;
+  using Smem = typename DkdvShape<ACT, NP>::Smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Lane constants are derived anew for every item from the lane counter (no register holds the
+  // thread index across the persistent loop, and nothing derived from it is hoisted out of it).
+  // lane_now() recomputes the lane index (two VALU) where a use sits far from the others.
+  auto lane_now = [] { return lane_opaque((int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u))); };
+  const int lane = lane_now();
+  const int tid = wave * 64 + lane, hh = lane >> 5, l32 = lane & 31;
   const int pair = wave % NP;
   const bool isB = wave >= NP;
-  const int32_t* it = a.kv_items + (size_t)blockIdx.x * kItemInts;
-  const int b = it[0], h = it[1], kt = it[2], q0 = it[3], q1 = it[4], slot = it[5];
-  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
-  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const WorkRec w = load_item(a.kv_items, item);
+  const int h = w.h, kt = w.tile, q0 = w.lo, q1 = w.hi, slot = w.slot;
+  const int qs = w.qs, Lq = w.Lq, ks = w.ks, Lkv = w.Lkv;
   const int rs = a.H * D;
   const int key_w = kt * BN + pair * 32;  // first key of this pair
   const int kj = key_w + l32;
 
   const float inv_scale = 1.0f / a.scale;
-  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
+  // The bias table is written to LDS after the other prologue loads are issued (its round trip
+  // overlaps theirs).
+  const float tabv = (BIAS == kBiasBucket && tid < kBuckets) ? a.bias[h * kBuckets + tid] : 0.0f;
   DbiasLane dbl;  // B waves: running bias-gradient sum of this lane
   if (DBIAS && isB) sm.dbh[pair][lane] = 0ull;
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
@@ -767,40 +806,40 @@ void bwd_dkdv_kernel2(BwdArgs a) {
   uint32_t T[2];
   tr_operand_bases(lane, T);
 
-  // Statistics of query row tid of a coming tile (softmax), loaded raw one step ahead and converted
-  // only when written to LDS, after the step's wait, so that no wait for them lands in between.
-  float pl = 0.0f, pd = 0.0f;
-  auto load_stats = [&](int qt) {
-    if (SOFTMAX && tid < BM) {
-      const int q = qt * BM + tid;
-      if (q < Lq) {
-        pl = a.lse[(size_t)h * a.Tq + qs + q];
-        pd = a.delta[(size_t)h * a.Tq + qs + q];
-      }
-    }
-  };
-  auto write_stats = [&](int qt, int stg) {
-    if (SOFTMAX && tid < BM) {
-      const bool in = qt * BM + tid < Lq;
-      // -lse in log2 units; -inf makes P of rows past the end (and of empty rows) 0
-      sm.lse2[stg][tid] = (in && pl != kNegInf) ? -(pl - lse_shift) * kLog2e : kNegInf;
-      sm.dlt[stg][tid] = in ? pd : 0.0f;
+  // Statistics of a query tile (softmax): lse and Delta of its 64 rows come into the tile's stage
+  // with the tile itself (one 256-byte load each, by wave 0). After the wait that precedes the
+  // tile's publishing barrier, wave 0 turns lse into -lse in log2 units in place; rows past the end
+  // read zeros and get -inf, which makes their P 0.
+  const __amdgpu_buffer_rsrc_t lser =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.lse) + (size_t)h * a.Tq + qs, (short)0, Lq * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t dltr =
+      __builtin_amdgcn_make_buffer_rsrc(a.delta + (size_t)h * a.Tq + qs, (short)0, Lq * 4, 0x00020000);
+  auto fix_stats = [&](int qt, int stg) {
+    if (SOFTMAX && wave == 0) {
+      const int r = lane_now();
+      const float x = sm.lse2[stg][r];
+      sm.lse2[stg][r] = (qt * BM + r < Lq && x != kNegInf) ? -(x - lse_shift) * kLog2e : kNegInf;
     }
   };
   auto issue_tile = [&](int qt, int stg) {
+    if (SOFTMAX && wave == 0) {
+      const uint32_t so = (uint32_t)(qt * BM + lane_now()) * 4u;
+      dma4(lser, so, sm.lse2[stg]);
+      dma4(dltr, so, sm.dlt[stg]);
+    }
     // loader offsets recomputed per tile (two VALU each) rather than held in registers
     if constexpr (NP == 4) {
-      const TileLoader ld = make_loader64_w8(wave, lane_opaque(lane), rs);
+      const TileLoader ld = make_loader64_w8(wave, lane_now(), rs);
       load_tile64_w8(ld, qsr, qt * BM, rs, sm.qg[stg][0], wave);
       load_tile64_w8(ld, gsr, qt * BM, rs, sm.qg[stg][1], wave);
     } else {
-      const TileLoader ld = make_loader64(wave, lane_opaque(lane), rs);
+      const TileLoader ld = make_loader64(wave, lane_now(), rs);
       load_tile64(ld, qsr, qt * BM, rs, sm.qg[stg][0], wave);
       load_tile64(ld, gsr, qt * BM, rs, sm.qg[stg][1], wave);
     }
   };
   auto fill = [&](int qt) {
-    if (BIAS == kBiasBucket && !isB) fill_diag(sm.diag[pair], sm.tab, qt * BM - key_w - 31, inv_scale, lane);
+    if (BIAS == kBiasBucket && !isB) fill_diag(sm.diag[pair], sm.tab, qt * BM - key_w - 31, inv_scale, lane_now());
   };
 
   auto stage_ptr = [&](auto st_tag, int which) -> const unsigned char* {
@@ -860,7 +899,8 @@ void bwd_dkdv_kernel2(BwdArgs a) {
             if (MASK || !SOFTMAX) {
 #pragma unroll
               for (int j = 0; j < 8; ++j) {
-                const int qi = qrow0 + rbase + j;
+                // row index from a fresh lane index: this path runs on diagonal tiles only
+                const int qi = qrow0 + 32 * qb + 16 * c8 + 8 * (lane_now() >> 5) + j;
                 const bool masked = (MASK && (kj >= Lkv || (CAUSAL && kj > qi))) || (!SOFTMAX && qi >= Lq);
                 pv[j] = masked ? 0.0f : pv[j];
                 if (!SOFTMAX) gv[j] = masked ? 0.0f : gv[j];
@@ -950,28 +990,22 @@ void bwd_dkdv_kernel2(BwdArgs a) {
     // stage tile t-1 used; phase 2 of t. Every wave is past phase 2 of t-1 when the barrier of step
     // t releases, so the stage and buffers it overwrites are free, and A's phase 1 of t+1 may run
     // while B still finishes phase 2 of t.
-    if (q0 < q1) {
-      issue_tile(q0, 0);
-      load_stats(q0);
-    }
+    if (q0 < q1) issue_tile(q0, 0);
     if (q0 + 1 < q1) issue_tile(q0 + 1, 1);
     wait_vm();
-    write_stats(q0, 0);
-    if (q0 + 1 < q1) load_stats(q0 + 1);
-    if (q0 < q1) fill(q0);
-    __syncthreads();  // also publishes wave 0's bias table
+    if (q0 < q1) fix_stats(q0, 0);
+    if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = tabv;
+    __syncthreads();  // also publishes wave 0's bias table, which the first fill reads
+    if (q0 < q1) fill(q0);  // the A wave reads its own window: no barrier needed before phase 1
     auto step = [&](const int qt, auto st_tag) {
       constexpr int ST = decltype(st_tag)::value;
       f32x16 pacc[2];
       phase1(qt, st_tag, st_tag, pacc);
       __builtin_amdgcn_sched_barrier(0);
       wait_vm();
-      if (qt + 1 < q1) write_stats(qt + 1, (ST + 1) % 3);
+      if (qt + 1 < q1) fix_stats(qt + 1, (ST + 1) % 3);
       __syncthreads();
-      if (qt + 2 < q1) {
-        issue_tile(qt + 2, (ST + 2) % 3);
-        load_stats(qt + 2);
-      }
+      if (qt + 2 < q1) issue_tile(qt + 2, (ST + 2) % 3);
       phase2(qt, st_tag, st_tag, pacc);
       if (qt + 1 < q1) fill(qt + 1);
       // Keep the compiler from hoisting the next tile's loads into this phase (register pressure).
@@ -985,23 +1019,20 @@ void bwd_dkdv_kernel2(BwdArgs a) {
   } else {
     // Two barriers per tile: the first publishes the tile and retires the other stage, the second
     // publishes the hand-off buffer.
-    if (q0 < q1) {
-      issue_tile(q0, 0);
-      load_stats(q0);
-    }
-    // Wave 0 wrote the bias table (and the B waves cleared their gradient bins); A waves read the
+    if (q0 < q1) issue_tile(q0, 0);
+    // Wave 0 writes the bias table (and the B waves cleared their gradient bins); A waves read the
     // table in the first tile's diagonal fill.
-    if (BIAS == kBiasBucket) __syncthreads();
+    if (BIAS == kBiasBucket) {
+      if (tid < kBuckets) sm.tab[tid] = tabv;
+      __syncthreads();
+    }
     auto step = [&](const int qt, auto st_tag) {
       constexpr int ST = decltype(st_tag)::value;
-      write_stats(qt, ST);
       wait_vm();
+      fix_stats(qt, ST);
       fill(qt);
       __syncthreads();
-      if (qt + 1 < q1) {
-        issue_tile(qt + 1, ST ^ 1);
-        load_stats(qt + 1);
-      }
+      if (qt + 1 < q1) issue_tile(qt + 1, ST ^ 1);
       f32x16 pacc[2];
       phase1(qt, st_tag, I0{}, pacc);
       __syncthreads();
@@ -1012,6 +1043,7 @@ void bwd_dkdv_kernel2(BwdArgs a) {
       if (qt + 1 < q1) step(qt + 1, I1{});
     }
   }
+  const int token = claim_next();
 
   if (DBIAS && isB) {
     dbl.flush(sm.dbh[pair]);
@@ -1045,6 +1077,98 @@ void bwd_dkdv_kernel2(BwdArgs a) {
         *reinterpret_cast<float4*>(pp + 32 * db + 8 * g + 4 * hh) =
             make_float4(acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]);
   }
+  take_next(token);
+}
+
+// Work queue of the dK/dV kernel. The items, in dispatch order, are dealt into kQueues queues:
+// position p goes to queue p % kQueues, the XCD whose L2 the dispatch order keeps the item's sequence
+// in. A workgroup takes items from the queue of the XCD it runs on and, once that is exhausted, from
+// the others; the counters only grow, so every item is taken exactly once and every workgroup
+// reaches the end when all queues are exhausted. Used by lane 0 of wave 0 only.
+struct ItemQueue {
+  int* ctr;        // kQueues counters, zero when the kernel starts
+  int n;           // items in the list
+  int home;        // queue of this workgroup's XCD
+  unsigned empty;  // queues seen exhausted
+  __device__ int claim(int x) { return __hip_atomic_fetch_add(ctr + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+  // list position of index i of queue x, or -1 (and x noted as exhausted)
+  __device__ int position(int x, int i) {
+    const int p = x + kQueues * i;
+    if (i >= 0 && p < n) return p;  // (a negative index can only come from uncleared counters)
+    empty |= 1u << x;
+    return -1;
+  }
+  __device__ int next() {
+#pragma nounroll
+    for (int k = 0; k < kQueues; ++k) {
+      const int x = (home + k) % kQueues;
+      if (empty & (1u << x)) continue;
+      const int p = position(x, claim(x));
+      if (p >= 0) return p;
+    }
+    return -1;
+  }
+};
+
+__device__ __forceinline__ int xcd_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(20, 0, 4)" : "=s"(v));  // XCC_ID
+  return (int)v;
+}
+
+// Persistent dK/dV kernel (NP = 4): as many workgroups as the GPU holds at once, each running items
+// from the work queue until none is left. Next to one workgroup per item this removes the gap between a
+// workgroup's end and the next one's start, and the queue balances what the items really cost.
+template <int ACT, int BIASX, bool CAUSAL, int NP>
+__global__ __attribute__((amdgpu_flat_work_group_size(NP * 128, NP * 128), amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_kernel2(BwdArgs a) {
+  __shared__ typename DkdvShape<ACT, NP>::Smem sm;
+  __shared__ int next_item;
+  __shared__ unsigned empty_queues;
+  // The arguments are read through a pointer made opaque at every item, so that they are loaded
+  // again (scalar loads) for each item instead of being held in registers across the whole loop;
+  // likewise the queue state lives in LDS and the XCD is read again where needed.
+  typedef const __attribute__((address_space(4))) BwdArgs* ArgPtr;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (NP == 2) {
+    // The short form (single-tile items, two workgroups per CU) runs one item per workgroup: the
+    // second resident workgroup already covers one's start and end, and the queue would only add
+    // its round trips.
+    ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    dkdv_item2<ACT, BIASX, CAUSAL, NP>(*ap, sm, blockIdx.x, wave, [] { return 0; }, [](int) {});
+    return;
+  }
+  if (threadIdx.x == 0) {
+    ItemQueue q{a.kv_queue, a.kv_n, xcd_id() % kQueues, 0u};
+    next_item = q.next();
+    empty_queues = q.empty;
+  }
+  __syncthreads();
+  for (;;) {
+    const int item = __builtin_amdgcn_readfirstlane(next_item);
+    if (item < 0) break;
+    // BwdArgs is the kernel's only argument: it starts the kernel-argument segment
+    ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ap));
+    auto leader = [&]() { return wave == 0 && __builtin_amdgcn_mbcnt_lo(~0u, 0u) == 0; };
+    // claim the home queue's next index while the epilogue's stores drain; resolve it afterwards
+    auto claim = [&]() -> int {
+      const int home = xcd_id() % kQueues;
+      if (!leader() || (empty_queues & (1u << home))) return -1;
+      return __hip_atomic_fetch_add(ap->kv_queue + home, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto take = [&](int claimed) {
+      if (!leader()) return;
+      const int home = xcd_id() % kQueues;
+      ItemQueue q{ap->kv_queue, ap->kv_n, home, empty_queues};
+      int p = claimed >= 0 ? q.position(home, claimed) : -1;
+      if (p < 0) p = q.next();
+      next_item = p;
+      empty_queues = q.empty;
+    };
+    dkdv_item2<ACT, BIASX, CAUSAL, NP>(*ap, sm, item, wave, claim, take);
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------- fixed-order partial sums
@@ -1052,9 +1176,9 @@ void bwd_dkdv_kernel2(BwdArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_dq_kernel(BwdArgs a) {
   constexpr int BM = kDqBM, HALF = D / 2;
-  const int32_t* g = a.dq_groups + (size_t)blockIdx.x * kGroupInts;
-  const int b = g[0], h = g[1], t = g[2], slot0 = g[3], R = g[4];
-  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
+  const WorkRec g = load_group(a.dq_groups, blockIdx.x);
+  const int h = g.h, t = g.tile, slot0 = g.lo, R = g.hi;
+  const int qs = g.qs, Lq = g.Lq;
   const int row = threadIdx.x >> 1, part = threadIdx.x & 1;
   const int qi = t * BM + row;
   if (qi >= Lq) return;
@@ -1080,9 +1204,9 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_dkdv_kernel(BwdArgs a) {
   constexpr int HALF = D / 2;
   const int BN = a.kv_bn;
-  const int32_t* g = a.kv_groups + (size_t)blockIdx.x * kGroupInts;
-  const int b = g[0], h = g[1], kt = g[2], slot0 = g[3], R = g[4];
-  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const WorkRec g = load_group(a.kv_groups, blockIdx.x);
+  const int h = g.h, kt = g.tile, slot0 = g.lo, R = g.hi;
+  const int ks = g.ks, Lkv = g.Lkv;
   const int row = threadIdx.x >> 1, part = threadIdx.x & 1;
   const int kj = kt * BN + row;
   if (row >= BN || kj >= Lkv) return;
@@ -1115,7 +1239,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_dkdv_kernel(BwdArgs a) {
 // come out as 0.
 __global__ __launch_bounds__(256) void bwd_dbias_clear_kernel(BwdArgs a, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) a.dbias_acc[i] = 0ull;
+  if (i < n && a.dbias_acc) a.dbias_acc[i] = 0ull;
+  if (i < kQueues && a.kv_queue) a.kv_queue[i] = 0;  // for backward passes with no dQ items
 }
 
 __global__ __launch_bounds__(256) void bwd_dbias_finish_kernel(BwdArgs a, int n) {
@@ -1193,11 +1318,12 @@ hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n, hipStream_t s)
   return JFA_DISPATCH_MODES(dq_select, m, n, s, a);
 }
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
+hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n, int resident, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int block = m.D == 128 ? (m.kv_short ? kDkdvThreads128 / 2 : kDkdvThreads128) : kThreads;
+  const int grid = (m.D == 128 && !m.kv_short) ? std::max(1, std::min(n, resident)) : n;
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(n), dim3(block), 0, s, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(block), 0, s, a);
     return hipGetLastError();
   };
   if (m.D == 64) {
@@ -1208,8 +1334,9 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n, hipStream_t 
 }
 
 hipError_t launch_bwd_dbias_clear(const BwdArgs& a, const Modes& m, hipStream_t s) {
-  const int n = a.H * (m.bias == kBiasBucket ? kDbiasBins : 1);
-  hipLaunchKernelGGL(bwd_dbias_clear_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a, n);
+  const int n = a.dbias_acc ? a.H * (m.bias == kBiasBucket ? kDbiasBins : 1) : 0;
+  const int threads = std::max(n, kQueues);
+  hipLaunchKernelGGL(bwd_dbias_clear_kernel, dim3((threads + 255) / 256), dim3(256), 0, s, a, n);
   return hipGetLastError();
 }
 

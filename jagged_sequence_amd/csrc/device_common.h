@@ -131,6 +131,23 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret
 // points at row 0 of the slice, rows are `rs` elements apart and `rows` of them are valid. Loads
 // past the last valid row fall outside the resource's byte range and return zeros, so tails of
 // jagged sequences need no branch and never read a neighbouring sequence.
+// A work record (item or split group), read through the constant address space: the list is never
+// written while a kernel runs, and the promise lets the compiler fetch the record with scalar loads.
+struct WorkRec {
+  int b, h, tile, lo, hi, slot, qs, Lq, ks, Lkv;
+};
+__device__ __forceinline__ WorkRec load_item(const int32_t* list, int i) {
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  const cptr r = (cptr)(list + (size_t)i * kItemInts);
+  return {r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7], r[8], r[9]};
+}
+__device__ __forceinline__ WorkRec load_group(const int32_t* list, int i) {
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  const cptr r = (cptr)(list + (size_t)i * kGroupInts);
+  // group layout: b, h, tile, slot0, R, qs, Lq, ks, Lkv (slot0 and R returned in lo and hi)
+  return {r[0], r[1], r[2], r[3], r[4], -1, r[5], r[6], r[7], r[8]};
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const uint16_t* base, int rows, int rs, int D) {
   const uint32_t bytes = rows > 0 ? (uint32_t)((rows - 1) * rs + D) * 2u : 0u;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);

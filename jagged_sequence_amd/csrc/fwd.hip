@@ -83,10 +83,9 @@ void fwd_kernel(FwdArgs a) {
   __shared__ FwdSmem<D> sm;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
-  const int32_t* it = a.items + (size_t)blockIdx.x * kItemInts;
-  const int b = it[0], h = it[1], t = it[2], k0 = it[3], k1 = it[4], slot = it[5];
-  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
-  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const WorkRec w = load_item(a.items, blockIdx.x);
+  const int h = w.h, t = w.tile, k0 = w.lo, k1 = w.hi, slot = w.slot;
+  const int qs = w.qs, Lq = w.Lq, ks = w.ks, Lkv = w.Lkv;
   const int rs = a.H * D;
   const int row0 = t * BM + wave * 32;
   const int qi = row0 + l32;
@@ -260,16 +259,17 @@ void fwd_kernel2(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int32_t* it = a.items + (size_t)blockIdx.x * kItemInts;
-  const int b = it[0], h = it[1], t = it[2], k0 = it[3], k1 = it[4], slot = it[5];
-  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
-  const int ks = a.kv_off[b], Lkv = a.kv_off[b + 1] - ks;
+  const WorkRec w = load_item(a.items, blockIdx.x);
+  const int h = w.h, t = w.tile, k0 = w.lo, k1 = w.hi, slot = w.slot;
+  const int qs = w.qs, Lq = w.Lq, ks = w.ks, Lkv = w.Lkv;
   const int rs = a.H * D;
   const int row0 = t * BM + wave * 32;
   const int qi = row0 + l32;
   const float inv_scale = 1.0f / a.scale;
 
-  if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
+  // The bias table is loaded here and written to LDS after the other prologue loads are issued, so
+  // that its round trip overlaps theirs.
+  const float tabv = (BIAS == kBiasBucket && tid < kBuckets) ? a.bias[h * kBuckets + tid] : 0.0f;
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
   const float acc0 = (BIAS == kBiasScalar && !SOFTMAX) ? bias_c * inv_scale : 0.0f;
 
@@ -297,8 +297,11 @@ void fwd_kernel2(FwdArgs a) {
     load_tile64(ld, kr, k0 * BN, rs, sm.kv[0][0], wave);
     load_tile64(ld, vr, k0 * BN, rs, sm.kv[0][1], wave);
   }
-  // Wave 0 wrote the bias table; every wave reads it in the first tile's diagonal fill.
-  if (BIAS == kBiasBucket) __syncthreads();
+  // Wave 0 writes the bias table; every wave reads it in the first tile's diagonal fill.
+  if (BIAS == kBiasBucket) {
+    if (tid < kBuckets) sm.tab[tid] = tabv;
+    __syncthreads();
+  }
   // One kv tile. ST is the ring stage holding tile kt (compile-time, so every LDS address is a
   // loop-invariant register plus an immediate offset).
   auto tile = [&](const int kt, auto st_tag) {
@@ -446,10 +449,9 @@ template <int D, int ACT, int BIAS>
 __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
   constexpr int BM = kFwdBM;
   constexpr bool SOFTMAX = ACT == kSoftmax;
-  const int32_t* g = a.groups + (size_t)blockIdx.x * kGroupInts;
-  const int b = g[0], h = g[1], t = g[2], slot0 = g[3], R = g[4];
-  const int qs = a.q_off[b], Lq = a.q_off[b + 1] - qs;
-  const int Lkv = a.kv_off[b + 1] - a.kv_off[b];
+  const WorkRec g = load_group(a.groups, blockIdx.x);
+  const int h = g.h, t = g.tile, slot0 = g.lo, R = g.hi;
+  const int qs = g.qs, Lq = g.Lq, Lkv = g.Lkv;
   const int row = threadIdx.x >> 1, part = threadIdx.x & 1;
   const int qi = t * BM + row;
   if (qi >= Lq) return;

@@ -196,6 +196,8 @@ struct jfa_plan_s {
   // workspace layout
   size_t ws_fwd = 0, off_part_lse = 0;
   size_t ws_bwd = 0, off_delta = 0, off_part_dq = 0, off_part_dk = 0, off_part_dv = 0, off_dbias = 0;
+  size_t off_queue = 0;  // dK/dV work-queue counters (D = 128)
+  int kv_resident = 1;   // dK/dV workgroups the GPU holds at once (grid of the persistent kernel)
   // timing
   bool timing = false;
   struct Rec {
@@ -339,6 +341,16 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
       slots[kKv] = cus * occupancy_dkdv(P->modes);
     }
   }
+  if (!host_only) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) {
+      delete P;
+      return hip_fail(e, "device query");
+    }
+    P->kv_resident = std::max(1, cus * occupancy_dkdv(P->modes));
+  }
   const bool causal = P->modes.causal != 0;
   query_tile_list(lq, lkv, P->H, causal, kFwdBM, kFwdBN, slots[kFwd], split, P->lists[kFwd]);
   query_tile_list(lq, lkv, P->H, causal, kDqBM, kDqBN, slots[kDq], split, P->lists[kDq]);
@@ -361,22 +373,39 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   o += align256((size_t)P->lists[kKv].nslots * P->kv_bn * D * 4);
   P->off_dbias = o;  // fixed-point bias-gradient totals, used when the caller asks for dbias
   if (P->modes.bias != kBiasNone) o += align256((size_t)P->H * (P->modes.bias == kBiasBucket ? kBuckets : 1) * 8);
+  P->off_queue = o;
+  if (P->D == 128) o += align256(kQueues * 4);
   P->ws_bwd = o;
   if (P->lists[kFwd].nslots == 0) P->ws_fwd = 0;
 
   if (!host_only) {
-    // device records: 8 int32 per item / group
+    // device records (kItemInts / kGroupInts int32 each): the list fields followed by the
+    // sequence's offsets and lengths, so that a workgroup needs no second, dependent load
     size_t total = 0;
-    for (auto& L : P->lists) total += (L.n_items() + L.n_groups()) * 8;
-    std::vector<int32_t> host(std::max<size_t>(total, 8), 0);
+    for (auto& L : P->lists) total += L.n_items() * kItemInts + L.n_groups() * kGroupInts;
+    std::vector<int32_t> host(std::max<size_t>(total, kItemInts), 0);
+    auto put_seq = [&](int32_t* r, int b) {
+      r[0] = P->q_off[b];
+      r[1] = P->q_off[b + 1] - P->q_off[b];
+      r[2] = P->kv_off[b];
+      r[3] = P->kv_off[b + 1] - P->kv_off[b];
+    };
     size_t pos = 0;
     size_t offs[3][2];
     for (int l = 0; l < 3; ++l) {
       List& L = P->lists[l];
       offs[l][0] = pos;
-      for (size_t i = 0; i < L.n_items(); ++i, pos += 8) std::copy_n(&L.items[(size_t)L.order[i] * 6], 6, &host[pos]);
+      for (size_t i = 0; i < L.n_items(); ++i, pos += kItemInts) {
+        const int32_t* it = &L.items[(size_t)L.order[i] * 6];
+        std::copy_n(it, 6, &host[pos]);
+        put_seq(&host[pos + 6], it[0]);
+      }
       offs[l][1] = pos;
-      for (size_t g = 0; g < L.n_groups(); ++g, pos += 8) std::copy_n(&L.groups[g * 5], 5, &host[pos]);
+      for (size_t g = 0; g < L.n_groups(); ++g, pos += kGroupInts) {
+        const int32_t* gr = &L.groups[g * 5];
+        std::copy_n(gr, 5, &host[pos]);
+        put_seq(&host[pos + 5], gr[0]);
+      }
     }
     hipError_t e = hipGetDevice(&P->device);
     if (e == hipSuccess) e = hipMalloc(&P->dev, host.size() * 4);
@@ -504,9 +533,12 @@ jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* 
   a.out_f32 = P->out_f32;
   a.grad_f32 = P->grad_f32;
   a.kv_bn = P->kv_bn;
+  a.kv_queue = (ws && P->D == 128) ? reinterpret_cast<int*>(ws + P->off_queue) : nullptr;
+  a.kv_n = (int)P->lists[kKv].n_items();
   Modes m = P->modes;
   m.dbias = dbias ? 1 : 0;
-  if (dbias) {
+  // The queue counters are zeroed by the dQ kernel, or here when there is no dQ item.
+  if (dbias || (a.kv_queue && P->lists[kDq].n_items() == 0 && a.kv_n > 0)) {
     st = timed(P, 6, s, [&] { return launch_bwd_dbias_clear(a, m, s); }, "bias-gradient clear launch");
     if (st != JFA_OK) return st;
   }
@@ -517,7 +549,7 @@ jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* 
     st = timed(P, 5, s, [&] { return launch_bwd_reduce_dq(a, m, (int)P->lists[kDq].n_groups(), s); }, "dQ reduce launch");
     if (st != JFA_OK) return st;
   }
-  st = timed(P, 3, s, [&] { return launch_bwd_dkdv(a, m, (int)P->lists[kKv].n_items(), s); }, "dK/dV launch");
+  st = timed(P, 3, s, [&] { return launch_bwd_dkdv(a, m, a.kv_n, P->kv_resident, s); }, "dK/dV launch");
   if (st != JFA_OK) return st;
   if (P->lists[kKv].n_groups() > 0) {
     st = timed(P, 5, s, [&] { return launch_bwd_reduce_dkdv(a, m, (int)P->lists[kKv].n_groups(), s); }, "dK/dV reduce launch");

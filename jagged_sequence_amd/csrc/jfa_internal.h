@@ -18,9 +18,15 @@ constexpr int kKvBM = 64, kKvBN = 128;
 // softmax with D = 128 then uses half-width items (64 keys, 4-wave workgroups, two per CU).
 constexpr int kKvBNShort = 64;
 constexpr int kThreads = 256;
-constexpr int kItemInts = 8;   // device record: b, h, tile, lo, hi, slot, 0, 0
-constexpr int kGroupInts = 8;  // device record: b, h, tile, slot0, R, 0, 0, 0
+// Device work records carry the sequence's offsets and lengths, so a workgroup starts with a single
+// load of its record (no dependent load of the offset arrays):
+//   item:  b, h, tile, lo, hi, slot, qs, Lq, ks, Lkv, 0 x 6
+//   group: b, h, tile, slot0, R, qs, Lq, ks, Lkv, 0 x 7
+constexpr int kItemInts = 16;
+constexpr int kGroupInts = 16;
 constexpr int kBuckets = 64;
+// Work queues of the persistent dK/dV kernel (D = 128): one per XCD.
+constexpr int kQueues = 8;
 
 enum Act { kSoftmax = 0, kSilu = 1, kGeluTanh = 2 };
 enum BiasKind { kBiasNone = 0, kBiasScalar = 1, kBiasBucket = 2 };
@@ -74,6 +80,8 @@ struct BwdArgs {
   int out_f32;
   int grad_f32;
   int kv_bn;  // keys per dK/dV item (kKvBN or kKvBNShort)
+  int* kv_queue;  // kQueues counters of the dK/dV work queue (D = 128); the dQ kernel zeroes them
+  int kv_n;       // dK/dV items
 };
 
 struct Modes {
@@ -92,10 +100,13 @@ constexpr int kBiasGrad = 4;
 // Launchers (defined next to their kernels). Each returns the hipGetLastError() of its launch.
 hipError_t launch_forward(const FwdArgs& a, const Modes& m, int n_items, hipStream_t s);
 hipError_t launch_forward_combine(const FwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
-hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n_items, hipStream_t s);
+// n_items dK/dV items; at D = 128 the kernel is persistent and runs min(n_items, resident)
+// workgroups (resident = how many the GPU holds at once).
+hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n_items, int resident, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n_items, hipStream_t s);
 hipError_t launch_bwd_reduce_dq(const BwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
 hipError_t launch_bwd_reduce_dkdv(const BwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
+// Clears the bias-gradient totals (when a.dbias_acc is set) and the dK/dV queue counters.
 hipError_t launch_bwd_dbias_clear(const BwdArgs& a, const Modes& m, hipStream_t s);
 hipError_t launch_bwd_dbias_finish(const BwdArgs& a, const Modes& m, hipStream_t s);
 

@@ -59,6 +59,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t src, uint32_t voff,
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "{m0}"(m0v), "v"(voff), "s"(src) : "memory");
 }
 
+// The same for 4 bytes per lane: lane i's bytes at `voff` land at `lds` + 4 i (one 256-byte row).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t src, uint32_t voff, const void* lds) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)to_lds(lds);
+  asm volatile("s_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" : : "{m0}"(m0v), "v"(voff), "s"(src) : "memory");
+}
+
 // Issue the loads of a 64-row tile whose first row is `row0` of the slice into LDS at `tile`.
 __device__ __forceinline__ void load_tile64(const TileLoader& t, __amdgpu_buffer_rsrc_t src, int row0, int rs,
                                             unsigned char* tile, int wave) {

@@ -129,9 +129,12 @@ def test_workspace_sizes():
     al = lambda x: (x + 255) // 256 * 256
     assert nf > 0 and nq > 0 and nk > 0
     assert fwd == al(nf * 128 * 128 * 4) + al(nf * 128 * 4)
-    assert bwd == al(2 * 830 * 4) + al(nq * 128 * 128 * 4) + 2 * al(nk * 128 * 128 * 4)
+    # Delta, dQ partials, dK and dV partials, and (D = 128) the dK/dV work-queue counters
+    assert bwd == al(2 * 830 * 4) + al(nq * 128 * 128 * 4) + 2 * al(nk * 128 * 128 * 4) + al(8 * 4)
     plan2 = _host_plan(lq, lq, 2, mask="causal", num_slots=4, no_split=True, act="silu")
-    assert plan2.workspace_bytes() == (0, 0)
+    assert plan2.workspace_bytes() == (0, al(8 * 4))
+    plan3 = _host_plan(lq, lq, 2, 64, mask="causal", num_slots=4, no_split=True, act="silu")
+    assert plan3.workspace_bytes() == (0, 0)
 
 
 def _status_of(fn):
