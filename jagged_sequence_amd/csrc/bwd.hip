@@ -749,8 +749,10 @@ struct DkdvShape {
 // One dK/dV item (the key tile and query-tile range at position `item` of the list) by the whole
 // workgroup. Its first LDS access follows a barrier that every wave has passed after the previous
 // item's last LDS access.
-// `claim_next()` runs when the item's tile loop ends and `take_next(token)` after its epilogue, so
-// that the work queue's round trip overlaps the epilogue's stores.
+// Work-queue hooks: `claim_next()` runs when the item's tile loop ends and `take_next(token)` after
+// its epilogue, so that the queue's round trip overlaps the epilogue's stores. (Claiming earlier
+// would hide it better but would hold the claimed item back for a whole item, which lengthens the
+// tail of the run.)
 template <int ACT, int BIASX, bool CAUSAL, int NP, class Claim, class Take>
 __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4))) BwdArgs& a,
                                            typename DkdvShape<ACT, NP>::Smem& sm, int item, const int wave,
@@ -778,9 +780,15 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
   const int kj = key_w + l32;
 
   const float inv_scale = 1.0f / a.scale;
-  // The bias table is written to LDS after the other prologue loads are issued (its round trip
-  // overlaps theirs).
-  const float tabv = (BIAS == kBiasBucket && tid < kBuckets) ? a.bias[h * kBuckets + tid] : 0.0f;
+  // The bias table (256 bytes) comes into LDS by the same kind of load as the tiles (wave 0), so
+  // no register waits for it; the prologue's wait and barrier publish it.
+  auto load_table = [&] {
+    if (BIAS == kBiasBucket && wave == 0) {
+      const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.bias) + h * kBuckets,
+                                                                          (short)0, kBuckets * 4, 0x00020000);
+      dma4(tr, (uint32_t)lane_now() * 4u, sm.tab);
+    }
+  };
   DbiasLane dbl;  // B waves: running bias-gradient sum of this lane
   if (DBIAS && isB) sm.dbh[pair][lane] = 0ull;
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
@@ -992,9 +1000,9 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
     // while B still finishes phase 2 of t.
     if (q0 < q1) issue_tile(q0, 0);
     if (q0 + 1 < q1) issue_tile(q0 + 1, 1);
+    load_table();
     wait_vm();
     if (q0 < q1) fix_stats(q0, 0);
-    if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = tabv;
     __syncthreads();  // also publishes wave 0's bias table, which the first fill reads
     if (q0 < q1) fill(q0);  // the A wave reads its own window: no barrier needed before phase 1
     auto step = [&](const int qt, auto st_tag) {
@@ -1020,10 +1028,11 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
     // Two barriers per tile: the first publishes the tile and retires the other stage, the second
     // publishes the hand-off buffer.
     if (q0 < q1) issue_tile(q0, 0);
-    // Wave 0 writes the bias table (and the B waves cleared their gradient bins); A waves read the
+    load_table();
+    // Wave 0 loads the bias table (and the B waves cleared their gradient bins); A waves read the
     // table in the first tile's diagonal fill.
     if (BIAS == kBiasBucket) {
-      if (tid < kBuckets) sm.tab[tid] = tabv;
+      wait_vm();
       __syncthreads();
     }
     auto step = [&](const int qt, auto st_tag) {
@@ -1043,38 +1052,41 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
       if (qt + 1 < q1) step(qt + 1, I1{});
     }
   }
-  const int token = claim_next();
 
+  const int token = claim_next();
+  // The epilogue derives its lane values afresh: kept from the prologue they would be spilled
+  // across the item, and their reloads here would make the next item's first loads wait.
+  const int le = lane_now(), hhe = le >> 5, kje = key_w + (le & 31);
   if (DBIAS && isB) {
     dbl.flush(sm.dbh[pair]);
     wave_lds_fence();
     constexpr int NB = BIAS == kBiasBucket ? kDbiasBins : 1;
-    if (lane < NB) {
-      const unsigned long long x = sm.dbh[pair][lane];
-      if (x) atomicAdd(a.dbias_acc + (size_t)h * NB + lane, x);
+    if (le < NB) {
+      const unsigned long long x = sm.dbh[pair][le];
+      if (x) atomicAdd(a.dbias_acc + (size_t)h * NB + le, x);
     }
   }
 
   // Accumulator register r of d-block db: dimension 32 db + 8 (r/4) + 4 hh + r%4, key kj.
   const float sc = isB ? a.scale : 1.0f;
   if (slot < 0) {
-    if (kj < Lkv) {
+    if (kje < Lkv) {
       void* dst = isB ? a.dk : a.dv;
-      const size_t base = ((size_t)(ks + kj) * a.H + h) * D;
+      const size_t base = ((size_t)(ks + kje) * a.H + h) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          store4(dst, base + 32 * db + 8 * g + 4 * hh, acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc,
+          store4(dst, base + 32 * db + 8 * g + 4 * hhe, acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc,
                  acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc, a.grad_f32);
     }
   } else {
-    float* pp = (isB ? a.part_dk : a.part_dv) + ((size_t)slot * BN + pair * 32 + l32) * D;
+    float* pp = (isB ? a.part_dk : a.part_dv) + ((size_t)slot * BN + pair * 32 + (le & 31)) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(pp + 32 * db + 8 * g + 4 * hh) =
+        *reinterpret_cast<float4*>(pp + 32 * db + 8 * g + 4 * hhe) =
             make_float4(acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]);
   }
   take_next(token);
@@ -1151,11 +1163,14 @@ void bwd_dkdv_kernel2(BwdArgs a) {
     ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(ap));
     auto leader = [&]() { return wave == 0 && __builtin_amdgcn_mbcnt_lo(~0u, 0u) == 0; };
-    // claim the home queue's next index while the epilogue's stores drain; resolve it afterwards
+    // The home queue's next index is claimed when the item's tile loop ends and resolved after its
+    // epilogue (or, with the home queue exhausted, an item is taken from another queue).
     auto claim = [&]() -> int {
       const int home = xcd_id() % kQueues;
       if (!leader() || (empty_queues & (1u << home))) return -1;
-      return __hip_atomic_fetch_add(ap->kv_queue + home, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // (the opaque zero keeps the compiler from rewriting the uniform-address atomic into a
+      // wave-wide one whose result it would wait for on the spot)
+      return __hip_atomic_fetch_add(ap->kv_queue + home + lane_opaque(0), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     auto take = [&](int claimed) {
       if (!leader()) return;
