@@ -9,7 +9,18 @@ chunking changes no arithmetic beyond the order of independent rows.
 For one sequence b and head h (i < Lq_b, j < Lkv_b):
 
   s_ij   = scale * <Q_i, K_j> + beta_h(i, j)        beta: 0 | c_h | T[h, bucket(i - j)]
-  vis_ij = (mask == none) or (j <= i)
+  vis_ij = base_ij and window_ij and block_ij
+    base:   (mask == none) or (j <= i)
+    window: W == 0, or i - j < W (and, without the causal mask, also j - i < W)
+    block:  B == 0, or floor(i / B) == floor(j / B)
+
+The window and block limits follow the pages' long-sequence masks: sliding-window attention
+limits each token to neighbouring events and its kernel skips the tiles outside the window
+(aihot.vn GEM page, "BlockAttention"), and BlockAttention cuts a long sequence into independent
+fixed blocks (vibekk.com GEM page, section on moving from padding to jagged kernels;
+kerneldigest.dev page, "Arquitectura del Sistema"). The pages fix neither the window's side nor the block's interior;
+here a window under the causal mask looks back only, and a block keeps the base mask inside it.
+GDPA keeps its 1 / Lkv_b normalisation under both.
 
 softmax (FlashAttention's result on jagged tensors; aihot.vn GEM page, "Jagged Sequence Flash
 Attention"; kerneldigest.dev page, "Fundamentos Teóricos"):
@@ -80,7 +91,7 @@ def gelu_tanh_grad(x):
 _ACTS = {"silu": (silu, silu_grad), "gelu_tanh": (gelu_tanh, gelu_tanh_grad)}
 
 
-def _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias):
+def _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias, window=0, block=0):
     q_off = np.asarray(q_off, dtype=np.int64)
     kv_off = np.asarray(kv_off, dtype=np.int64)
     if q_off.ndim != 1 or q_off.shape != kv_off.shape or len(q_off) < 2:
@@ -91,6 +102,8 @@ def _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias):
         raise ValueError("tensor rows do not match offsets")
     if mask not in ("none", "causal") or act not in ("softmax", "silu", "gelu_tanh"):
         raise ValueError("bad mode")
+    if int(window) != window or window < 0 or int(block) != block or block < 0:
+        raise ValueError("window and block must be integers >= 0")
     H = q.shape[1]
     if bias_kind == "scalar":
         assert bias is not None and np.shape(bias) == (H,)
@@ -101,7 +114,19 @@ def _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias):
     return q_off, kv_off
 
 
-def _scores(Qc, K, i0, scale, mask, bias_kind, bias_h):
+def visible(i, j, mask, window=0, block=0):
+    """Visibility of query position i and key position j (numpy broadcasting)."""
+    vis = (j <= i) if mask == "causal" else np.ones(np.broadcast(i, j).shape, dtype=bool)
+    if window:
+        vis = vis & (i - j < window)
+        if mask != "causal":
+            vis = vis & (j - i < window)
+    if block:
+        vis = vis & (i // block == j // block)
+    return vis
+
+
+def _scores(Qc, K, i0, scale, mask, bias_kind, bias_h, window=0, block=0):
     """Scores and visibility of query rows i0.. of one (sequence, head) against all its keys."""
     rows, lkv = Qc.shape[0], K.shape[0]
     S = scale * (Qc @ K.T)
@@ -111,10 +136,7 @@ def _scores(Qc, K, i0, scale, mask, bias_kind, bias_h):
         S = S + bias_h
     elif bias_kind == "bucket":
         S = S + bias_h[bucket(i - j)]
-    if mask == "causal":
-        vis = j <= i
-    else:
-        vis = np.ones((rows, lkv), dtype=bool)
+    vis = visible(i, j, mask, window, block) & np.ones((rows, lkv), dtype=bool)
     return S, vis, i - j
 
 
@@ -141,7 +163,7 @@ def _select(n, subset):
     return range(n) if subset is None else subset
 
 
-def forward(q, k, v, q_off, kv_off, *, mask="none", act="softmax", bias_kind="none", bias=None,
+def forward(q, k, v, q_off, kv_off, *, mask="none", act="softmax", bias_kind="none", bias=None, window=0, block=0,
             scale: Optional[float] = None, seqs: Optional[Sequence[int]] = None,
             heads: Optional[Sequence[int]] = None):
     """Attention output ``[Tq, H, D]`` and, for softmax, ``lse [H, Tq]`` (natural log).
@@ -149,7 +171,7 @@ def forward(q, k, v, q_off, kv_off, *, mask="none", act="softmax", bias_kind="no
     ``q``, ``k``, ``v`` are float64 (use :func:`bf16_bits_to_f64` for bf16 operands). ``seqs`` /
     ``heads`` restrict the work to a subset; entries outside it are left NaN.
     """
-    q_off, kv_off = _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias)
+    q_off, kv_off = _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias, window, block)
     Tq, H, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -162,7 +184,7 @@ def forward(q, k, v, q_off, kv_off, *, mask="none", act="softmax", bias_kind="no
             K, V = k[ks:ke, h], v[ks:ke, h]
             bias_h = None if bias is None else np.asarray(bias, dtype=np.float64)[h]
             for i0, i1 in _chunks(lq, lkv):
-                S, vis, _ = _scores(q[qs + i0:qs + i1, h], K, i0, scale, mask, bias_kind, bias_h)
+                S, vis, _ = _scores(q[qs + i0:qs + i1, h], K, i0, scale, mask, bias_kind, bias_h, window, block)
                 if act == "softmax":
                     P, lse_c = _softmax_rows(S, vis)
                     out[qs + i0:qs + i1, h] = P @ V
@@ -174,7 +196,7 @@ def forward(q, k, v, q_off, kv_off, *, mask="none", act="softmax", bias_kind="no
     return out, lse
 
 
-def backward(q, k, v, q_off, kv_off, dout, *, mask="none", act="softmax", bias_kind="none", bias=None,
+def backward(q, k, v, q_off, kv_off, dout, *, mask="none", act="softmax", bias_kind="none", bias=None, window=0, block=0,
              scale: Optional[float] = None, seqs: Optional[Sequence[int]] = None,
              heads: Optional[Sequence[int]] = None):
     """Gradients ``(dq, dk, dv, dbias)`` of ``<forward(...).out, dout>``.
@@ -182,7 +204,7 @@ def backward(q, k, v, q_off, kv_off, dout, *, mask="none", act="softmax", bias_k
     ``dbias`` has the bias shape (``[H]`` or ``[H, 64]``) or is None without a bias; when
     ``seqs`` / ``heads`` select a subset, ``dbias`` sums over that subset only.
     """
-    q_off, kv_off = _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias)
+    q_off, kv_off = _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias, window, block)
     Tq, H, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -201,7 +223,7 @@ def backward(q, k, v, q_off, kv_off, dout, *, mask="none", act="softmax", bias_k
             for i0, i1 in _chunks(lq, lkv):
                 Qc = q[qs + i0:qs + i1, h]
                 dOc = dout[qs + i0:qs + i1, h]
-                S, vis, rel = _scores(Qc, K, i0, scale, mask, bias_kind, bias_h)
+                S, vis, rel = _scores(Qc, K, i0, scale, mask, bias_kind, bias_h, window, block)
                 if act == "softmax":
                     P, _ = _softmax_rows(S, vis)
                     dP = dOc @ V.T
@@ -226,7 +248,7 @@ def backward(q, k, v, q_off, kv_off, dout, *, mask="none", act="softmax", bias_k
     return dq, dk, dv, dbias
 
 
-def gdpa_magnitude(q, k, v, q_off, kv_off, *, mask="none", act="silu", bias_kind="none", bias=None,
+def gdpa_magnitude(q, k, v, q_off, kv_off, *, mask="none", act="silu", bias_kind="none", bias=None, window=0, block=0,
                    scale: Optional[float] = None, seqs=None, heads=None):
     """(1 / Lkv_b) sum_vis |act(s_ij)| |V_jd|: the scale of each GDPA output element.
 
@@ -235,7 +257,7 @@ def gdpa_magnitude(q, k, v, q_off, kv_off, *, mask="none", act="silu", bias_kind
     """
     if act == "softmax":
         raise ValueError("GDPA only")
-    q_off, kv_off = _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias)
+    q_off, kv_off = _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias, window, block)
     Tq, H, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -248,7 +270,7 @@ def gdpa_magnitude(q, k, v, q_off, kv_off, *, mask="none", act="silu", bias_kind
             K, V = k[ks:ke, h], np.abs(v[ks:ke, h])
             bias_h = None if bias is None else np.asarray(bias, dtype=np.float64)[h]
             for i0, i1 in _chunks(lq, lkv):
-                S, vis, _ = _scores(q[qs + i0:qs + i1, h], K, i0, scale, mask, bias_kind, bias_h)
+                S, vis, _ = _scores(q[qs + i0:qs + i1, h], K, i0, scale, mask, bias_kind, bias_h, window, block)
                 Aa = np.where(vis, np.abs(f(S)), 0.0)
                 out[qs + i0:qs + i1, h] = (Aa @ V) / lkv if lkv > 0 else 0.0
     return out

@@ -18,6 +18,15 @@ key-tile lists (dK/dV), tile BNk keys x BMq queries:
   for b, h, kt in lexicographic order with kt < ceil(Lkv_b / BNk):
       n_q = ceil(Lq_b / BMq);  first = floor(kt BNk / BMq) under the causal mask, else 0
       cost = max(0, n_q - first);  item covers query tiles [first, first + cost)
+with a window W or block size B (the visibility of oracle.attention), the ranges shrink to the
+tiles that hold a visible pair: the keys seen by rows r0..r1 = t BM .. min((t+1) BM, Lq_b) - 1
+form the interval [max(0, r0 - W + 1, B floor(r0 / B)), min(Lkv_b - 1, r1 (causal),
+r1 + W - 1 (no mask), B floor(r1 / B) + B - 1)] (each bound only when its mode is on), and the
+rows that see keys c0..c1 = kt BNk .. min((kt+1) BNk, Lkv_b) - 1 form
+[max(c0 (causal), c0 - W + 1 (no mask), B floor(c0 / B)), min(Lq_b - 1, c1 + W - 1,
+B floor(c1 / B) + B - 1)]; the item covers the tiles from the one holding the lower bound through
+the one holding the upper bound (none when the interval is empty: key tiles [0, 0), query tiles
+[lo, lo)). Without a window or block the rules above apply unchanged.
 splitting (both lists), given the number of concurrent workgroups ``slots``:
   target = max(1, ceil(sum(cost) / slots)); an item with cost > target becomes
   R = ceil(cost / target) pieces, piece r covering [lo + floor(r cost / R), lo + floor((r+1) cost / R));
@@ -53,28 +62,73 @@ def _finish(raw, slots: int, split: bool):
     return items, groups, next_slot
 
 
-def query_tile_items(lq, lkv, H: int, causal: bool, BM: int, BN: int, slots: int, split: bool = True):
+def _key_range(t, Lq, Lkv, causal, BM, BN, window, block):
+    """Key tiles [lo, hi) holding a visible pair for query tile t under a window or block."""
+    r0, r1 = t * BM, min((t + 1) * BM, Lq) - 1
+    lo_key, hi_key = 0, Lkv - 1
+    if window:
+        lo_key = max(lo_key, r0 - window + 1)
+        if not causal:
+            hi_key = min(hi_key, r1 + window - 1)
+    if causal:
+        hi_key = min(hi_key, r1)
+    if block:
+        lo_key = max(lo_key, (r0 // block) * block)
+        hi_key = min(hi_key, (r1 // block) * block + block - 1)
+    if hi_key < lo_key:
+        return 0, 0
+    return lo_key // BN, hi_key // BN + 1
+
+
+def _query_range(kt, Lq, Lkv, causal, BMq, BNk, window, block):
+    """Query tiles [lo, hi) holding a visible pair for key tile kt under a window or block."""
+    c0, c1 = kt * BNk, min((kt + 1) * BNk, Lkv) - 1
+    lo_row, hi_row = 0, Lq - 1
+    if causal:
+        lo_row = c0
+    if window:
+        hi_row = min(hi_row, c1 + window - 1)
+        if not causal:
+            lo_row = max(lo_row, c0 - window + 1)
+    if block:
+        lo_row = max(lo_row, (c0 // block) * block)
+        hi_row = min(hi_row, (c1 // block) * block + block - 1)
+    lo = lo_row // BMq
+    if hi_row < lo_row:
+        return lo, lo
+    return lo, hi_row // BMq + 1
+
+
+def query_tile_items(lq, lkv, H: int, causal: bool, BM: int, BN: int, slots: int, split: bool = True,
+                     window: int = 0, block: int = 0):
     """(items, groups, n_partial_slots) for a kernel that owns query tiles and loops over keys."""
     raw = []
     for b in range(len(lq)):
         n_kv = _ceil_div(int(lkv[b]), BN)
         for h in range(H):
             for t in range(_ceil_div(int(lq[b]), BM)):
-                cost = min(_ceil_div((t + 1) * BM, BN), n_kv) if causal else n_kv
-                raw.append((b, h, t, 0, cost))
+                if window or block:
+                    lo, hi = _key_range(t, int(lq[b]), int(lkv[b]), causal, BM, BN, window, block)
+                else:
+                    lo, hi = 0, (min(_ceil_div((t + 1) * BM, BN), n_kv) if causal else n_kv)
+                raw.append((b, h, t, lo, hi))
     return _finish(raw, slots, split)
 
 
-def key_tile_items(lq, lkv, H: int, causal: bool, BMq: int, BNk: int, slots: int, split: bool = True):
+def key_tile_items(lq, lkv, H: int, causal: bool, BMq: int, BNk: int, slots: int, split: bool = True,
+                   window: int = 0, block: int = 0):
     """(items, groups, n_partial_slots) for a kernel that owns key tiles and loops over queries."""
     raw = []
     for b in range(len(lq)):
         n_q = _ceil_div(int(lq[b]), BMq)
         for h in range(H):
             for kt in range(_ceil_div(int(lkv[b]), BNk)):
-                first = (kt * BNk) // BMq if causal else 0
-                cost = max(0, n_q - first)
-                raw.append((b, h, kt, first, first + cost))
+                if window or block:
+                    lo, hi = _query_range(kt, int(lq[b]), int(lkv[b]), causal, BMq, BNk, window, block)
+                else:
+                    lo = (kt * BNk) // BMq if causal else 0
+                    hi = lo + max(0, n_q - lo)
+                raw.append((b, h, kt, lo, hi))
     return _finish(raw, slots, split)
 
 

@@ -50,7 +50,7 @@ def unpad(x: torch.Tensor, off: np.ndarray) -> np.ndarray:
     return np.concatenate(parts, axis=0) if parts else np.zeros((0,) + tuple(x.shape[1::2]))
 
 
-def dense_bias_and_mask(q_off, kv_off, H, Lq, Lk, mask, bias_kind, bias):
+def dense_bias_and_mask(q_off, kv_off, H, Lq, Lk, mask, bias_kind, bias, window=0, block=0):
     """Additive bias [B, H, Lq, Lk] and boolean visibility [B, 1, Lq, Lk] for the padded layout."""
     B = len(q_off) - 1
     i = np.arange(Lq)[:, None]
@@ -62,6 +62,10 @@ def dense_bias_and_mask(q_off, kv_off, H, Lq, Lk, mask, bias_kind, bias):
         v = (i < lq) & (j < lk)
         if mask == "causal":
             v &= j <= i
+        if window:  # neighbours within the window: earlier ones only under the causal mask
+            v &= (i - j < window) & ((mask == "causal") | (j - i < window))
+        if block:  # same block of positions
+            v &= (i // block) == (j // block)
         vis[b, 0] = v
         for h in range(H):
             if bias_kind == "scalar":
@@ -71,7 +75,7 @@ def dense_bias_and_mask(q_off, kv_off, H, Lq, Lk, mask, bias_kind, bias):
     return torch.from_numpy(add), torch.from_numpy(vis)
 
 
-def dense_softmax(q, k, v, q_off, kv_off, mask, bias_kind, bias, scale, want_grad=False, dout=None):
+def dense_softmax(q, k, v, q_off, kv_off, mask, bias_kind, bias, scale, want_grad=False, dout=None, window=0, block=0):
     """Softmax attention through torch's CPU attention kernels on a padded batch.
 
     Returns (out [Tq,H,D], lse [H,Tq]) and, with ``want_grad``, autograd gradients (dq, dk, dv,
@@ -84,7 +88,7 @@ def dense_softmax(q, k, v, q_off, kv_off, mask, bias_kind, bias, scale, want_gra
     Q = padded(q, q_off, Lq).requires_grad_(want_grad)
     K = padded(k, kv_off, Lk).requires_grad_(want_grad)
     V = padded(v, kv_off, Lk).requires_grad_(want_grad)
-    add, vis = dense_bias_and_mask(q_off, kv_off, H, Lq, Lk, mask, bias_kind, bias)
+    add, vis = dense_bias_and_mask(q_off, kv_off, H, Lq, Lk, mask, bias_kind, bias, window, block)
     bias_param = None
     if want_grad and bias_kind != "none":
         bias_param = torch.tensor(np.asarray(bias, dtype=np.float64), requires_grad=True)
@@ -116,7 +120,7 @@ def dense_softmax(q, k, v, q_off, kv_off, mask, bias_kind, bias, scale, want_gra
     return res
 
 
-def dense_gdpa(q, k, v, q_off, kv_off, mask, act, bias_kind, bias, scale, want_grad=False, dout=None):
+def dense_gdpa(q, k, v, q_off, kv_off, mask, act, bias_kind, bias, scale, want_grad=False, dout=None, window=0, block=0):
     """GDPA on a padded batch with torch's own activation routines (F.silu, F.gelu tanh)."""
     H = q.shape[1]
     Lq = int(np.max(np.diff(q_off)))
@@ -124,7 +128,7 @@ def dense_gdpa(q, k, v, q_off, kv_off, mask, act, bias_kind, bias, scale, want_g
     Q = padded(q, q_off, Lq).requires_grad_(want_grad)
     K = padded(k, kv_off, Lk).requires_grad_(want_grad)
     V = padded(v, kv_off, Lk).requires_grad_(want_grad)
-    add, vis = dense_bias_and_mask(q_off, kv_off, H, Lq, Lk, mask, bias_kind, bias)
+    add, vis = dense_bias_and_mask(q_off, kv_off, H, Lq, Lk, mask, bias_kind, bias, window, block)
     bias_param = None
     if want_grad and bias_kind != "none":
         bias_param = torch.tensor(np.asarray(bias, dtype=np.float64), requires_grad=True)

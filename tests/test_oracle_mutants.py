@@ -64,7 +64,7 @@ def _pins_pass(mod):
 
 
 MUTATIONS = [
-    ("causal mask off by one", "vis = j <= i", "vis = j < i"),
+    ("causal mask off by one", "vis = (j <= i) if mask", "vis = (j < i) if mask"),
     ("scale dropped", "S = scale * (Qc @ K.T)", "S = (Qc @ K.T)"),
     ("scale applied after the bias", "S = S + bias_h[bucket(i - j)]", "S = S + scale * bias_h[bucket(i - j)]"),
     ("bucket index shifted", "S = S + bias_h[bucket(i - j)]", "S = S + bias_h[bucket(i - j + 1)]"),
@@ -95,3 +95,54 @@ def test_real_oracle_passes():
 @pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_planted_mistake_is_caught(name, old, new):
     assert not _pins_pass(_mutant(old, new)), name
+
+
+def _band_pins_pass(mod):
+    """True when the mutated oracle passes library pins with window and block limits."""
+    D = 8
+    scale = 1 / math.sqrt(D)
+    lens = [13, 2, 21]
+    for mask, act, window, block in [("causal", "softmax", 4, 0), ("none", "softmax", 3, 0), ("causal", "softmax", 0, 5),
+                                     ("none", "silu", 0, 6), ("causal", "gelu_tanh", 3, 8)]:
+        x = ji.make_inputs(lens, lens, 2, D, wid=22, mask=mask, act=act, bias_kind="bucket", bias_sigma=0.5)
+        f = A.bf16_bits_to_f64
+        q, k, v, do = f(x.q), f(x.k), f(x.v), f(x.do)
+        bias = x.bias.astype(np.float64)
+        kw = dict(mask=mask, act=act, bias_kind="bucket", bias=bias, window=window, block=block)
+        try:
+            out, _ = mod.forward(q, k, v, x.q_off, x.kv_off, **kw)
+            grads = mod.backward(q, k, v, x.q_off, x.kv_off, do, **kw)
+        except Exception:
+            return False
+        if act == "softmax":
+            r_out, _ = dense_softmax(q, k, v, x.q_off, x.kv_off, mask, "bucket", bias, scale, window=window, block=block)
+            _, _, *rg = dense_softmax(q, k, v, x.q_off, x.kv_off, mask, "bucket", bias, scale, True, do,
+                                      window=window, block=block)
+        else:
+            (r_out,) = dense_gdpa(q, k, v, x.q_off, x.kv_off, mask, act, "bucket", bias, scale, window=window,
+                                  block=block)
+            _, *rg = dense_gdpa(q, k, v, x.q_off, x.kv_off, mask, act, "bucket", bias, scale, True, do,
+                                window=window, block=block)
+        if not np.allclose(out, r_out, rtol=0, atol=1e-10):
+            return False
+        for g, r in zip(grads, rg):
+            if not np.allclose(g, r, rtol=0, atol=1e-10):
+                return False
+    return True
+
+
+BAND_MUTATIONS = [
+    ("window off by one", "vis = vis & (i - j < window)", "vis = vis & (i - j <= window)"),
+    ("window without its forward side", "vis = vis & (j - i < window)", "vis = vis & (j - i < 10 ** 9)"),
+    ("block boundary shifted", "vis = vis & (i // block == j // block)", "vis = vis & ((i + 1) // block == j // block)"),
+    ("block ignored", "vis = vis & (i // block == j // block)", "vis = vis"),
+]
+
+
+def test_real_oracle_passes_band_pins():
+    assert _band_pins_pass(A)
+
+
+@pytest.mark.parametrize("name,old,new", BAND_MUTATIONS, ids=[m[0] for m in BAND_MUTATIONS])
+def test_planted_band_mistake_is_caught(name, old, new):
+    assert not _band_pins_pass(_mutant(old, new)), name

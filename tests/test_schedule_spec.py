@@ -8,7 +8,7 @@ import jfa_inputs as ji
 from oracle import schedule as S
 
 
-def _visible_blocks(lq, lkv, H, causal, BQ, BK):
+def _visible_blocks(lq, lkv, H, causal, BQ, BK, window=0, block=0):
     """Brute force: every (b, h, query tile, key tile) holding at least one visible (i, j) pair."""
     out = set()
     for b in range(len(lq)):
@@ -18,6 +18,10 @@ def _visible_blocks(lq, lkv, H, causal, BQ, BK):
         i = np.arange(Lq)[:, None]
         j = np.arange(Lk)[None, :]
         vis = (j <= i) if causal else np.ones((Lq, Lk), dtype=bool)
+        if window:  # |i - j| < window, looking back only under the causal mask
+            vis = vis & (np.abs(i - j) < window)
+        if block:
+            vis = vis & ((i // block) == (j // block))
         ii, jj = np.nonzero(vis)
         blocks = set(zip((ii // BQ).tolist(), (jj // BK).tolist()))
         for h in range(H):
@@ -114,3 +118,45 @@ def test_splitting_matches_the_worked_counts():
     items2, groups2, nslots = S.query_tile_items(lq, lkv, w.H, False, 64, 64, 512)
     assert sum(hi - lo for (*_a, lo, hi, _s) in items2) == sum(hi - lo for (*_a, lo, hi, _s) in items)
     assert len(groups2) > 0 and nslots == sum(R for (*_g, R) in groups2)
+
+
+BAND_CASES = [
+    ([5, 130, 0, 257, 64, 700], [5, 130, 0, 257, 64, 700], True, 100, 0),
+    ([5, 130, 0, 257, 64, 700], [5, 130, 0, 257, 64, 700], True, 1, 0),
+    ([5, 130, 0, 257, 64, 700], [5, 130, 0, 257, 64, 700], True, 0, 200),
+    ([5, 130, 0, 257, 64, 700], [5, 130, 0, 257, 64, 700], True, 300, 256),
+    ([1, 40, 3, 64, 300], [300, 17, 0, 1000, 90], False, 70, 0),
+    ([1, 40, 3, 64, 300], [300, 17, 0, 1000, 90], False, 0, 50),
+    ([700, 129, 1], [700, 129, 1], False, 64, 128),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BAND_CASES)))
+def test_band_ranges_cover_each_visible_block_once(case):
+    """Window / block masks: query- and key-tile ranges are exactly the tiles with a visible pair."""
+    lq, lkv, causal, window, block = BAND_CASES[case]
+    items, groups, nslots = S.query_tile_items(lq, lkv, 2, causal, 128, 64, 7, window=window, block=block)
+    cover = _expand(items)
+    assert len(cover) == len(set(cover))
+    assert set(cover) == _visible_blocks(lq, lkv, 2, causal, 128, 64, window, block)
+    tiles = {(b, h, t) for (b, h, t, *_rest) in items}
+    assert tiles == {(b, h, t) for b in range(len(lq)) for h in range(2) for t in range(-(-lq[b] // 128))}
+    _check_order_and_groups(items, groups, nslots, 7)
+    items, groups, nslots = S.key_tile_items(lq, lkv, 2, causal, 64, 128, 5, window=window, block=block)
+    cover = _expand(items)
+    assert len(cover) == len(set(cover))
+    assert {(b, h, x, t) for (b, h, t, x) in cover} == _visible_blocks(lq, lkv, 2, causal, 64, 128, window, block)
+    tiles = {(b, h, t) for (b, h, t, *_rest) in items}
+    assert tiles == {(b, h, t) for b in range(len(lq)) for h in range(2) for t in range(-(-lkv[b] // 128))}
+    _check_order_and_groups(items, groups, nslots, 5)
+
+
+def test_band_without_limits_is_the_plain_schedule():
+    lq = [5, 130, 0, 257, 64, 700]
+    for causal in (True, False):
+        a = S.query_tile_items(lq, lq, 2, causal, 128, 64, 9)
+        b = S.query_tile_items(lq, lq, 2, causal, 128, 64, 9, window=10**6, block=10**6)
+        assert a == b
+        a = S.key_tile_items(lq, lq, 2, causal, 64, 128, 9)
+        b = S.key_tile_items(lq, lq, 2, causal, 64, 128, 9, window=10**6, block=10**6)
+        assert a == b
