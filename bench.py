@@ -104,6 +104,7 @@ def cpu_baseline(x, workload, seconds_target=15.0):
     budget = seconds_target * est_rate
     seqs, acc = [], 0.0
     for b in range(len(lq)):
+        # the oracle's cost follows the dense score rows it forms, whatever the window or block
         n = int(min(lq[b], lkv[b]))
         pairs = n * (n + 1) // 2 if causal else int(lq[b]) * int(lkv[b])
         w = (4 + (10 if workload_backward(workload) else 0)) * x.D * pairs * x.H
@@ -117,13 +118,13 @@ def cpu_baseline(x, workload, seconds_target=15.0):
     sk = np.concatenate([[0], np.cumsum(lkv[seqs])])
     q, k, v = f(x.q[rows]), f(x.k[krows]), f(x.v[krows])
     bias = None if x.bias is None else x.bias.astype(np.float64)
-    kw = dict(mask=x.mask, act=x.act, bias_kind=x.bias_kind, bias=bias)
+    kw = dict(mask=x.mask, act=x.act, bias_kind=x.bias_kind, bias=bias, window=x.window, block=x.block)
     t0 = time.perf_counter()
     A.forward(q, k, v, sq, sk, **kw)
     if workload_backward(workload):
         A.backward(q, k, v, sq, sk, f(x.do[rows]), **kw)
     dt = time.perf_counter() - t0
-    fw, bw = useful_flops(sq, sk, x.H, x.D, causal, workload_backward(workload))
+    fw, bw = useful_flops(sq, sk, x.H, x.D, causal, workload_backward(workload), x.window, x.block)
     return {"value": (fw + bw) / dt / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
             "sample": f"{len(seqs)} of {len(lq)} sequences (the first ones), all {x.H} heads, "
                       f"fwd{'+bwd' if workload_backward(workload) else ''}, {dt:.1f} s, numpy float64"}
@@ -183,7 +184,8 @@ def main() -> int:
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
-    plan = J.Plan(x.q_off, x.kv_off, w.H, w.D, mask=w.mask, act=w.act, bias=w.bias, out_dtype=args.out_dtype,
+    plan = J.Plan(x.q_off, x.kv_off, w.H, w.D, mask=w.mask, act=w.act, bias=w.bias, window=w.window, block=w.block,
+                  out_dtype=args.out_dtype,
                   grad_dtype=args.out_dtype)
     plan_ms = (time.perf_counter() - t0) * 1e3
     fwd_ws, bwd_ws = plan.workspace_bytes()
@@ -222,10 +224,10 @@ def main() -> int:
             kernels[name] = {"avg_ms": ms / n, "launches_per_step": n / args.steps, "total_ms": ms}
     plan.timing_enable(False)
 
-    fw, bw = useful_flops(x.q_off, x.kv_off, w.H, w.D, causal, w.backward)
+    fw, bw = useful_flops(x.q_off, x.kv_off, w.H, w.D, causal, w.backward, w.window, w.block)
     ms_per_step = elapsed / args.steps * 1e3
     value = (fw + bw) / (elapsed / args.steps) / 1e12
-    pairs = visible_pairs(x.q_off, x.kv_off, causal) * w.H
+    pairs = visible_pairs(x.q_off, x.kv_off, causal, w.window, w.block) * w.H
 
     # roofline of the dominant kernel (largest share of the timed region): its algorithmic FLOPs and
     # bytes per launch decide the bound (MFMA above the ridge point, HBM below it)
@@ -260,7 +262,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded jagged lengths and N(0,1) bf16 values; no dataset)",
         "config": {"workload": args.workload, "B": w.B, "H": w.H, "D": w.D, "mask": w.mask, "act": w.act,
-                   "bias": w.bias, "tokens_q": int(x.q_off[-1]), "tokens_kv": int(x.kv_off[-1]),
+                   "bias": w.bias, "window": w.window, "block": w.block, "tokens_q": int(x.q_off[-1]), "tokens_kv": int(x.kv_off[-1]),
                    "visible_pairs_x_heads": int(pairs), "out_dtype": args.out_dtype, "bias_gradient": bool(want_db),
                    "description": w.description},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),

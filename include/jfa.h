@@ -14,7 +14,10 @@
  * For sequence b with Lq = q_off[b+1]-q_off[b] queries and Lkv = kv_off[b+1]-kv_off[b] keys, head h,
  * query i < Lq, key j < Lkv:
  *   s_ij = scale * <q_i, k_j> + beta_h(i, j),  beta = 0 | c_h | T[h][bucket(|i - j|)]
- *   visible(i, j) = (mask == NONE) || (j <= i)
+ *   visible(i, j) = base && window && block
+ *     base   = (mask == NONE) || (j <= i)
+ *     window = (W == 0) || (i - j < W && (mask == CAUSAL || j - i < W))
+ *     block  = (Bk == 0) || (i / Bk == j / Bk)
  *   softmax: out_i = sum_j P_ij v_j with P the softmax of s_i over visible j; lse_i = ln sum exp
  *            (a row with no visible key gives out_i = 0 and lse_i = -inf)
  *   GDPA:    out_i = (1 / Lkv) * sum_{visible j} act(s_ij) v_j,  act = SiLU | GELU (tanh form)
@@ -57,7 +60,8 @@ typedef enum {
   JFA_OK = 0,
   JFA_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
   JFA_ERR_BAD_OFFSETS = 2,  /* offsets[0] != 0, decreasing offsets, or a total beyond int32 */
-  JFA_ERR_BAD_SHAPE = 3,    /* B < 1, H < 1, D not 64/128, causal with some Lq != Lkv */
+  JFA_ERR_BAD_SHAPE = 3,    /* B < 1, H < 1, D not 64/128, causal with some Lq != Lkv,
+                               window or block < 0 */
   JFA_ERR_UNSUPPORTED = 4,  /* enum out of range, or a feature this build does not provide */
   JFA_ERR_MISALIGNED = 5,   /* a tensor pointer is not 16-byte aligned */
   JFA_ERR_WORKSPACE = 6,    /* workspace smaller than jfa_workspace_bytes reports */
@@ -89,6 +93,16 @@ typedef struct {
   int32_t num_slots;              /* concurrent workgroups the split rule balances for; 0: from the device
                                      (CUs x resident workgroups), or 512 for a host-only plan */
   uint32_t flags;                 /* JFA_PLAN_* */
+  /* Optional long-sequence limits on visibility, 0 = off (aihot.vn GEM page, "BlockAttention":
+   * sliding-window attention restricted to neighbouring events, whose kernel skips the tiles
+   * outside the window; vibekk.com GEM page, section on moving from padding to jagged kernels,
+   * and kerneldigest.dev page, "Arquitectura del Sistema": block attention over fixed blocks).
+   * window W: a query sees keys fewer than W positions before it (and, without the causal mask,
+   * fewer than W after it). block Bk: a query sees only keys of its own block of Bk positions,
+   * with the base mask kept inside the block. The work lists hold only the tiles that contain a
+   * visible pair. GDPA still divides by the sequence's full key count. */
+  int32_t window;                 /* W >= 0 */
+  int32_t block;                  /* Bk >= 0 */
 } jfa_problem;
 
 /* Validate the problem, build the longest-first work lists (jagged tile scheduler) and, unless

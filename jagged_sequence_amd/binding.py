@@ -46,7 +46,7 @@ class Problem(ctypes.Structure):
                 ("q_offsets_host", ctypes.POINTER(ctypes.c_int32)), ("kv_offsets_host", ctypes.POINTER(ctypes.c_int32)),
                 ("mask", ctypes.c_int32), ("act", ctypes.c_int32), ("bias", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("out_dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32), ("num_slots", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("window", ctypes.c_int32), ("block", ctypes.c_int32)]
 
 
 def _load():
@@ -105,12 +105,13 @@ class Plan:
     def __init__(self, q_offsets, kv_offsets, num_heads: int, head_dim: int, *, mask: str = "none",
                  act: str = "softmax", bias: str = "none", scale: float = 0.0, out_dtype: str = "bf16",
                  grad_dtype: str = "bf16", num_slots: int = 0, host_only: bool = False, no_split: bool = False,
-                 stream=None):
+                 window: int = 0, block: int = 0, stream=None):
         self._q_off = _i32(q_offsets)
         self._kv_off = _i32(kv_offsets)
         self.B = len(self._q_off) - 1
         self.H, self.D = int(num_heads), int(head_dim)
         self.mask, self.act, self.bias_kind = mask, act, bias
+        self.window, self.block = int(window), int(block)
         self.out_dtype, self.grad_dtype = out_dtype, grad_dtype
         self.Tq = int(self._q_off[-1]) if self.B >= 0 and len(self._q_off) else 0
         self.Tkv = int(self._kv_off[-1]) if len(self._kv_off) else 0
@@ -128,6 +129,8 @@ class Plan:
         p.grad_dtype = DTYPES[grad_dtype]
         p.num_slots = int(num_slots)
         p.flags = (PLAN_HOST_ONLY if host_only else 0) | (PLAN_NO_SPLIT if no_split else 0)
+        p.window = self.window
+        p.block = self.block
         handle = ctypes.c_void_p()
         s = None if host_only else _stream_handle(stream)
         _check(LIB.jfa_plan(ctypes.byref(p), s, ctypes.byref(handle)))

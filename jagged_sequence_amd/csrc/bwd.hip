@@ -110,12 +110,13 @@ struct alignas(16) DqSmem {
   float diag[4][kDiagLen];
 };
 
-template <int D, int ACT, int BIAS, bool CAUSAL>
+template <int D, int ACT, int BIAS, int MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a) {
   constexpr int BM = kDqBM, BN = kDqBN, NKB = D / 16, NDB = D / 32;
   constexpr int RS = DqSmem<D>::RS, TS = DqSmem<D>::TS;
   constexpr bool SOFTMAX = ACT == kSoftmax;
+  constexpr bool CAUSAL = MASK == kMaskCausal, BAND = MASK == kMaskBand;
   __shared__ DqSmem<D> sm;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
@@ -125,6 +126,17 @@ void bwd_dq_kernel(BwdArgs a) {
   const int rs = a.H * D;
   const int row0 = t * BM + wave * 32;
   const int qi = row0 + l32;
+  // Band: this lane's row sees keys [klo, khi]; the wave's rows together see keys within
+  // [wlo, whi], and every one of them sees all of [wlo_all, whi_all].
+  int klo = 0, khi = 0, wlo = 0, whi = 0, wlo_all = 0, whi_all = 0;
+  if (BAND) {
+    klo = band_key_lo(qi, a.band);
+    khi = band_key_hi(qi, Lkv, a.band);
+    wlo = band_key_lo(row0, a.band);
+    whi = band_key_hi(row0 + 31, Lkv, a.band);
+    wlo_all = band_key_lo(row0 + 31, a.band);
+    whi_all = band_key_hi(row0, Lkv, a.band);
+  }
 
   const float inv_scale = 1.0f / a.scale;
   if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
@@ -145,7 +157,7 @@ void bwd_dq_kernel(BwdArgs a) {
   float nlse2 = kNegInf, dlt = 0.0f;  // -lse in log2 units; -inf makes every P of the row 0
   if (SOFTMAX) {
     // Delta_i = <dO_i, O_i>: this lane's half of the row, then the other half from lane ^ 32. The
-    // first piece of the query tile (k0 == 0) also stores it for the dK/dV kernel, which runs after.
+    // first piece of the query tile (w.first) also stores it for the dK/dV kernel, which runs after.
     float part = 0.0f;
     if (qi < Lq) {
       const float l = a.lse[(size_t)h * a.Tq + qs + qi];
@@ -153,7 +165,7 @@ void bwd_dq_kernel(BwdArgs a) {
       part = row_dot_out<NKB>(a, ((size_t)(qs + qi) * a.H + h) * D + hh * 8, df);
     }
     dlt = part + __shfl_xor(part, 32);
-    if (k0 == 0 && hh == 0 && qi < Lq) a.delta[(size_t)h * a.Tq + qs + qi] = dlt;
+    if (w.first && hh == 0 && qi < Lq) a.delta[(size_t)h * a.Tq + qs + qi] = dlt;
   }
   const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
   const float invL = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
@@ -205,7 +217,8 @@ void bwd_dq_kernel(BwdArgs a) {
       }
     }
 
-    const bool need_mask = (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
+    const bool need_mask = BAND ? (wlo_all > key0 || whi_all < key0 + BN - 1)
+                                : (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
     float ds[2][16];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -222,7 +235,7 @@ void bwd_dq_kernel(BwdArgs a) {
         }
         if (need_mask) {
           const int key = key0 + 32 * sb + acc_row(r, hh);
-          d = (key >= Lkv || (CAUSAL && key > qi)) ? 0.0f : d;
+          d = (BAND ? (key < klo || key > khi) : (key >= Lkv || (CAUSAL && key > qi))) ? 0.0f : d;
         }
         ds[sb][r] = d;
       }
@@ -268,11 +281,12 @@ struct alignas(16) DqSmem2 {
   float diag[4][kDiagLen];
 };
 
-template <int ACT, int BIAS, bool CAUSAL>
+template <int ACT, int BIAS, int MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel2(BwdArgs a) {
   constexpr int D = 128, BM = kDqBM, BN = kDqBN, NKB = D / 16, NDB = D / 32;
   constexpr bool SOFTMAX = ACT == kSoftmax;
+  constexpr bool CAUSAL = MASK == kMaskCausal, BAND = MASK == kMaskBand;
   __shared__ DqSmem2 sm;
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
@@ -286,6 +300,17 @@ void bwd_dq_kernel2(BwdArgs a) {
   const int rs = a.H * D;
   const int row0 = t * BM + wave * 32;
   const int qi = row0 + l32;
+  // Band: this lane's row sees keys [klo, khi]; the wave's rows together see keys within
+  // [wlo, whi], and every one of them sees all of [wlo_all, whi_all].
+  int klo = 0, khi = 0, wlo = 0, whi = 0, wlo_all = 0, whi_all = 0;
+  if (BAND) {
+    klo = band_key_lo(qi, a.band);
+    khi = band_key_hi(qi, Lkv, a.band);
+    wlo = band_key_lo(row0, a.band);
+    whi = band_key_hi(row0 + 31, Lkv, a.band);
+    wlo_all = band_key_lo(row0 + 31, a.band);
+    whi_all = band_key_hi(row0, Lkv, a.band);
+  }
 
   const float inv_scale = 1.0f / a.scale;
   // The bias table is written to LDS after the other prologue loads are issued (its round trip
@@ -318,7 +343,7 @@ void bwd_dq_kernel2(BwdArgs a) {
   float nlse2 = kNegInf, dlt = 0.0f;  // -lse in log2 units; -inf makes every P of the row 0
   if (SOFTMAX) {
     // Delta_i = <dO_i, O_i>: this lane's half of the row, then the other half from lane ^ 32. The
-    // first piece of the query tile (k0 == 0) also stores it for the dK/dV kernel, which runs after.
+    // first piece of the query tile (w.first) also stores it for the dK/dV kernel, which runs after.
     float part = 0.0f;
     if (qi < Lq) {
       const float l = a.lse[(size_t)h * a.Tq + qs + qi];
@@ -326,7 +351,7 @@ void bwd_dq_kernel2(BwdArgs a) {
       part = row_dot_out<NKB>(a, ((size_t)(qs + qi) * a.H + h) * D + hh * 8, df);
     }
     dlt = part + __shfl_xor(part, 32);
-    if (k0 == 0 && hh == 0 && qi < Lq) a.delta[(size_t)h * a.Tq + qs + qi] = dlt;
+    if (w.first && hh == 0 && qi < Lq) a.delta[(size_t)h * a.Tq + qs + qi] = dlt;
   }
   const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
   const float invL = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
@@ -348,19 +373,21 @@ void bwd_dq_kernel2(BwdArgs a) {
   auto tile = [&](const int kt, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     const int key0 = kt * BN;
+    // A tile with no visible pair for this wave's rows (past the diagonal, or outside the band)
+    // contributes nothing to them.
+    const bool wskip = CAUSAL ? key0 > row0 + 31 : (BAND ? (key0 > whi || key0 + BN - 1 < wlo) : false);
     wait_vm();
     // Bias of score (qi, key) at diag[31 - l32 + key - key0], ascending in register order.
-    if (BIAS == kBiasBucket && !(CAUSAL && key0 > row0 + 31))
+    if (BIAS == kBiasBucket && !wskip)
       fill_diag(sm.diag[wave], sm.tab, key0 - row0 - 31, inv_scale, lane);
     __syncthreads();
     if (kt + 1 < k1) {
       load_tile64(ld, kr, (kt + 1) * BN, rs, sm.kv[ST ^ 1][0], wave);
       load_tile64(ld, vr, (kt + 1) * BN, rs, sm.kv[ST ^ 1][1], wave);
     }
-    // Under the causal mask a tile whose first key lies past this wave's last query contributes
-    // nothing; the wave skips its work (it has taken part in the barrier and the loads above) and
-    // leaves the SIMD to the other workgroup's wave.
-    if (CAUSAL && key0 > row0 + 31) return;
+    // Such a tile's work is skipped (the wave has taken part in the barrier and the loads above),
+    // which leaves the SIMD to the other workgroup's wave.
+    if (wskip) return;
     const unsigned char* Kt = sm.kv[ST][0];
     const unsigned char* Vt = sm.kv[ST][1];
 
@@ -387,7 +414,8 @@ void bwd_dq_kernel2(BwdArgs a) {
       }
     }
 
-    const bool need_mask = (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
+    const bool need_mask = BAND ? (wlo_all > key0 || whi_all < key0 + BN - 1)
+                                : (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
     float ds[2][16];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -411,7 +439,7 @@ void bwd_dq_kernel2(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * sb + acc_row(r, hh);
-          ds[sb][r] = (key >= Lkv || (CAUSAL && key > qi)) ? 0.0f : ds[sb][r];
+          ds[sb][r] = (BAND ? (key < klo || key > khi) : (key >= Lkv || (CAUSAL && key > qi))) ? 0.0f : ds[sb][r];
         }
     }
     bf16x8 dsb[4];
@@ -468,12 +496,13 @@ struct alignas(16) KvSmem {
   unsigned long long dbh[4][kDbiasBins];  // per-wave bias-gradient bins (fixed point)
 };
 
-template <int D, int ACT, int BIASX, bool CAUSAL>
+template <int D, int ACT, int BIASX, int MK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int BM = kKvBM, BN = kKvBN, NKB = D / 16, NDB = D / 32;
   constexpr int RS = KvSmem<D>::RS, TS = KvSmem<D>::TS;
   constexpr bool SOFTMAX = ACT == kSoftmax;
+  constexpr bool CAUSAL = MK == kMaskCausal, BAND = MK == kMaskBand;
   constexpr int BIAS = BIASX & 3;
   constexpr bool DBIAS = (BIASX & kBiasGrad) != 0;
   __shared__ KvSmem<D> sm;
@@ -485,6 +514,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const int rs = a.H * D;
   const int key_w = kt * BN + wave * 32;  // first key of this wave
   const int kj = key_w + l32;
+  // Band: this lane's key is seen by rows [rlo, rhi]; every key of the wave by all of
+  // [wr_all_lo, wr_all_hi].
+  int rlo = 0, rhi = 0, wr_all_lo = 0, wr_all_hi = 0;
+  if (BAND) {
+    rlo = band_row_lo(kj, a.band);
+    rhi = band_row_hi(kj, Lq, a.band);
+    wr_all_lo = band_row_lo(key_w + 31, a.band);
+    wr_all_hi = band_row_hi(key_w, Lq, a.band);
+  }
 
   const float inv_scale = 1.0f / a.scale;
   if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
@@ -556,7 +594,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
     // Two 32-query blocks, one after the other (keeps the score temporaries of one block live):
     // S = Q K^T and dP = dO V^T with lane column = key kj and register r = query
     // qrow0 + 32 qb + acc_row(r, hh); then dV += P^T dO and dK += dS^T Q over those 32 queries.
-    const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0);
+    const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0) ||
+                           (BAND && (wr_all_lo > qrow0 || wr_all_hi < qrow0 + BM - 1));
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 sacc, pacc = f32x16{};
@@ -608,7 +647,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
           }
           if (need_mask || !SOFTMAX) {
             const int qi = qrow0 + rbase + j;
-            const bool masked = (need_mask && (kj >= Lkv || (CAUSAL && kj > qi))) || (!SOFTMAX && qi >= Lq);
+            const bool masked =
+                (need_mask && (kj >= Lkv || (CAUSAL && kj > qi) || (BAND && (qi < rlo || qi > rhi)))) ||
+                (!SOFTMAX && qi >= Lq);
             pj = masked ? 0.0f : pj;
             dj = masked ? 0.0f : dj;
           }
@@ -753,7 +794,7 @@ struct DkdvShape {
 // its epilogue, so that the queue's round trip overlaps the epilogue's stores. (Claiming earlier
 // would hide it better but would hold the claimed item back for a whole item, which lengthens the
 // tail of the run.)
-template <int ACT, int BIASX, bool CAUSAL, int NP, class Claim, class Take>
+template <int ACT, int BIASX, int MK, int NP, class Claim, class Take>
 __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4))) BwdArgs& a,
                                            typename DkdvShape<ACT, NP>::Smem& sm, int item, const int wave,
                                            Claim claim_next, Take take_next) {
@@ -762,6 +803,7 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
   constexpr bool DBIAS = (BIASX & kBiasGrad) != 0;
   constexpr bool SOFTMAX = ACT == kSoftmax;
   constexpr bool ONEBAR = DkdvShape<ACT, NP>::ONEBAR;
+  constexpr bool CAUSAL = MK == kMaskCausal, BAND = MK == kMaskBand;
   using Smem = typename DkdvShape<ACT, NP>::Smem;
 
   // Lane constants are derived anew for every item from the lane counter (no register holds the
@@ -778,6 +820,14 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
   const int rs = a.H * D;
   const int key_w = kt * BN + pair * 32;  // first key of this pair
   const int kj = key_w + l32;
+  // Band: every key of the pair is seen by all rows of [wr_all_lo, wr_all_hi] (wave-uniform). The
+  // limits are read from the argument segment where they are used.
+  auto band = [&] { return Band{a.band.window, a.band.block, a.band.causal}; };
+  int wr_all_lo = 0, wr_all_hi = 0;
+  if (BAND) {
+    wr_all_lo = band_row_lo(key_w + 31, band());
+    wr_all_hi = band_row_hi(key_w, Lq, band());
+  }
 
   const float inv_scale = 1.0f / a.scale;
   // The bias table (256 bytes) comes into LDS by the same kind of load as the tiles (wave 0), so
@@ -867,6 +917,13 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
     if (!isB) {
       auto run = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
+        // Band: rows [rlo, rhi] see this lane's key (derived here, on masked tiles only).
+        int rlo = 0, rhi = 0;
+        if (MASK && BAND) {
+          const int kjm = key_w + (lane_now() & 31);
+          rlo = band_row_lo(kjm, band());
+          rhi = band_row_hi(kjm, Lq, band());
+        }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           f32x16 sacc;
@@ -909,7 +966,9 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
               for (int j = 0; j < 8; ++j) {
                 // row index from a fresh lane index: this path runs on diagonal tiles only
                 const int qi = qrow0 + 32 * qb + 16 * c8 + 8 * (lane_now() >> 5) + j;
-                const bool masked = (MASK && (kj >= Lkv || (CAUSAL && kj > qi))) || (!SOFTMAX && qi >= Lq);
+                const bool masked =
+                    (MASK && (kj >= Lkv || (CAUSAL && kj > qi) || (BAND && (qi < rlo || qi > rhi)))) ||
+                    (!SOFTMAX && qi >= Lq);
                 pv[j] = masked ? 0.0f : pv[j];
                 if (!SOFTMAX) gv[j] = masked ? 0.0f : gv[j];
               }
@@ -919,7 +978,8 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
           }
         }
       };
-      if ((key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0))
+      if ((key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > qrow0) ||
+          (BAND && (wr_all_lo > qrow0 || wr_all_hi < qrow0 + BM - 1)))
         run(std::true_type{});
       else
         run(std::false_type{});
@@ -1131,7 +1191,7 @@ __device__ __forceinline__ int xcd_id() {
 // Persistent dK/dV kernel (NP = 4): as many workgroups as the GPU holds at once, each running items
 // from the work queue until none is left. Next to one workgroup per item this removes the gap between a
 // workgroup's end and the next one's start, and the queue balances what the items really cost.
-template <int ACT, int BIASX, bool CAUSAL, int NP>
+template <int ACT, int BIASX, int MK, int NP>
 __global__ __attribute__((amdgpu_flat_work_group_size(NP * 128, NP * 128), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel2(BwdArgs a) {
   __shared__ typename DkdvShape<ACT, NP>::Smem sm;
@@ -1147,7 +1207,7 @@ void bwd_dkdv_kernel2(BwdArgs a) {
     // second resident workgroup already covers one's start and end, and the queue would only add
     // its round trips.
     ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
-    dkdv_item2<ACT, BIASX, CAUSAL, NP>(*ap, sm, blockIdx.x, wave, [] { return 0; }, [](int) {});
+    dkdv_item2<ACT, BIASX, MK, NP>(*ap, sm, blockIdx.x, wave, [] { return 0; }, [](int) {});
     return;
   }
   if (threadIdx.x == 0) {
@@ -1181,7 +1241,7 @@ void bwd_dkdv_kernel2(BwdArgs a) {
       next_item = p;
       empty_queues = q.empty;
     };
-    dkdv_item2<ACT, BIASX, CAUSAL, NP>(*ap, sm, item, wave, claim, take);
+    dkdv_item2<ACT, BIASX, MK, NP>(*ap, sm, item, wave, claim, take);
     __syncthreads();
   }
 }
@@ -1266,11 +1326,11 @@ __global__ __launch_bounds__(256) void bwd_dbias_finish_kernel(BwdArgs a, int n)
 // ---------------------------------------------------------------- dispatch
 // D = 128 runs the LDS-ring kernels; D = 64 the register-staged ones.
 constexpr int kDkdvThreads128 = 512;
-template <int D, int ACT, int BIASX, bool CAUSAL, int NP = 4>
+template <int D, int ACT, int BIASX, int MK, int NP = 4>
 constexpr auto dkdv_select =
-    D == 128 ? &bwd_dkdv_kernel2<ACT, BIASX, CAUSAL, NP> : &bwd_dkdv_kernel<D, ACT, BIASX, CAUSAL>;
-template <int D, int ACT, int BIAS, bool CAUSAL>
-constexpr auto dq_select = D == 128 ? &bwd_dq_kernel2<ACT, BIAS, CAUSAL> : &bwd_dq_kernel<D, ACT, BIAS, CAUSAL>;
+    D == 128 ? &bwd_dkdv_kernel2<ACT, BIASX, MK, NP> : &bwd_dkdv_kernel<D, ACT, BIASX, MK>;
+template <int D, int ACT, int BIAS, int MK>
+constexpr auto dq_select = D == 128 ? &bwd_dq_kernel2<ACT, BIAS, MK> : &bwd_dq_kernel<D, ACT, BIAS, MK>;
 
 
 #define JFA_DISPATCH_MODES(KERNEL, m, n, s, a)                                                          \
@@ -1293,22 +1353,31 @@ constexpr auto dq_select = D == 128 ? &bwd_dq_kernel2<ACT, BIAS, CAUSAL> : &bwd_
     default: JFA_DISPATCH_BIAS(KERNEL, DD, kGeluTanh, m, go)                                            \
   }
 
+#define JFA_GO_MASK(KERNEL, DD, AA, BB, m, go)                                                          \
+  switch (m.mask_kind()) {                                                                              \
+    case kMaskBand: return go(KERNEL<DD, AA, BB, kMaskBand>);                                           \
+    case kMaskCausal: return go(KERNEL<DD, AA, BB, kMaskCausal>);                                       \
+    default: return go(KERNEL<DD, AA, BB, kMaskNone>);                                                  \
+  }
 #define JFA_DISPATCH_BIAS(KERNEL, DD, AA, m, go)                                                        \
   switch (m.bias) {                                                                                     \
-    case kBiasNone:                                                                                     \
-      return m.causal ? go(KERNEL<DD, AA, kBiasNone, true>) : go(KERNEL<DD, AA, kBiasNone, false>);     \
-    case kBiasScalar:                                                                                   \
-      return m.causal ? go(KERNEL<DD, AA, kBiasScalar, true>) : go(KERNEL<DD, AA, kBiasScalar, false>); \
-    default:                                                                                            \
-      return m.causal ? go(KERNEL<DD, AA, kBiasBucket, true>) : go(KERNEL<DD, AA, kBiasBucket, false>); \
+    case kBiasNone: JFA_GO_MASK(KERNEL, DD, AA, kBiasNone, m, go)                                       \
+    case kBiasScalar: JFA_GO_MASK(KERNEL, DD, AA, kBiasScalar, m, go)                                   \
+    default: JFA_GO_MASK(KERNEL, DD, AA, kBiasBucket, m, go)                                            \
   }
 
 // The dK/dV kernels also come in bias-gradient variants (bias | kBiasGrad).
 #define JFA_GO_CAUSAL(KERNEL, DD, AA, BB, m, go)                                                   \
   if constexpr (DD == 128 && AA == kSoftmax) {                                                     \
-    if (m.kv_short) return m.causal ? go(KERNEL<DD, AA, BB, true, 2>) : go(KERNEL<DD, AA, BB, false, 2>); \
+    if (m.kv_short) {                                                                              \
+      switch (m.mask_kind()) {                                                                     \
+        case kMaskBand: return go(KERNEL<DD, AA, BB, kMaskBand, 2>);                               \
+        case kMaskCausal: return go(KERNEL<DD, AA, BB, kMaskCausal, 2>);                           \
+        default: return go(KERNEL<DD, AA, BB, kMaskNone, 2>);                                      \
+      }                                                                                            \
+    }                                                                                              \
   }                                                                                                \
-  return m.causal ? go(KERNEL<DD, AA, BB, true>) : go(KERNEL<DD, AA, BB, false>);
+  JFA_GO_MASK(KERNEL, DD, AA, BB, m, go)
 #define JFA_DISPATCH_BIAS_GRAD(KERNEL, DD, AA, m, go)                                       \
   switch (m.bias | (m.dbias && !(m.bias == kBiasScalar && AA == kSoftmax) ? kBiasGrad : 0)) { \
     case kBiasNone: JFA_GO_CAUSAL(KERNEL, DD, AA, kBiasNone, m, go)                         \
@@ -1382,19 +1451,19 @@ hipError_t launch_bwd_reduce_dkdv(const BwdArgs& a, const Modes& m, int n, hipSt
 int occupancy_dq(const Modes& m) {
   int n = 0;
   hipError_t e = m.D == 64
-                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dq_kernel<64, kSoftmax, kBiasBucket, true>, kThreads, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dq_kernel2<kSoftmax, kBiasBucket, true>, kThreads, 0);
+                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dq_kernel<64, kSoftmax, kBiasBucket, kMaskCausal>, kThreads, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dq_kernel2<kSoftmax, kBiasBucket, kMaskCausal>, kThreads, 0);
   return (e == hipSuccess && n > 0) ? n : 1;
 }
 
 int occupancy_dkdv(const Modes& m) {
   int n = 0;
   hipError_t e = m.D == 64
-                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dkdv_kernel<64, kSoftmax, kBiasBucket, true>, kThreads, 0)
+                     ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, bwd_dkdv_kernel<64, kSoftmax, kBiasBucket, kMaskCausal>, kThreads, 0)
                      : m.kv_short ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                                        &n, dkdv_select<128, kSoftmax, kBiasScalar, false, 2>, kDkdvThreads128 / 2, 0)
+                                        &n, dkdv_select<128, kSoftmax, kBiasScalar, kMaskNone, 2>, kDkdvThreads128 / 2, 0)
                                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                                        &n, dkdv_select<128, kSoftmax, kBiasBucket, true>, kDkdvThreads128, 0);
+                                        &n, dkdv_select<128, kSoftmax, kBiasBucket, kMaskCausal>, kDkdvThreads128, 0);
   return (e == hipSuccess && n > 0) ? n : 1;
 }
 

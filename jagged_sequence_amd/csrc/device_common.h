@@ -134,18 +134,50 @@ __device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret
 // A work record (item or split group), read through the constant address space: the list is never
 // written while a kernel runs, and the promise lets the compiler fetch the record with scalar loads.
 struct WorkRec {
-  int b, h, tile, lo, hi, slot, qs, Lq, ks, Lkv;
+  int b, h, tile, lo, hi, slot, qs, Lq, ks, Lkv, first;
 };
 __device__ __forceinline__ WorkRec load_item(const int32_t* list, int i) {
   typedef const __attribute__((address_space(4))) int32_t* cptr;
   const cptr r = (cptr)(list + (size_t)i * kItemInts);
-  return {r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7], r[8], r[9]};
+  return {r[0], r[1], r[2], r[3], r[4], r[5], r[6], r[7], r[8], r[9], r[10]};
 }
 __device__ __forceinline__ WorkRec load_group(const int32_t* list, int i) {
   typedef const __attribute__((address_space(4))) int32_t* cptr;
   const cptr r = (cptr)(list + (size_t)i * kGroupInts);
   // group layout: b, h, tile, slot0, R, qs, Lq, ks, Lkv (slot0 and R returned in lo and hi)
-  return {r[0], r[1], r[2], r[3], r[4], -1, r[5], r[6], r[7], r[8]};
+  return {r[0], r[1], r[2], r[3], r[4], -1, r[5], r[6], r[7], r[8], 0};
+}
+
+// Band visibility (window W and / or block Bk, with or without the causal limit). Query i and key
+// j are visible together iff band_key_lo(i) <= j <= band_key_hi(i), equivalently iff
+// band_row_lo(j) <= i <= band_row_hi(j); every bound is non-decreasing in its argument, so the
+// bounds of a run of rows (keys) are those of its first and last. Positions are within-sequence;
+// the sequence's key (row) count clips the upper bound, so one test also masks the ragged tail.
+__device__ __forceinline__ int band_key_lo(int i, Band b) {
+  int lo = 0;
+  if (b.window) lo = max(lo, i - b.window + 1);
+  if (b.block) lo = max(lo, (i / b.block) * b.block);
+  return lo;
+}
+__device__ __forceinline__ int band_key_hi(int i, int Lkv, Band b) {
+  int hi = Lkv - 1;
+  if (b.causal) hi = min(hi, i);
+  else if (b.window) hi = min(hi, i + b.window - 1);
+  if (b.block) hi = min(hi, (i / b.block) * b.block + b.block - 1);
+  return hi;
+}
+__device__ __forceinline__ int band_row_lo(int j, Band b) {
+  int lo = 0;
+  if (b.causal) lo = j;
+  else if (b.window) lo = max(lo, j - b.window + 1);
+  if (b.block) lo = max(lo, (j / b.block) * b.block);
+  return lo;
+}
+__device__ __forceinline__ int band_row_hi(int j, int Lq, Band b) {
+  int hi = Lq - 1;
+  if (b.window) hi = min(hi, j + b.window - 1);
+  if (b.block) hi = min(hi, (j / b.block) * b.block + b.block - 1);
+  return hi;
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const uint16_t* base, int rows, int rs, int D) {

@@ -74,12 +74,13 @@ __device__ __forceinline__ void store_kv(const KvRegs<D>& r, FwdSmem<D>& sm, int
 // exact in fp32 and as relative-precision bf16 operands), which skips most rescales.
 constexpr float kLazy = 8.0f;
 
-template <int D, int ACT, int BIAS, bool CAUSAL>
+template <int D, int ACT, int BIAS, int MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdArgs a) {
   constexpr int BM = kFwdBM, BN = kFwdBN, NKB = D / 16, NDB = D / 32;
   constexpr int KS = FwdSmem<D>::KS, VS = FwdSmem<D>::VS;
   constexpr bool SOFTMAX = ACT == kSoftmax;
+  constexpr bool CAUSAL = MASK == kMaskCausal, BAND = MASK == kMaskBand;
   __shared__ FwdSmem<D> sm;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
@@ -90,6 +91,17 @@ void fwd_kernel(FwdArgs a) {
   const int row0 = t * BM + wave * 32;
   const int qi = row0 + l32;
   const float inv_scale = 1.0f / a.scale;
+  // Band: this lane's row sees keys [klo, khi]; the wave's rows together see keys within
+  // [wlo, whi], and every one of them sees all of [wlo_all, whi_all].
+  int klo = 0, khi = 0, wlo = 0, whi = 0, wlo_all = 0, whi_all = 0;
+  if (BAND) {
+    klo = band_key_lo(qi, a.band);
+    khi = band_key_hi(qi, Lkv, a.band);
+    wlo = band_key_lo(row0, a.band);
+    whi = band_key_hi(row0 + 31, Lkv, a.band);
+    wlo_all = band_key_lo(row0 + 31, a.band);
+    whi_all = band_key_hi(row0, Lkv, a.band);
+  }
 
   if (BIAS == kBiasBucket && tid < kBuckets) sm.tab[tid] = a.bias[h * kBuckets + tid];
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
@@ -143,14 +155,15 @@ void fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < NKB; ++kb) sacc[sb] = mfma32(lds_load8(kp + kb * 16), qf[kb], sacc[sb]);
     }
 
-    const bool need_mask = (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
+    const bool need_mask = BAND ? (wlo_all > key0 || whi_all < key0 + BN - 1)
+                                : (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
     if (need_mask) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * sb + acc_row(r, hh);
-          const bool masked = key >= Lkv || (CAUSAL && key > qi);
+          const bool masked = BAND ? (key < klo || key > khi) : (key >= Lkv || (CAUSAL && key > qi));
           sacc[sb][r] = masked ? (SOFTMAX ? kNegInf : __builtin_nanf("")) : sacc[sb][r];
         }
     }
@@ -250,11 +263,12 @@ struct alignas(16) FwdSmem2 {
   float diag[4][kDiagLen];
 };
 
-template <int ACT, int BIAS, bool CAUSAL>
+template <int ACT, int BIAS, int MASK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel2(FwdArgs a) {
   constexpr int D = 128, BM = kFwdBM, BN = kFwdBN, NKB = D / 16, NDB = D / 32;
   constexpr bool SOFTMAX = ACT == kSoftmax;
+  constexpr bool CAUSAL = MASK == kMaskCausal, BAND = MASK == kMaskBand;
   __shared__ FwdSmem2 sm;
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
@@ -266,6 +280,17 @@ void fwd_kernel2(FwdArgs a) {
   const int row0 = t * BM + wave * 32;
   const int qi = row0 + l32;
   const float inv_scale = 1.0f / a.scale;
+  // Band: this lane's row sees keys [klo, khi]; the wave's rows together see keys within
+  // [wlo, whi], and every one of them sees all of [wlo_all, whi_all].
+  int klo = 0, khi = 0, wlo = 0, whi = 0, wlo_all = 0, whi_all = 0;
+  if (BAND) {
+    klo = band_key_lo(qi, a.band);
+    khi = band_key_hi(qi, Lkv, a.band);
+    wlo = band_key_lo(row0, a.band);
+    whi = band_key_hi(row0 + 31, Lkv, a.band);
+    wlo_all = band_key_lo(row0 + 31, a.band);
+    whi_all = band_key_hi(row0, Lkv, a.band);
+  }
 
   // The bias table is loaded here and written to LDS after the other prologue loads are issued, so
   // that its round trip overlaps theirs.
@@ -307,20 +332,22 @@ void fwd_kernel2(FwdArgs a) {
   auto tile = [&](const int kt, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     const int key0 = kt * BN;
+    // A tile with no visible pair for this wave's rows (past the diagonal, or outside the band)
+    // contributes nothing to them.
+    const bool wskip = CAUSAL ? key0 > row0 + 31 : (BAND ? (key0 > whi || key0 + BN - 1 < wlo) : false);
     wait_vm();
     // Bias of score (qi, key) sits at diag[qi - key + 31 - (row0 - key0)] = diag[31 - l32 + key - key0]:
     // ascending in the accumulator's register order.
-    if (BIAS == kBiasBucket && !(CAUSAL && key0 > row0 + 31))
+    if (BIAS == kBiasBucket && !wskip)
       fill_diag(sm.diag[wave], sm.tab, key0 - row0 - 31, inv_scale, lane);
     __syncthreads();
     if (kt + 1 < k1) {
       load_tile64(ld, kr, (kt + 1) * BN, rs, sm.kv[ST ^ 1][0], wave);
       load_tile64(ld, vr, (kt + 1) * BN, rs, sm.kv[ST ^ 1][1], wave);
     }
-    // Under the causal mask a tile whose first key lies past this wave's last query contributes
-    // nothing; the wave skips its work (it has taken part in the barrier and the loads above) and
-    // leaves the SIMD to the other workgroup's wave.
-    if (CAUSAL && key0 > row0 + 31) return;
+    // Such a tile's work is skipped (the wave has taken part in the barrier and the loads above),
+    // which leaves the SIMD to the other workgroup's wave.
+    if (wskip) return;
     const unsigned char* Kt = sm.kv[ST][0];
     const unsigned char* Vt = sm.kv[ST][1];
 
@@ -343,14 +370,15 @@ void fwd_kernel2(FwdArgs a) {
         sacc[sb] = mfma32(lds_read16(Kt, (kaddr ^ (uint32_t)(kb << 5)) + sb * 32 * kRowBytes), qf[kb], sacc[sb]);
     }
 
-    const bool need_mask = (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
+    const bool need_mask = BAND ? (wlo_all > key0 || whi_all < key0 + BN - 1)
+                                : (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
     if (need_mask) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * sb + acc_row(r, hh);
-          const bool masked = key >= Lkv || (CAUSAL && key > qi);
+          const bool masked = BAND ? (key < klo || key > khi) : (key >= Lkv || (CAUSAL && key > qi));
           sacc[sb][r] = masked ? (SOFTMAX ? kNegInf : __builtin_nanf("")) : sacc[sb][r];
         }
     }
@@ -504,18 +532,22 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
         lse2 == kNegInf ? kNegInf : lse2 * kLn2 + (BIAS == kBiasScalar ? a.bias[h] : 0.0f);
 }
 
-template <int D, int ACT, int BIAS, bool CAUSAL>
+template <int D, int ACT, int BIAS, int MASK>
 hipError_t fwd_launch_t(const FwdArgs& a, int n, hipStream_t s) {
   if (D == 128)
-    hipLaunchKernelGGL((fwd_kernel2<ACT, BIAS, CAUSAL>), dim3(n), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel2<ACT, BIAS, MASK>), dim3(n), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<D, ACT, BIAS, CAUSAL>), dim3(n), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<D, ACT, BIAS, MASK>), dim3(n), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D, int ACT, int BIAS>
 hipError_t fwd_launch_c(const FwdArgs& a, const Modes& m, int n, hipStream_t s) {
-  return m.causal ? fwd_launch_t<D, ACT, BIAS, true>(a, n, s) : fwd_launch_t<D, ACT, BIAS, false>(a, n, s);
+  switch (m.mask_kind()) {
+    case kMaskBand: return fwd_launch_t<D, ACT, BIAS, kMaskBand>(a, n, s);
+    case kMaskCausal: return fwd_launch_t<D, ACT, BIAS, kMaskCausal>(a, n, s);
+    default: return fwd_launch_t<D, ACT, BIAS, kMaskNone>(a, n, s);
+  }
 }
 
 template <int D, int ACT>
@@ -570,9 +602,9 @@ int occupancy_forward(const Modes& m) {
   int n = 0;
   hipError_t e;
   if (m.D == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<64, kSoftmax, kBiasBucket, true>, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel<64, kSoftmax, kBiasBucket, kMaskCausal>, kThreads, 0);
   else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel2<kSoftmax, kBiasBucket, true>, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fwd_kernel2<kSoftmax, kBiasBucket, kMaskCausal>, kThreads, 0);
   return (e == hipSuccess && n > 0) ? n : 1;
 }
 

@@ -145,8 +145,56 @@ std::vector<int> dispatch_order(const List& L) {
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Query-tile list: item (b, h, t) covers key tiles [0, cost).
-void query_tile_list(const std::vector<int>& lq, const std::vector<int>& lkv, int H, bool causal, int BM, int BN,
+// Optional window / block limits on visibility (0 = off). With either on, an item covers only the
+// tiles that hold a visible pair: the keys seen by a run of rows, and the rows that see a run of
+// keys, form one interval because every bound is non-decreasing in the position.
+struct Limits {
+  bool causal;
+  int window, block;
+  bool band() const { return window > 0 || block > 0; }
+};
+
+// Key tiles [lo, hi) holding a visible pair for query tile t (band limits on).
+void band_key_tiles(int t, int Lq, int Lkv, const Limits& m, int BM, int BN, int& lo, int& hi) {
+  const int64_t r0 = (int64_t)t * BM, r1 = std::min<int64_t>((int64_t)(t + 1) * BM, Lq) - 1;
+  int64_t first = 0, last = (int64_t)Lkv - 1;
+  if (m.window) {
+    first = std::max<int64_t>(first, r0 - m.window + 1);
+    if (!m.causal) last = std::min<int64_t>(last, r1 + m.window - 1);
+  }
+  if (m.causal) last = std::min(last, r1);
+  if (m.block) {
+    first = std::max<int64_t>(first, (r0 / m.block) * m.block);
+    last = std::min<int64_t>(last, (r1 / m.block) * m.block + m.block - 1);
+  }
+  if (last < first) {
+    lo = hi = 0;
+    return;
+  }
+  lo = (int)(first / BN);
+  hi = (int)(last / BN) + 1;
+}
+
+// Query tiles [lo, hi) holding a visible pair for key tile kt (band limits on); empty: [lo, lo).
+void band_query_tiles(int kt, int Lq, int Lkv, const Limits& m, int BMq, int BNk, int& lo, int& hi) {
+  const int64_t c0 = (int64_t)kt * BNk, c1 = std::min<int64_t>((int64_t)(kt + 1) * BNk, Lkv) - 1;
+  int64_t first = 0, last = (int64_t)Lq - 1;
+  if (m.causal) first = c0;
+  if (m.window) {
+    last = std::min<int64_t>(last, c1 + m.window - 1);
+    if (!m.causal) first = std::max<int64_t>(first, c0 - m.window + 1);
+  }
+  if (m.block) {
+    first = std::max<int64_t>(first, (c0 / m.block) * m.block);
+    last = std::min<int64_t>(last, (c1 / m.block) * m.block + m.block - 1);
+  }
+  lo = (int)(first / BMq);
+  hi = last < first ? lo : (int)(last / BMq) + 1;
+}
+
+// Query-tile list: item (b, h, t) covers key tiles [0, cost) (band limits: the tiles holding a
+// visible pair).
+void query_tile_list(const std::vector<int>& lq, const std::vector<int>& lkv, int H, const Limits& m, int BM, int BN,
                      int slots, bool split, List& out) {
   std::vector<Raw> raw;
   for (size_t b = 0; b < lq.size(); ++b) {
@@ -154,15 +202,20 @@ void query_tile_list(const std::vector<int>& lq, const std::vector<int>& lkv, in
     const int n_t = ceil_div(lq[b], BM);
     for (int h = 0; h < H; ++h)
       for (int t = 0; t < n_t; ++t) {
-        const int cost = causal ? std::min(ceil_div((t + 1) * BM, BN), n_kv) : n_kv;
-        raw.push_back({(int)b, h, t, 0, cost});
+        int lo = 0, hi = 0;
+        if (m.band())
+          band_key_tiles(t, lq[b], lkv[b], m, BM, BN, lo, hi);
+        else
+          hi = m.causal ? std::min(ceil_div((t + 1) * BM, BN), n_kv) : n_kv;
+        raw.push_back({(int)b, h, t, lo, hi});
       }
   }
   finish(raw, slots, split, out);
 }
 
-// Key-tile list: item (b, h, kt) covers query tiles [first, first + cost).
-void key_tile_list(const std::vector<int>& lq, const std::vector<int>& lkv, int H, bool causal, int BMq, int BNk,
+// Key-tile list: item (b, h, kt) covers query tiles [first, first + cost) (band limits: the tiles
+// holding a visible pair).
+void key_tile_list(const std::vector<int>& lq, const std::vector<int>& lkv, int H, const Limits& m, int BMq, int BNk,
                    int slots, bool split, List& out) {
   std::vector<Raw> raw;
   for (size_t b = 0; b < lq.size(); ++b) {
@@ -170,9 +223,14 @@ void key_tile_list(const std::vector<int>& lq, const std::vector<int>& lkv, int 
     const int n_kt = ceil_div(lkv[b], BNk);
     for (int h = 0; h < H; ++h)
       for (int kt = 0; kt < n_kt; ++kt) {
-        const int first = causal ? (int)(((int64_t)kt * BNk) / BMq) : 0;
-        const int cost = std::max(0, n_q - first);
-        raw.push_back({(int)b, h, kt, first, first + cost});
+        int lo = 0, hi = 0;
+        if (m.band()) {
+          band_query_tiles(kt, lq[b], lkv[b], m, BMq, BNk, lo, hi);
+        } else {
+          lo = m.causal ? (int)(((int64_t)kt * BNk) / BMq) : 0;
+          hi = lo + std::max(0, n_q - lo);
+        }
+        raw.push_back({(int)b, h, kt, lo, hi});
       }
   }
   finish(raw, slots, split, out);
@@ -186,6 +244,7 @@ struct jfa_plan_s {
   int B = 0, H = 0, D = 0, Tq = 0, Tkv = 0;
   int kv_bn = kKvBN;  // keys per dK/dV item
   Modes modes{};
+  Band band{};
   float scale = 0.0f;
   int out_f32 = 0, grad_f32 = 0;
   uint32_t flags = 0;
@@ -225,6 +284,7 @@ jfa_status check_problem(const jfa_problem* p, std::vector<int>& lq, std::vector
   if (p->num_slots < 0) return fail(JFA_ERR_BAD_SHAPE, "num_slots must be >= 0");
   if (!std::isfinite(p->scale)) return fail(JFA_ERR_UNSUPPORTED, "scale must be finite");
   if ((p->flags & ~(JFA_PLAN_HOST_ONLY | JFA_PLAN_NO_SPLIT)) != 0) return fail(JFA_ERR_UNSUPPORTED, "unknown flags");
+  if (p->window < 0 || p->block < 0) return fail(JFA_ERR_BAD_SHAPE, "window and block must be >= 0");
   const int B = p->num_seqs;
   if (p->q_offsets_host[0] != 0 || p->kv_offsets_host[0] != 0) return fail(JFA_ERR_BAD_OFFSETS, "offsets[0] must be 0");
   lq.resize(B);
@@ -310,6 +370,8 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   P->Tq = P->q_off[P->B];
   P->Tkv = P->kv_off[P->B];
   P->modes = Modes{p.head_dim, p.act, p.bias, p.mask == JFA_MASK_CAUSAL ? 1 : 0};
+  P->band = Band{p.window, p.block, p.mask == JFA_MASK_CAUSAL ? 1 : 0};
+  P->modes.band = (p.window > 0 || p.block > 0) ? 1 : 0;
   {
     int max_lq = 0;
     for (int x : lq) max_lq = std::max(max_lq, x);
@@ -351,10 +413,10 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
     }
     P->kv_resident = std::max(1, cus * occupancy_dkdv(P->modes));
   }
-  const bool causal = P->modes.causal != 0;
-  query_tile_list(lq, lkv, P->H, causal, kFwdBM, kFwdBN, slots[kFwd], split, P->lists[kFwd]);
-  query_tile_list(lq, lkv, P->H, causal, kDqBM, kDqBN, slots[kDq], split, P->lists[kDq]);
-  key_tile_list(lq, lkv, P->H, causal, kKvBM, P->kv_bn, slots[kKv], split, P->lists[kKv]);
+  const Limits lim{P->modes.causal != 0, p.window, p.block};
+  query_tile_list(lq, lkv, P->H, lim, kFwdBM, kFwdBN, slots[kFwd], split, P->lists[kFwd]);
+  query_tile_list(lq, lkv, P->H, lim, kDqBM, kDqBN, slots[kDq], split, P->lists[kDq]);
+  key_tile_list(lq, lkv, P->H, lim, kKvBM, P->kv_bn, slots[kKv], split, P->lists[kKv]);
   for (auto& L : P->lists) L.order = dispatch_order(L);
 
   // workspace layout
@@ -395,10 +457,13 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
     for (int l = 0; l < 3; ++l) {
       List& L = P->lists[l];
       offs[l][0] = pos;
+      std::vector<char> first_slot(L.nslots, 0);  // slot of the first piece of each split item
+      for (size_t g = 0; g < L.n_groups(); ++g) first_slot[L.groups[g * 5 + 3]] = 1;
       for (size_t i = 0; i < L.n_items(); ++i, pos += kItemInts) {
         const int32_t* it = &L.items[(size_t)L.order[i] * 6];
         std::copy_n(it, 6, &host[pos]);
         put_seq(&host[pos + 6], it[0]);
+        host[pos + 10] = (it[5] < 0 || first_slot[it[5]]) ? 1 : 0;
       }
       offs[l][1] = pos;
       for (size_t g = 0; g < L.n_groups(); ++g, pos += kGroupInts) {
@@ -472,6 +537,7 @@ jfa_status jfa_forward(jfa_plan_t P, const void* q, const void* k, const void* v
   a.Tq = P->Tq;
   a.scale = P->scale;
   a.out_f32 = P->out_f32;
+  a.band = P->band;
   const List& L = P->lists[kFwd];
   st = timed(P, 0, s, [&] { return launch_forward(a, P->modes, (int)L.n_items(), s); }, "forward launch");
   if (st != JFA_OK) return st;
@@ -531,6 +597,7 @@ jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* 
   a.Tkv = P->Tkv;
   a.scale = P->scale;
   a.out_f32 = P->out_f32;
+  a.band = P->band;
   a.grad_f32 = P->grad_f32;
   a.kv_bn = P->kv_bn;
   a.kv_queue = (ws && P->D == 128) ? reinterpret_cast<int*>(ws + P->off_queue) : nullptr;

@@ -20,7 +20,8 @@ constexpr int kKvBNShort = 64;
 constexpr int kThreads = 256;
 // Device work records carry the sequence's offsets and lengths, so a workgroup starts with a single
 // load of its record (no dependent load of the offset arrays):
-//   item:  b, h, tile, lo, hi, slot, qs, Lq, ks, Lkv, 0 x 6
+//   item:  b, h, tile, lo, hi, slot, qs, Lq, ks, Lkv, first, 0 x 5
+//          (first = 1 on an unsplit item and on the first piece of a split one)
 //   group: b, h, tile, slot0, R, qs, Lq, ks, Lkv, 0 x 7
 constexpr int kItemInts = 16;
 constexpr int kGroupInts = 16;
@@ -29,6 +30,17 @@ constexpr int kBuckets = 64;
 constexpr int kQueues = 8;
 
 enum Act { kSoftmax = 0, kSilu = 1, kGeluTanh = 2 };
+// Mask template argument of the attention kernels. kMaskBand covers a window and / or a block
+// limit (with or without the causal limit, given at run time): every lane derives the interval of
+// positions it may pair with, so one comparison pair masks a score whatever limits are on.
+enum MaskKind { kMaskNone = 0, kMaskCausal = 1, kMaskBand = 2 };
+
+// Run-time limits of kMaskBand (0 = off).
+struct Band {
+  int window;
+  int block;
+  int causal;
+};
 enum BiasKind { kBiasNone = 0, kBiasScalar = 1, kBiasBucket = 2 };
 
 struct FwdArgs {
@@ -48,6 +60,7 @@ struct FwdArgs {
   int Tq;
   float scale;
   int out_f32;
+  Band band;
 };
 
 struct BwdArgs {
@@ -82,6 +95,7 @@ struct BwdArgs {
   int kv_bn;  // keys per dK/dV item (kKvBN or kKvBNShort)
   int* kv_queue;  // kQueues counters of the dK/dV work queue (D = 128); the dQ kernel zeroes them
   int kv_n;       // dK/dV items
+  Band band;
 };
 
 struct Modes {
@@ -91,6 +105,8 @@ struct Modes {
   int causal;
   int dbias;     // the bias gradient is requested
   int kv_short;  // dK/dV items of kKvBNShort keys (D = 128, every Lq <= kKvBM)
+  int band;      // a window or block limit is on (kMaskBand kernels)
+  int mask_kind() const { return band ? kMaskBand : (causal ? kMaskCausal : kMaskNone); }
 };
 
 // Bias template argument of the dK/dV kernels: kBiasScalar / kBiasBucket, plus kBiasGrad when the

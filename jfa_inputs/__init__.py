@@ -50,6 +50,8 @@ class Workload:
     bias_sigma: float = 0.0
     backward: bool = True
     description: str = ""
+    window: int = 0               # sliding-window limit (0 = off)
+    block: int = 0                # block-attention limit (0 = off)
 
 
 WORKLOADS = {
@@ -77,6 +79,12 @@ WORKLOADS = {
         Workload("longtail_1m", 5, 1652, 8, 128, ("pareto", 1.2, 128, 32768), None, "causal", "softmax",
                  "bucket", 0.5,
                  description="as longtail, B=1652: the first batch of the same stream with >= 1M tokens"),
+        # Sliding-window attention on the long-tail lengths: the pages apply it to long-sequence
+        # self-attention and skip the tiles outside the window, without naming a window size;
+        # 1024 keys (a few times the median length) is the stand-in.
+        Workload("longtail_swa", 5, 512, 8, 128, ("pareto", 1.2, 128, 32768), None, "causal", "softmax",
+                 "bucket", 0.5, window=1024,
+                 description="as longtail with a causal sliding window of 1024 keys"),
     ]
 }
 
@@ -146,6 +154,8 @@ class Inputs:
     mask: str
     act: str
     bias_kind: str
+    window: int = 0
+    block: int = 0
 
     @property
     def B(self) -> int:
@@ -153,7 +163,8 @@ class Inputs:
 
 
 def make_inputs(lq, lkv, H: int, D: int, *, wid: int, mask: str = "none", act: str = "softmax",
-                bias_kind: str = "none", bias_sigma: float = 0.5, with_do: bool = True) -> Inputs:
+                bias_kind: str = "none", bias_sigma: float = 0.5, with_do: bool = True, window: int = 0,
+                block: int = 0) -> Inputs:
     """Operands for arbitrary per-sequence lengths, from the value streams of id ``wid``."""
     if mask not in MASKS or act not in ACTS or bias_kind not in BIASES:
         raise ValueError("bad mode")
@@ -170,7 +181,7 @@ def make_inputs(lq, lkv, H: int, D: int, *, wid: int, mask: str = "none", act: s
         shape = (H,) if bias_kind == "scalar" else (H, NUM_BUCKETS)
         rng = np.random.default_rng([wid, _T_BIAS])
         bias = (rng.standard_normal(int(np.prod(shape)), dtype=np.float32) * np.float32(bias_sigma)).reshape(shape)
-    return Inputs(q, k, v, do, bias, q_off, kv_off, H, D, mask, act, bias_kind)
+    return Inputs(q, k, v, do, bias, q_off, kv_off, H, D, mask, act, bias_kind, int(window), int(block))
 
 
 def workload_inputs(name: str, with_do: Optional[bool] = None) -> Inputs:
@@ -180,4 +191,4 @@ def workload_inputs(name: str, with_do: Optional[bool] = None) -> Inputs:
     if with_do is None:
         with_do = w.backward
     return make_inputs(lq, lkv, w.H, w.D, wid=w.wid, mask=w.mask, act=w.act, bias_kind=w.bias,
-                       bias_sigma=w.bias_sigma, with_do=with_do)
+                       bias_sigma=w.bias_sigma, with_do=with_do, window=w.window, block=w.block)

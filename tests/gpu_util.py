@@ -43,7 +43,8 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 def run_gpu(x: ji.Inputs, *, out_dtype="f32", grad_dtype="f32", num_slots=0, no_split=False, backward=True,
             scale=0.0, dbias=False):
     plan = J.Plan(x.q_off, x.kv_off, x.H, x.D, mask=x.mask, act=x.act, bias=x.bias_kind, out_dtype=out_dtype,
-                  grad_dtype=grad_dtype, num_slots=num_slots, no_split=no_split, scale=scale)
+                  grad_dtype=grad_dtype, num_slots=num_slots, no_split=no_split, scale=scale, window=x.window,
+                  block=x.block)
     q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
     qo = torch.from_numpy(x.q_off).cuda()
     ko = torch.from_numpy(x.kv_off).cuda()
@@ -66,7 +67,8 @@ def oracle(x: ji.Inputs, *, backward=True, seqs=None, heads=None):
     f = A.bf16_bits_to_f64
     q, k, v = f(x.q), f(x.k), f(x.v)
     bias = None if x.bias is None else x.bias.astype(np.float64)
-    kw = dict(mask=x.mask, act=x.act, bias_kind=x.bias_kind, bias=bias, seqs=seqs, heads=heads)
+    kw = dict(mask=x.mask, act=x.act, bias_kind=x.bias_kind, bias=bias, seqs=seqs, heads=heads, window=x.window,
+              block=x.block)
     out, lse = A.forward(q, k, v, x.q_off, x.kv_off, **kw)
     res = {"out": out, "lse": lse}
     if x.act != "softmax":

@@ -47,11 +47,12 @@ CASES = [
 ]
 
 
-def _compare(plan, lq, lkv, H, causal, slots, split):
+def _compare(plan, lq, lkv, H, causal, slots, split, window=0, block=0):
     info = plan.info()
-    fi, fg, _ = S.query_tile_items(lq, lkv, H, causal, info["fwd_bm"], info["fwd_bn"], slots, split)
-    qi, qg, _ = S.query_tile_items(lq, lkv, H, causal, info["dq_bm"], info["dq_bn"], slots, split)
-    ki, kg, _ = S.key_tile_items(lq, lkv, H, causal, info["kv_bm"], info["kv_bn"], slots, split)
+    kw = dict(window=window, block=block)
+    fi, fg, _ = S.query_tile_items(lq, lkv, H, causal, info["fwd_bm"], info["fwd_bn"], slots, split, **kw)
+    qi, qg, _ = S.query_tile_items(lq, lkv, H, causal, info["dq_bm"], info["dq_bn"], slots, split, **kw)
+    ki, kg, _ = S.key_tile_items(lq, lkv, H, causal, info["kv_bm"], info["kv_bn"], slots, split, **kw)
     for which, expect in enumerate([fi, fg, qi, qg, ki, kg]):
         got = plan.schedule(which)
         np.testing.assert_array_equal(got, np.array(expect, dtype=np.int32).reshape(got.shape), err_msg=str(which))
@@ -69,6 +70,28 @@ def test_schedule_bit_exact_vs_spec(case, slots, split):
     plan = _host_plan(lq, lkv, 3, mask=mask, num_slots=slots, no_split=not split)
     assert plan.info()["fwd_slots"] == slots
     _compare(plan, lq, lkv, 3, mask == "causal", slots, split)
+
+
+BAND_CASES = [
+    ([5, 130, 0, 257, 64, 700], [5, 130, 0, 257, 64, 700], "causal", 100, 0),
+    ([5, 130, 0, 257, 64, 700], [5, 130, 0, 257, 64, 700], "causal", 1, 0),
+    ([5, 130, 0, 257, 64, 700], [5, 130, 0, 257, 64, 700], "causal", 0, 200),
+    ([5, 130, 0, 257, 64, 700], [5, 130, 0, 257, 64, 700], "causal", 300, 256),
+    ([1, 40, 3, 64, 300], [300, 17, 0, 1000, 90], "none", 70, 0),
+    ([1, 40, 3, 64, 300], [300, 17, 0, 1000, 90], "none", 0, 50),
+    ([700, 129, 1], [700, 129, 1], "none", 64, 128),
+    ([40, 3, 64], [40, 3, 64], "none", 0, 16),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BAND_CASES)))
+@pytest.mark.parametrize("slots", [1, 7, 512])
+@pytest.mark.parametrize("D", [64, 128])
+def test_band_schedule_bit_exact_vs_spec(case, slots, D):
+    """Window / block limits: the planner's lists equal the spec's, including empty ranges."""
+    lq, lkv, mask, window, block = BAND_CASES[case]
+    plan = _host_plan(lq, lkv, 2, D=D, mask=mask, num_slots=slots, window=window, block=block)
+    _compare(plan, lq, lkv, 2, mask == "causal", slots, True, window, block)
 
 
 @pytest.mark.parametrize("name", ["small_fwd", "causal_bucket", "target_attn", "gdpa_silu", "longtail"])
@@ -153,6 +176,8 @@ def test_plan_validation_errors():
     assert _status_of(lambda: _host_plan([3, 4], [3, 5], 2, mask="causal")) == "JFA_ERR_BAD_SHAPE"
     assert _status_of(lambda: _host_plan(*ok, 2, num_slots=-1)) == "JFA_ERR_BAD_SHAPE"
     assert _status_of(lambda: _host_plan(*ok, 2, scale=float("nan"))) == "JFA_ERR_UNSUPPORTED"
+    assert _status_of(lambda: _host_plan(*ok, 2, window=-1)) == "JFA_ERR_BAD_SHAPE"
+    assert _status_of(lambda: _host_plan(*ok, 2, block=-3)) == "JFA_ERR_BAD_SHAPE"
     # causal with equal lengths and an empty sequence is fine
     _host_plan([3, 0, 4], [3, 0, 4], 2, mask="causal")
 
