@@ -293,7 +293,7 @@ void bwd_dq_kernel2(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // The dK/dV kernel, which runs after this one, takes its items from a queue whose counters
   // start at zero.
-  if (blockIdx.x == 0 && threadIdx.x < kQueues && a.kv_queue) a.kv_queue[threadIdx.x] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < kQueueCounters && a.kv_queue) a.kv_queue[threadIdx.x] = 0;
   const WorkRec w = load_item(a.dq_items, blockIdx.x);
   const int h = w.h, t = w.tile, k0 = w.lo, k1 = w.hi, slot = w.slot;
   const int qs = w.qs, Lq = w.Lq, ks = w.ks, Lkv = w.Lkv;
@@ -1129,7 +1129,34 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
 
   // Accumulator register r of d-block db: dimension 32 db + 8 (r/4) + 4 hh + r%4, key kj.
   const float sc = isB ? a.scale : 1.0f;
-  if (slot < 0) {
+  if (slot < 0 && !a.grad_f32) {
+    // bf16 rows go out through LDS: each lane holds 4-element pieces of 16 rows' columns, so a direct
+    // store would touch 32 rows with 16 bytes each; staged, a store writes 4 whole 256-byte rows.
+    // Once every wave is past the last tile the Q / dO ring is free: 8 KB per wave (32 rows x 128
+    // bf16); the 16-byte chunk c of row r sits at c ^ (r & 15), so neither side conflicts.
+    __syncthreads();
+    unsigned char* stg = &sm.qg[0][0][0] + wave * (32 * kRowBytes);
+    const int r = le & 31;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 4 * db + g;
+        *reinterpret_cast<uint2*>(stg + r * kRowBytes + ((c ^ (r & 15)) << 4) + 8 * hhe) =
+            make_uint2(pack2_bf16(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc),
+                       pack2_bf16(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc));
+      }
+    wave_lds_fence();
+    char* dst = static_cast<char*>(isB ? a.dk : a.dv);
+    const int cc = le & 15;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int row = 4 * it + (le >> 4);
+      const uint4 x = *reinterpret_cast<const uint4*>(stg + row * kRowBytes + ((cc ^ (row & 15)) << 4));
+      if (key_w + row < Lkv)
+        *reinterpret_cast<uint4*>(dst + (((size_t)(ks + key_w + row) * a.H + h) * D) * 2 + cc * 16) = x;
+    }
+  } else if (slot < 0) {
     if (kje < Lkv) {
       void* dst = isB ? a.dk : a.dv;
       const size_t base = ((size_t)(ks + kje) * a.H + h) * D;
@@ -1150,6 +1177,33 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
             make_float4(acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]);
   }
   take_next(token);
+}
+
+// dQ of one split group (b, h, tile, slot0, R) by NT threads: NT / BM threads per row, each summing
+// its columns over r = 0..R-1 in that order.
+template <int D, int NT>
+__device__ __forceinline__ void reduce_dq_group(const WorkRec& g, const float* part_dq, void* dq, int H, float scale,
+                                                int grad_f32, int tid) {
+  constexpr int BM = kDqBM, TPR = NT / BM, COLS = D / TPR;
+  const int h = g.h, t = g.tile, slot0 = g.lo, R = g.hi;
+  const int row = tid / TPR, part = tid % TPR;
+  const int qi = t * BM + row;
+  if (qi >= g.Lq) return;
+  float acc[COLS];
+#pragma unroll
+  for (int d = 0; d < COLS; ++d) acc[d] = 0.0f;
+  for (int r = 0; r < R; ++r) {
+    const float* p = part_dq + ((size_t)(slot0 + r) * BM + row) * D + part * COLS;
+#pragma unroll
+    for (int d = 0; d < COLS; d += 4) {
+      float4 x = *reinterpret_cast<const float4*>(p + d);
+      acc[d] += x.x; acc[d + 1] += x.y; acc[d + 2] += x.z; acc[d + 3] += x.w;
+    }
+  }
+  const size_t base = ((size_t)(g.qs + qi) * H + h) * D + part * COLS;
+#pragma unroll
+  for (int d = 0; d < COLS; d += 4)
+    store4(dq, base + d, acc[d] * scale, acc[d + 1] * scale, acc[d + 2] * scale, acc[d + 3] * scale, grad_f32);
 }
 
 // Work queue of the dK/dV kernel. The items, in dispatch order, are dealt into kQueues queues:
@@ -1244,35 +1298,31 @@ void bwd_dkdv_kernel2(BwdArgs a) {
     dkdv_item2<ACT, BIASX, MK, NP>(*ap, sm, item, wave, claim, take);
     __syncthreads();
   }
+  // The fixed-order sums of split dQ pieces (written by the dQ kernel, which has finished) are taken
+  // here by the workgroups that run out of items first, in the time the others finish theirs.
+  __syncthreads();  // every wave has read the last next_item before it is reused
+  ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(ap));
+  const int n_red = ap->dq_reduce_n;
+  for (;;) {
+    if (threadIdx.x == 0)
+      next_item = n_red > 0 ? __hip_atomic_fetch_add(ap->kv_queue + kQueues, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : 0;
+    __syncthreads();
+    const int gi = __builtin_amdgcn_readfirstlane(next_item);
+    __syncthreads();  // everyone has read next_item before it is written again
+    if (gi >= n_red) break;
+    reduce_dq_group<128, NP * 128>(load_group(ap->dq_groups, gi), ap->part_dq, ap->dq, ap->H, ap->scale, ap->grad_f32,
+                                   threadIdx.x);
+  }
 }
 
 // ---------------------------------------------------------------- fixed-order partial sums
-// One workgroup per split group (b, h, tile, slot0, R); 2 threads per row, D/2 columns each.
+// One workgroup per split group.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_dq_kernel(BwdArgs a) {
-  constexpr int BM = kDqBM, HALF = D / 2;
-  const WorkRec g = load_group(a.dq_groups, blockIdx.x);
-  const int h = g.h, t = g.tile, slot0 = g.lo, R = g.hi;
-  const int qs = g.qs, Lq = g.Lq;
-  const int row = threadIdx.x >> 1, part = threadIdx.x & 1;
-  const int qi = t * BM + row;
-  if (qi >= Lq) return;
-  float acc[HALF];
-#pragma unroll
-  for (int d = 0; d < HALF; ++d) acc[d] = 0.0f;
-  for (int r = 0; r < R; ++r) {
-    const float* p = a.part_dq + ((size_t)(slot0 + r) * BM + row) * D + part * HALF;
-#pragma unroll
-    for (int d = 0; d < HALF; d += 4) {
-      float4 x = *reinterpret_cast<const float4*>(p + d);
-      acc[d] += x.x; acc[d + 1] += x.y; acc[d + 2] += x.z; acc[d + 3] += x.w;
-    }
-  }
-  const size_t base = ((size_t)(qs + qi) * a.H + h) * D + part * HALF;
-  const float sc = a.scale;
-#pragma unroll
-  for (int d = 0; d < HALF; d += 4)
-    store4(a.dq, base + d, acc[d] * sc, acc[d + 1] * sc, acc[d + 2] * sc, acc[d + 3] * sc, a.grad_f32);
+  reduce_dq_group<D, 256>(load_group(a.dq_groups, blockIdx.x), a.part_dq, a.dq, a.H, a.scale, a.grad_f32,
+                          threadIdx.x);
 }
 
 template <int D>
@@ -1315,7 +1365,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_dkdv_kernel(BwdArgs a) {
 __global__ __launch_bounds__(256) void bwd_dbias_clear_kernel(BwdArgs a, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n && a.dbias_acc) a.dbias_acc[i] = 0ull;
-  if (i < kQueues && a.kv_queue) a.kv_queue[i] = 0;  // for backward passes with no dQ items
+  if (i < kQueueCounters && a.kv_queue) a.kv_queue[i] = 0;  // for backward passes with no dQ items
 }
 
 __global__ __launch_bounds__(256) void bwd_dbias_finish_kernel(BwdArgs a, int n) {
@@ -1419,7 +1469,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n, int resident
 
 hipError_t launch_bwd_dbias_clear(const BwdArgs& a, const Modes& m, hipStream_t s) {
   const int n = a.dbias_acc ? a.H * (m.bias == kBiasBucket ? kDbiasBins : 1) : 0;
-  const int threads = std::max(n, kQueues);
+  const int threads = std::max(n, kQueueCounters);
   hipLaunchKernelGGL(bwd_dbias_clear_kernel, dim3((threads + 255) / 256), dim3(256), 0, s, a, n);
   return hipGetLastError();
 }

@@ -436,7 +436,7 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   P->off_dbias = o;  // fixed-point bias-gradient totals, used when the caller asks for dbias
   if (P->modes.bias != kBiasNone) o += align256((size_t)P->H * (P->modes.bias == kBiasBucket ? kBuckets : 1) * 8);
   P->off_queue = o;
-  if (P->D == 128) o += align256(kQueues * 4);
+  if (P->D == 128) o += align256(kQueueCounters * 4);
   P->ws_bwd = o;
   if (P->lists[kFwd].nslots == 0) P->ws_fwd = 0;
 
@@ -612,8 +612,13 @@ jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* 
   // dQ first: it also computes Delta = rowsum(dO * O) (softmax) for the dK/dV kernel.
   st = timed(P, 4, s, [&] { return launch_bwd_dq(a, m, (int)P->lists[kDq].n_items(), s); }, "dQ launch");
   if (st != JFA_OK) return st;
-  if (P->lists[kDq].n_groups() > 0) {
-    st = timed(P, 5, s, [&] { return launch_bwd_reduce_dq(a, m, (int)P->lists[kDq].n_groups(), s); }, "dQ reduce launch");
+  // The persistent dK/dV kernel (D = 128, full-width items) takes the dQ partial sums once its items
+  // are exhausted; otherwise a reduce kernel does.
+  const int dq_groups = (int)P->lists[kDq].n_groups();
+  const bool dq_in_kv = P->D == 128 && !P->modes.kv_short && a.kv_n > 0 && dq_groups > 0;
+  a.dq_reduce_n = dq_in_kv ? dq_groups : 0;
+  if (dq_groups > 0 && !dq_in_kv) {
+    st = timed(P, 5, s, [&] { return launch_bwd_reduce_dq(a, m, dq_groups, s); }, "dQ reduce launch");
     if (st != JFA_OK) return st;
   }
   st = timed(P, 3, s, [&] { return launch_bwd_dkdv(a, m, a.kv_n, P->kv_resident, s); }, "dK/dV launch");

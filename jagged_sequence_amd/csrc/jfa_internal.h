@@ -26,8 +26,10 @@ constexpr int kThreads = 256;
 constexpr int kItemInts = 16;
 constexpr int kGroupInts = 16;
 constexpr int kBuckets = 64;
-// Work queues of the persistent dK/dV kernel (D = 128): one per XCD.
+// Work queues of the persistent dK/dV kernel (D = 128): one per XCD, then one counter of the dQ
+// partial-sum tasks that the same kernel takes once its items are exhausted.
 constexpr int kQueues = 8;
+constexpr int kQueueCounters = kQueues + 1;
 
 enum Act { kSoftmax = 0, kSilu = 1, kGeluTanh = 2 };
 // Mask template argument of the attention kernels. kMaskBand covers a window and / or a block
@@ -93,8 +95,9 @@ struct BwdArgs {
   int out_f32;
   int grad_f32;
   int kv_bn;  // keys per dK/dV item (kKvBN or kKvBNShort)
-  int* kv_queue;  // kQueues counters of the dK/dV work queue (D = 128); the dQ kernel zeroes them
+  int* kv_queue;  // kQueueCounters counters of the dK/dV work queue (D = 128); the dQ kernel zeroes them
   int kv_n;       // dK/dV items
+  int dq_reduce_n;  // dQ split groups whose fixed-order sums the persistent dK/dV kernel takes (else 0)
   Band band;
 };
 

@@ -166,3 +166,29 @@ def test_short_query_items_split():
     assert g1["plan"].info()["kv_bn"] == 64 and len(g1["plan"].schedule(5)) == 0
     assert len(g1["plan"].schedule(1)) > 0 and len(g1["plan"].schedule(3)) > 0
     compare(x, g1, oracle(x))
+
+
+# bf16 gradients at D = 128: the dK/dV kernel stages its output rows through LDS on this path.
+BF16_GRAD_CASES = [("causal", "softmax", "bucket", False), ("none", "softmax", "scalar", False),
+                   ("causal", "silu", "none", False), ("none", "gelu_tanh", "bucket", False),
+                   ("none", "softmax", "bucket", True)]
+
+
+@pytest.mark.parametrize("mask,act,bias,short", BF16_GRAD_CASES, ids=["-".join(map(str, c)) for c in BF16_GRAD_CASES])
+def test_bf16_gradients_d128(mask, act, bias, short):
+    if short:
+        lq, lkv = SHORT_Q, SHORT_KV
+    else:
+        lq, lkv = (SELF_LENS, SELF_LENS) if mask == "causal" else (CROSS_Q, CROSS_KV)
+    x = ji.make_inputs(lq, lkv, 2, 128, wid=47, mask=mask, act=act, bias_kind=bias, bias_sigma=0.5)
+    say(f"case bf16 grads mask={mask} act={act} bias={bias} short={short}")
+    gpu = run_gpu(x, grad_dtype="bf16")
+    assert gpu["dk"].dtype == torch.bfloat16
+    assert gpu["plan"].info()["kv_bn"] == (64 if short else 128)
+    rep = compare(x, gpu, oracle(x))
+    # the same kernels with fp32 gradients: bf16 rounding of each element is the only difference
+    g32 = run_gpu(x)
+    for name in ["dq", "dk", "dv"]:
+        a, b = to_np(gpu[name]), to_np(g32[name])
+        assert np.all(np.abs(a - b) <= 2.0 ** -8 * np.abs(b) + 1e-30), name
+    say(f"  {rep}")
