@@ -459,7 +459,15 @@ void bwd_dq_kernel2(BwdArgs a) {
     if (kt + 1 < k1) tile(kt + 1, std::integral_constant<int, 1>{});
   }
 
-  if (slot < 0) {
+  if (slot < 0 && !a.grad_f32) {
+    // bf16 rows through the ring stage that the last tile did not use (every wave finished reading
+    // it before the last tile's barrier, and no load went into it since): 8 KB per wave.
+    const int free_st = ((k1 - 1 - k0) & 1) ^ 1;
+    char* dst = static_cast<char*>(a.dq);
+    const int H = a.H;
+    store_rows_staged(&sm.kv[free_st][0][0] + wave * (32 * kRowBytes), qacc, a.scale, lane, Lq - row0,
+                      [&](int r) { return dst + (((size_t)(qs + row0 + r) * H + h) * D) * 2; });
+  } else if (slot < 0) {
     if (qi < Lq) {
       const size_t base = ((size_t)(qs + qi) * a.H + h) * D;
       const float sc = a.scale;
@@ -1130,32 +1138,13 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
   // Accumulator register r of d-block db: dimension 32 db + 8 (r/4) + 4 hh + r%4, key kj.
   const float sc = isB ? a.scale : 1.0f;
   if (slot < 0 && !a.grad_f32) {
-    // bf16 rows go out through LDS: each lane holds 4-element pieces of 16 rows' columns, so a direct
-    // store would touch 32 rows with 16 bytes each; staged, a store writes 4 whole 256-byte rows.
-    // Once every wave is past the last tile the Q / dO ring is free: 8 KB per wave (32 rows x 128
-    // bf16); the 16-byte chunk c of row r sits at c ^ (r & 15), so neither side conflicts.
+    // bf16 rows go out through LDS as whole rows. Once every wave is past the last tile the Q / dO
+    // ring is free: 8 KB per wave.
     __syncthreads();
-    unsigned char* stg = &sm.qg[0][0][0] + wave * (32 * kRowBytes);
-    const int r = le & 31;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = 4 * db + g;
-        *reinterpret_cast<uint2*>(stg + r * kRowBytes + ((c ^ (r & 15)) << 4) + 8 * hhe) =
-            make_uint2(pack2_bf16(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc),
-                       pack2_bf16(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc));
-      }
-    wave_lds_fence();
     char* dst = static_cast<char*>(isB ? a.dk : a.dv);
-    const int cc = le & 15;
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int row = 4 * it + (le >> 4);
-      const uint4 x = *reinterpret_cast<const uint4*>(stg + row * kRowBytes + ((cc ^ (row & 15)) << 4));
-      if (key_w + row < Lkv)
-        *reinterpret_cast<uint4*>(dst + (((size_t)(ks + key_w + row) * a.H + h) * D) * 2 + cc * 16) = x;
-    }
+    const int H = a.H;
+    store_rows_staged(&sm.qg[0][0][0] + wave * (32 * kRowBytes), acc, sc, le, Lkv - key_w,
+                      [&](int r) { return dst + (((size_t)(ks + key_w + r) * H + h) * D) * 2; });
   } else if (slot < 0) {
     if (kje < Lkv) {
       void* dst = isB ? a.dk : a.dv;

@@ -444,7 +444,19 @@ void fwd_kernel2(FwdArgs a) {
     inv = (slot < 0 && Lkv > 0) ? 1.0f / (float)Lkv : 1.0f;
   }
   if (slot < 0) {
-    if (qi < Lq) {
+    if (qi < Lq && SOFTMAX && hh == 0)
+      a.lse[(size_t)h * a.Tq + qs + qi] =
+          l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 + (BIAS == kBiasScalar ? bias_c : 0.0f) : kNegInf;
+    if (!a.out_f32) {
+      // bf16 rows through the ring stage that the last tile did not use (every wave finished reading
+      // it before the last tile's barrier, and no load went into it since): 8 KB per wave. Each lane
+      // scales its row by its own 1 / l.
+      const int free_st = ((k1 - 1 - k0) & 1) ^ 1;
+      char* dst = static_cast<char*>(a.out);
+      const int H = a.H;
+      store_rows_staged(&sm.kv[free_st][0][0] + wave * (32 * kRowBytes), o, inv, lane, Lq - row0,
+                        [&](int r) { return dst + (((size_t)(qs + row0 + r) * H + h) * D) * 2; });
+    } else if (qi < Lq) {
       const size_t base = ((size_t)(qs + qi) * a.H + h) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -452,9 +464,6 @@ void fwd_kernel2(FwdArgs a) {
         for (int g = 0; g < 4; ++g)
           store4(a.out, base + 32 * db + 8 * g + 4 * hh, o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
                  o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv, a.out_f32);
-      if (SOFTMAX && hh == 0)
-        a.lse[(size_t)h * a.Tq + qs + qi] =
-            l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 + (BIAS == kBiasScalar ? bias_c : 0.0f) : kNegInf;
     }
   } else {
     const int prow = wave * 32 + l32;

@@ -133,4 +133,33 @@ __device__ __forceinline__ bf16x8 lds_read_tr(const unsigned char* tile, uint32_
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Stores a wave's 32-row x 128-column tile, held in the MFMA accumulator layout (lane l: row l % 32;
+// register r of block db: column 32 db + 8 (r / 4) + 4 (l / 32) + r % 4), as bf16 rows through an
+// 8 KB LDS area `stg` that no other wave uses meanwhile. Held directly, a lane owns 4-column pieces
+// of its row, so a store instruction would touch 32 rows with 16 bytes each; staged, each store
+// writes 4 whole 256-byte rows. The 16-byte chunk c of row r sits at c ^ (r & 15), which keeps both
+// the writes and the reads free of bank conflicts. Row r (< nrows) goes to row_ptr(r).
+template <class RowPtr>
+__device__ __forceinline__ void store_rows_staged(unsigned char* stg, const f32x16 (&acc)[4], float mul, int lane,
+                                                  int nrows, RowPtr row_ptr) {
+  const int r = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 4 * db + g;
+      *reinterpret_cast<uint2*>(stg + r * kRowBytes + ((c ^ (r & 15)) << 4) + 8 * hh) =
+          make_uint2(pack2_bf16(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
+                     pack2_bf16(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul));
+    }
+  wave_lds_fence();
+  const int cc = lane & 15;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int row = 4 * it + (lane >> 4);
+    const uint4 x = *reinterpret_cast<const uint4*>(stg + row * kRowBytes + ((cc ^ (row & 15)) << 4));
+    if (row < nrows) *reinterpret_cast<uint4*>(row_ptr(row) + cc * 16) = x;
+  }
+}
+
 }  // namespace jfa
