@@ -482,60 +482,92 @@ void fwd_kernel2(FwdArgs a) {
 // Merge the pieces of split items in fixed order r = 0..R-1:
 //   softmax: lse* = log2 sum_r 2^lse_r,  O = sum_r 2^(lse_r - lse*) O_r   (O_r normalised per piece)
 //   GDPA:    O = (sum_r O_r) / Lkv
+// The kernel is a chain of dependent memory round trips (record, pieces, output), so everything a
+// thread needs is requested up front: the log-sum-exps of up to kCombinePre pieces and the rows of
+// the first two pieces, before any arithmetic.
+constexpr int kCombineThreads = 512;  // 4 threads per row
+constexpr int kCombinePre = 8;
+
 template <int D, int ACT, int BIAS>
-__global__ __launch_bounds__(256) void fwd_combine_kernel(FwdArgs a) {
-  constexpr int BM = kFwdBM;
+__global__ __launch_bounds__(kCombineThreads) void fwd_combine_kernel(FwdArgs a) {
+  constexpr int BM = kFwdBM, TPR = kCombineThreads / BM, COLS = D / TPR, NC = COLS / 4;
   constexpr bool SOFTMAX = ACT == kSoftmax;
   const WorkRec g = load_group(a.groups, blockIdx.x);
   const int h = g.h, t = g.tile, slot0 = g.lo, R = g.hi;
   const int qs = g.qs, Lq = g.Lq, Lkv = g.Lkv;
-  const int row = threadIdx.x >> 1, part = threadIdx.x & 1;
+  const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
   const int qi = t * BM + row;
   if (qi >= Lq) return;
-  constexpr int HALF = D / 2;
-  float acc[HALF];
+  const size_t stride = (size_t)BM * D;
+  const float* p0 = a.part_o + ((size_t)slot0 * BM + row) * D + part * COLS;
+  float4 x0[NC], x1[NC];
 #pragma unroll
-  for (int d = 0; d < HALF; ++d) acc[d] = 0.0f;
+  for (int c = 0; c < NC; ++c) x0[c] = *reinterpret_cast<const float4*>(p0 + 4 * c);
+  if (R > 1) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) x1[c] = *reinterpret_cast<const float4*>(p0 + stride + 4 * c);
+  }
+  const float* pl = a.part_lse + (size_t)slot0 * BM + row;
+  float lp[kCombinePre];  // indexed with unrolled (constant) r only
+  if (SOFTMAX) {
+#pragma unroll
+    for (int r = 0; r < kCombinePre; ++r) {
+      lp[r] = kNegInf;
+      if (r < R) lp[r] = pl[(size_t)r * BM];
+    }
+  }
+
+  float acc[COLS];
+#pragma unroll
+  for (int d = 0; d < COLS; ++d) acc[d] = 0.0f;
+  auto add = [&](const float4 (&x)[NC], float w) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      acc[4 * c] += w * x[c].x;
+      acc[4 * c + 1] += w * x[c].y;
+      acc[4 * c + 2] += w * x[c].z;
+      acc[4 * c + 3] += w * x[c].w;
+    }
+  };
+  auto add_piece = [&](int r, float w) {
+    if (r == 0) {
+      add(x0, w);
+    } else if (r == 1) {
+      add(x1, w);
+    } else {
+      float4 x[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) x[c] = *reinterpret_cast<const float4*>(p0 + (size_t)r * stride + 4 * c);
+      add(x, w);
+    }
+  };
   float lse2 = kNegInf;
   if (SOFTMAX) {
     float mx = kNegInf;
-    for (int r = 0; r < R; ++r) mx = fmaxf(mx, a.part_lse[(size_t)(slot0 + r) * BM + row]);
+#pragma unroll
+    for (int r = 0; r < kCombinePre; ++r) mx = fmaxf(mx, lp[r]);
+    for (int r = kCombinePre; r < R; ++r) mx = fmaxf(mx, pl[(size_t)r * BM]);
     if (mx != kNegInf) {
       float sum = 0.0f;
-      for (int r = 0; r < R; ++r) sum += fast_exp2(a.part_lse[(size_t)(slot0 + r) * BM + row] - mx);
-      lse2 = mx + fast_log2(sum);
-      for (int r = 0; r < R; ++r) {
-        const float w = fast_exp2(a.part_lse[(size_t)(slot0 + r) * BM + row] - lse2);
-        const float* po = a.part_o + ((size_t)(slot0 + r) * BM + row) * D + part * HALF;
 #pragma unroll
-        for (int d = 0; d < HALF; d += 4) {
-          float4 x = *reinterpret_cast<const float4*>(po + d);
-          acc[d] += w * x.x;
-          acc[d + 1] += w * x.y;
-          acc[d + 2] += w * x.z;
-          acc[d + 3] += w * x.w;
-        }
-      }
+      for (int r = 0; r < kCombinePre; ++r)
+        if (r < R) sum += fast_exp2(lp[r] - mx);
+      for (int r = kCombinePre; r < R; ++r) sum += fast_exp2(pl[(size_t)r * BM] - mx);
+      lse2 = mx + fast_log2(sum);
+#pragma unroll
+      for (int r = 0; r < kCombinePre; ++r)
+        if (r < R) add_piece(r, fast_exp2(lp[r] - lse2));
+      for (int r = kCombinePre; r < R; ++r) add_piece(r, fast_exp2(pl[(size_t)r * BM] - lse2));
     }
   } else {
-    for (int r = 0; r < R; ++r) {
-      const float* po = a.part_o + ((size_t)(slot0 + r) * BM + row) * D + part * HALF;
-#pragma unroll
-      for (int d = 0; d < HALF; d += 4) {
-        float4 x = *reinterpret_cast<const float4*>(po + d);
-        acc[d] += x.x;
-        acc[d + 1] += x.y;
-        acc[d + 2] += x.z;
-        acc[d + 3] += x.w;
-      }
-    }
+    for (int r = 0; r < R; ++r) add_piece(r, 1.0f);
     const float inv = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
 #pragma unroll
-    for (int d = 0; d < HALF; ++d) acc[d] *= inv;
+    for (int d = 0; d < COLS; ++d) acc[d] *= inv;
   }
-  const size_t base = ((size_t)(qs + qi) * a.H + h) * D + part * HALF;
+  const size_t base = ((size_t)(qs + qi) * a.H + h) * D + part * COLS;
 #pragma unroll
-  for (int d = 0; d < HALF; d += 4) store4(a.out, base + d, acc[d], acc[d + 1], acc[d + 2], acc[d + 3], a.out_f32);
+  for (int d = 0; d < COLS; d += 4) store4(a.out, base + d, acc[d], acc[d + 1], acc[d + 2], acc[d + 3], a.out_f32);
   if (SOFTMAX && part == 0)
     a.lse[(size_t)h * a.Tq + qs + qi] =
         lse2 == kNegInf ? kNegInf : lse2 * kLn2 + (BIAS == kBiasScalar ? a.bias[h] : 0.0f);
@@ -580,9 +612,9 @@ hipError_t fwd_launch_a(const FwdArgs& a, const Modes& m, int n, hipStream_t s) 
 template <int D, int ACT>
 hipError_t comb_launch_b(const FwdArgs& a, const Modes& m, int n, hipStream_t s) {
   if (m.bias == kBiasScalar)
-    hipLaunchKernelGGL((fwd_combine_kernel<D, ACT, kBiasScalar>), dim3(n), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((fwd_combine_kernel<D, ACT, kBiasScalar>), dim3(n), dim3(kCombineThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_combine_kernel<D, ACT, kBiasNone>), dim3(n), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((fwd_combine_kernel<D, ACT, kBiasNone>), dim3(n), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }
 

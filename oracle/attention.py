@@ -275,3 +275,42 @@ def gdpa_magnitude(q, k, v, q_off, kv_off, *, mask="none", act="silu", bias_kind
                 out[qs + i0:qs + i1, h] = (Aa @ V) / lkv if lkv > 0 else 0.0
     return out
 
+
+
+def rows(q, k, v, q_off, kv_off, b, h, rows_, dout=None, *, mask="none", act="softmax", bias_kind="none", bias=None,
+         window=0, block=0, scale: Optional[float] = None):
+    """Output, log-sum-exp (softmax) and, given ``dout``, dQ of selected query rows of one sequence and
+    head, each from its own score row against all the sequence's keys.
+
+    The same definition as :func:`forward` and :func:`backward`, evaluated one query row at a time, so
+    that single outputs of very long sequences can be checked without the whole score matrix. Returns
+    ``(out [n, D], lse [n] or None, dq [n, D] or None)``.
+    """
+    q_off, kv_off = _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias, window, block)
+    D = q.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    qs, ks, ke = q_off[b], kv_off[b], kv_off[b + 1]
+    lkv = ke - ks
+    K, V = k[ks:ke, h], v[ks:ke, h]
+    bias_h = None if bias is None else np.asarray(bias, dtype=np.float64)[h]
+    n = len(rows_)
+    out, lse = np.zeros((n, D)), (np.zeros(n) if act == "softmax" else None)
+    dq = None if dout is None else np.zeros((n, D))
+    for r, i in enumerate(rows_):
+        S, vis, _ = _scores(q[qs + i:qs + i + 1, h], K, i, scale, mask, bias_kind, bias_h, window, block)
+        if act == "softmax":
+            P, l = _softmax_rows(S, vis)
+            out[r], lse[r] = (P @ V)[0], l[0]
+            if dout is not None:
+                dP = dout[qs + i:qs + i + 1, h] @ V.T
+                dS = P * (dP - (P * dP).sum())
+                dq[r] = scale * (dS @ K)[0]
+        else:
+            f, fprime = _ACTS[act]
+            inv_l = 1.0 / lkv if lkv > 0 else 0.0
+            out[r] = (np.where(vis, f(S), 0.0) @ V)[0] * inv_l
+            if dout is not None:
+                dS = np.where(vis, (dout[qs + i:qs + i + 1, h] @ V.T) * inv_l * fprime(S), 0.0)
+                dq[r] = scale * (dS @ K)[0]
+    return out, lse, dq

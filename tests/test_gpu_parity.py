@@ -192,3 +192,71 @@ def test_bf16_gradients_d128(mask, act, bias, short):
         a, b = to_np(gpu[name]), to_np(g32[name])
         assert np.all(np.abs(a - b) <= 2.0 ** -8 * np.abs(b) + 1e-30), name
     say(f"  {rep}")
+
+
+def _sub_inputs(x, seqs):
+    """The listed sequences of a batch as a batch of their own, with their rows in the full layout."""
+    import dataclasses
+    qr = np.concatenate([np.arange(x.q_off[b], x.q_off[b + 1]) for b in seqs])
+    kr = np.concatenate([np.arange(x.kv_off[b], x.kv_off[b + 1]) for b in seqs])
+    sub = dataclasses.replace(x, q=x.q[qr], k=x.k[kr], v=x.v[kr], do=x.do[qr],
+                              q_off=ji.offsets(np.diff(x.q_off)[seqs]), kv_off=ji.offsets(np.diff(x.kv_off)[seqs]))
+    return sub, torch.from_numpy(qr).cuda(), torch.from_numpy(kr).cuda()
+
+
+def test_full_size_longtail_max_length():
+    """The long-tail workload at full size (B = 512, two sequences of 32,768 tokens) in the benchmark's
+    launch configuration. Whole short sequences go to the oracle; for the 32,768-token sequences the
+    oracle evaluates sampled query rows one by one (output, lse, dQ), and dK / dV are checked through
+    identities that hold at any size: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per head."""
+    from oracle import attention as A
+    from tests.gpu_util import LSE_MAX_ABS, OUT_MAX_ABS, rel_l2
+    name = "longtail"
+    w = ji.WORKLOADS[name]
+    x = ji.workload_inputs(name)
+    lq, _ = ji.lengths(w)
+    short = [int(b) for b in np.argsort(lq, kind="stable")[:1]] + [int(b) for b in np.flatnonzero(lq <= 2048)[[5, 77]]]
+    longest = [int(b) for b in np.flatnonzero(lq == lq.max())]
+    say(f"case workload {name} full size; short seqs {short}, longest {longest}")
+    gpu = run_gpu(x, out_dtype="bf16", grad_dtype="bf16")
+    sub, qr, kr = _sub_inputs(x, short)
+    g_sub = {"out": gpu["out"][qr], "lse": gpu["lse"][:, qr], "dq": gpu["dq"][qr], "dk": gpu["dk"][kr],
+             "dv": gpu["dv"][kr]}
+    rep = compare(sub, g_sub, oracle(sub), out_bf16=True, plain=True)
+    say(f"  short sequences {rep}")
+    f = A.bf16_bits_to_f64
+    kw = dict(mask=w.mask, act=w.act, bias_kind=w.bias, bias=x.bias.astype(np.float64))
+    for b in longest:
+        L = int(lq[b])
+        qs, ks = int(x.q_off[b]), int(x.kv_off[b])
+        q, k, v, do = (f(t[s:s + L]) for t, s in [(x.q, qs), (x.k, ks), (x.v, ks), (x.do, qs)])
+        off = np.array([0, L], dtype=np.int32)
+        # Rows drawn uniformly, plus the first and last ones: the sample's rel-L2 of dQ estimates that of
+        # the whole sequence, which is what the gradient bound is stated for. (A row with two visible
+        # keys alone can be off by several percent: Delta = dO . O uses the stored bf16 output and
+        # dP - Delta cancels there; whole short sequences, which contain such rows, are checked above.)
+        rng = np.random.default_rng(b)
+        sel = sorted({0, 1, 2, L - 1} | set(rng.choice(L, 60, replace=False).tolist()))
+        uniform = [r for r, i in enumerate(sel) if i not in (1, 2)]
+        rows = [qs + i for i in sel]
+        for h in (0, w.H - 1):
+            o, l, g = A.rows(q, k, v, off, off, 0, h, sel, do, **kw)
+            og = gpu["out"][rows, h].float().cpu().numpy().astype(np.float64)
+            lg = gpu["lse"][h, rows].cpu().numpy().astype(np.float64)
+            gg = gpu["dq"][rows, h].float().cpu().numpy().astype(np.float64)
+            bound = OUT_MAX_ABS + np.exp2(np.floor(np.log2(np.maximum(np.abs(o), 1e-30))) - 8)
+            assert np.all(np.abs(og - o) <= bound), (b, h, np.abs(og - o).max())
+            assert np.abs(lg - l).max() <= LSE_MAX_ABS, (b, h, np.abs(lg - l).max())
+            err = rel_l2(gg[uniform], g[uniform])
+            assert err <= 2e-2, (b, h, err)
+            say(f"  seq {b} head {h}: out max-abs {np.abs(og - o).max():.2e}, lse {np.abs(lg - l).max():.2e}, "
+                f"dQ rel-L2 (sampled rows) {err:.2e}")
+        dk = gpu["dk"][ks:ks + L].double()
+        dv = gpu["dv"][ks:ks + L].double()
+        dO = torch.from_numpy(do).to(dk.device)
+        for hh in range(w.H):
+            s_dk = dk[:, hh].sum(0).norm().item()
+            assert s_dk <= 1e-3 * dk[:, hh].norm(dim=1).sum().item(), (b, hh, s_dk)
+            err = (dv[:, hh].sum(0) - dO[:, hh].sum(0)).norm().item()
+            assert err <= 1e-2 * dO[:, hh].sum(0).norm().item(), (b, hh, err)
+    say("  longest sequences: sampled rows and gradient identities within bounds")

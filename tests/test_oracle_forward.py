@@ -230,3 +230,25 @@ def test_gdpa_magnitude_bounds_output():
     out, _ = A.forward(q0, k, va, x.q_off, x.kv_off, act="gelu_tanh", bias_kind="scalar", bias=c)
     mag = A.gdpa_magnitude(q0, k, va, x.q_off, x.kv_off, act="gelu_tanh", bias_kind="scalar", bias=c)
     np.testing.assert_allclose(mag, out, rtol=1e-14)
+
+
+@pytest.mark.parametrize("act", ["softmax", "silu", "gelu_tanh"])
+@pytest.mark.parametrize("mask,window", [("causal", 0), ("none", 0), ("causal", 9)])
+def test_row_by_row_equals_whole_batch(act, mask, window):
+    """oracle.rows (one score row at a time) reproduces forward / backward on the same rows."""
+    import jfa_inputs as ji
+    lens = [30, 1, 45]
+    x = ji.make_inputs(lens, lens, 2, 8, wid=61, mask=mask, act=act, bias_kind="bucket", bias_sigma=0.7,
+                       window=window)
+    f = A.bf16_bits_to_f64
+    q, k, v, do = f(x.q), f(x.k), f(x.v), f(x.do)
+    kw = dict(mask=mask, act=act, bias_kind="bucket", bias=x.bias.astype(np.float64), window=window)
+    out, lse = A.forward(q, k, v, x.q_off, x.kv_off, **kw)
+    dq, _, _, _ = A.backward(q, k, v, x.q_off, x.kv_off, do, **kw)
+    for b, h, sel in [(0, 1, [0, 7, 29]), (2, 0, [44, 3]), (1, 1, [0])]:
+        o, l, g = A.rows(q, k, v, x.q_off, x.kv_off, b, h, sel, do, **kw)
+        idx = [x.q_off[b] + i for i in sel]
+        np.testing.assert_allclose(o, out[idx, h], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(g, dq[idx, h], rtol=1e-10, atol=1e-12)
+        if act == "softmax":
+            np.testing.assert_allclose(l, lse[h, idx], rtol=1e-12, atol=1e-12)
