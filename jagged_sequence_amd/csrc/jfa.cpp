@@ -18,7 +18,6 @@
 #include <cstring>
 #include <new>
 #include <string>
-#include <map>
 #include <vector>
 
 #include "jfa.h"
@@ -108,25 +107,39 @@ void finish(const std::vector<Raw>& raw, int slots, bool split, List& out) {
 // Longest groups first keeps the longest-first dispatch of the list within each XCD.
 constexpr int kXcds = 8;
 
-std::vector<int> dispatch_order(const List& L) {
+std::vector<int> dispatch_order(const List& L, int B, int H) {
+  // Dense per-group arrays (group id b * H + h, ascending in (b, h)) and counting sorts keep this
+  // linear in the items apart from one sort of the groups.
   const size_t n = L.n_items();
-  std::map<std::pair<int, int>, int64_t> cost;
-  for (size_t i = 0; i < n; ++i) cost[{L.items[i * 6], L.items[i * 6 + 1]}] += L.items[i * 6 + 4] - L.items[i * 6 + 3];
-  std::vector<std::pair<std::pair<int, int>, int64_t>> gs(cost.begin(), cost.end());  // (b, h) ascending
-  std::stable_sort(gs.begin(), gs.end(), [](const auto& x, const auto& y) { return x.second > y.second; });
-  std::map<std::pair<int, int>, std::pair<int, int>> where;  // (b, h) -> (xcd, rank)
+  const size_t G = (size_t)B * H;
+  std::vector<int64_t> cost(G, 0);
+  std::vector<int> count(G, 0);
+  for (size_t i = 0; i < n; ++i) {
+    const size_t g = (size_t)L.items[i * 6] * H + L.items[i * 6 + 1];
+    cost[g] += L.items[i * 6 + 4] - L.items[i * 6 + 3];
+    ++count[g];
+  }
+  std::vector<int> gs;  // groups with at least one item, longest first, then (b, h) ascending
+  for (size_t g = 0; g < G; ++g)
+    if (count[g]) gs.push_back((int)g);
+  std::stable_sort(gs.begin(), gs.end(), [&](int x, int y) { return cost[x] > cost[y]; });
+  std::vector<int> xcd_of(G, 0);
   std::vector<int64_t> load(kXcds, 0);
-  for (size_t g = 0; g < gs.size(); ++g) {
+  for (int g : gs) {
     int x = 0;
     for (int y = 1; y < kXcds; ++y)
       if (load[y] < load[x]) x = y;
-    where[gs[g].first] = {x, (int)g};
-    load[x] += gs[g].second;
+    xcd_of[g] = x;
+    load[x] += cost[g];
   }
+  // items of each group in list order (counting sort by group)
+  std::vector<int> start(G + 1, 0);
+  for (size_t g = 0; g < G; ++g) start[g + 1] = start[g] + count[g];
+  std::vector<int> by_group(n), fill(start.begin(), start.end() - 1);
+  for (size_t i = 0; i < n; ++i) by_group[fill[(size_t)L.items[i * 6] * H + L.items[i * 6 + 1]]++] = (int)i;
+  // XCD x's queue: its groups in rank order, each group's items in list order
   std::vector<std::vector<int>> q(kXcds);
-  for (size_t i = 0; i < n; ++i) q[where[{L.items[i * 6], L.items[i * 6 + 1]}].first].push_back((int)i);
-  auto rank = [&](int i) { return where[{L.items[(size_t)i * 6], L.items[(size_t)i * 6 + 1]}].second; };
-  for (auto& v : q) std::stable_sort(v.begin(), v.end(), [&](int x, int y) { return rank(x) < rank(y); });
+  for (int g : gs) q[xcd_of[g]].insert(q[xcd_of[g]].end(), by_group.begin() + start[g], by_group.begin() + start[g + 1]);
   std::vector<size_t> head(kXcds, 0);
   std::vector<int> order;
   order.reserve(n);
@@ -417,7 +430,7 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   query_tile_list(lq, lkv, P->H, lim, kFwdBM, kFwdBN, slots[kFwd], split, P->lists[kFwd]);
   query_tile_list(lq, lkv, P->H, lim, kDqBM, kDqBN, slots[kDq], split, P->lists[kDq]);
   key_tile_list(lq, lkv, P->H, lim, kKvBM, P->kv_bn, slots[kKv], split, P->lists[kKv]);
-  for (auto& L : P->lists) L.order = dispatch_order(L);
+  for (auto& L : P->lists) L.order = dispatch_order(L, P->B, P->H);
 
   // workspace layout
   const size_t D = P->D;
