@@ -750,7 +750,7 @@ struct alignas(16) KvSmem2<false, GDPA, NP> {
 // are reached through a wave-uniform base offset.
 template <bool GDPA, int NP>
 struct alignas(16) KvSmem2<true, GDPA, NP> {
-  static constexpr int NPG = GDPA ? 2 : 1;
+  static constexpr int NPG = 1;  // P (softmax) or act'/Lkv (GDPA; A parks its own P in the next buffer)
   float diag[NP][kDiagLen];  // first: the 8-byte pair reads of a lane's bias window share one base
   float tab[kBuckets];
   unsigned long long dbh[NP][kDbiasBins];
@@ -786,12 +786,13 @@ __device__ __forceinline__ void unpack8(uint4 w, float (&x)[8]) {
 // general; NP = 2 (64 keys, 4 waves, two workgroups per CU, about 75 KB of LDS) when every sequence
 // has a single query tile, where an item is one latency-bound pass and two resident workgroups
 // overlap one's loads with the other's work.
-// Softmax hands over P only, so a third ring stage and three hand-off buffers fit in LDS and one
-// barrier per query tile suffices; GDPA also hands over act'/Lkv and keeps two barriers per tile,
-// as does the short form (NP = 2), whose items have a single query tile.
+// With NP = 4 the hand-off carries one array per tile (P for softmax; act'/Lkv for GDPA, whose A
+// wave parks its own P in the next tile's buffer), so a third ring stage and three hand-off buffers fit in LDS
+// and one barrier per query tile suffices. The short form (NP = 2), whose items have a single query
+// tile, keeps two barriers per tile.
 template <int ACT, int NP>
 struct DkdvShape {
-  static constexpr bool ONEBAR = ACT == kSoftmax && NP == 4;
+  static constexpr bool ONEBAR = NP == 4;
   using Smem = KvSmem2<ONEBAR, ACT != kSoftmax, NP>;
 };
 
@@ -811,6 +812,11 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
   constexpr bool DBIAS = (BIASX & kBiasGrad) != 0;
   constexpr bool SOFTMAX = ACT == kSoftmax;
   constexpr bool ONEBAR = DkdvShape<ACT, NP>::ONEBAR;
+  // GDPA with one barrier per tile hands B only act'/Lkv (in buffer t % 3) and parks A's own P of
+  // tile t in buffer (t + 1) % 3: nobody reads that buffer between A's phase 1 of t and A's phase 2 of
+  // t (B read it for tile t - 2, before the barrier of tile t - 1), and A itself overwrites it with
+  // act'/Lkv of tile t + 1 only after phase 2 of t.
+  constexpr bool P_NEXT = ONEBAR && ACT != kSoftmax;
   constexpr bool CAUSAL = MK == kMaskCausal, BAND = MK == kMaskBand;
   using Smem = typename DkdvShape<ACT, NP>::Smem;
 
@@ -919,6 +925,7 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
   // ---- phase 1. A: S = Q K^T, probabilities, hand-off to B. B: dP = dO V^T.
   auto phase1 = [&](const int qt, auto st_tag, auto xb_tag, f32x16 (&pacc)[2]) {
     constexpr int ST = decltype(st_tag)::value, XB = decltype(xb_tag)::value;
+    constexpr int PB = P_NEXT ? (XB + 1) % 3 : XB;  // buffer of A's P
     const int qrow0 = qt * BM;
     const unsigned char* Qt = stage_ptr(st_tag, 0);
     const unsigned char* Gt = stage_ptr(st_tag, 1);
@@ -981,7 +988,7 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
                 if (!SOFTMAX) gv[j] = masked ? 0.0f : gv[j];
               }
             }
-            sm.xch[XB][pair][0][qb][c8][lane] = __builtin_bit_cast(uint4, pack8(pv));
+            sm.xch[PB][pair][0][qb][c8][lane] = __builtin_bit_cast(uint4, pack8(pv));
             if (!SOFTMAX) sm.xch[XB][pair][Smem::NPG - 1][qb][c8][lane] = __builtin_bit_cast(uint4, pack8(gv));
           }
         }
@@ -1005,6 +1012,7 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
   // ---- phase 2. A: dV += P^T dO (P read back from the hand-off buffer). B: dS, dK += dS^T Q.
   auto phase2 = [&](const int qt, auto st_tag, auto xb_tag, const f32x16 (&pacc)[2]) {
     constexpr int ST = decltype(st_tag)::value, XB = decltype(xb_tag)::value;
+    constexpr int PB = P_NEXT ? (XB + 1) % 3 : XB;  // buffer of A's P
     const int qrow0 = qt * BM;
     const unsigned char* Qt = stage_ptr(st_tag, 0);
     const unsigned char* Gt = stage_ptr(st_tag, 1);
@@ -1013,7 +1021,7 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int c8 = 0; c8 < 2; ++c8) {
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, sm.xch[XB][pair][0][qb][c8][lane]);
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, sm.xch[PB][pair][0][qb][c8][lane]);
           const uint32_t base = (uint32_t)((32 * qb + 16 * c8) * kRowBytes);
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
@@ -1026,9 +1034,10 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
         bf16x8 dsb[2];
 #pragma unroll
         for (int c8 = 0; c8 < 2; ++c8) {
-          float pv[8], dsv[8];
-          unpack8(sm.xch[XB][pair][0][qb][c8][lane], pv);
+          float dsv[8];
           if (SOFTMAX) {
+            float pv[8];
+            unpack8(sm.xch[XB][pair][0][qb][c8][lane], pv);
             const int rbase = 32 * qb + 16 * c8 + 8 * hh;
             const float* dl = sm.dlt[ST];
             const float4 y0 = *reinterpret_cast<const float4*>(&dl[rbase]);
