@@ -82,6 +82,13 @@ __device__ __forceinline__ int rel_bucket(int d) {
   return d < 16 ? d : (b < 63 ? b : 63);
 }
 
+// First distance of bucket u >= 16: 2^e + m 2^(e - 2) with e = 4 + (u - 16) / 4, m = (u - 16) % 4
+// (the inverse of rel_bucket on its logarithmic part; bucket 63 also takes every larger distance).
+__device__ __forceinline__ int rel_bucket_start(int u) {
+  const int e = 4 + ((u - 16) >> 2), m = (u - 16) & 3;
+  return (1 << e) + (m << (e - 2));
+}
+
 // Score activations for GDPA. sigma(z) = 1 / (1 + 2^(-z log2 e)); SiLU(x) = x sigma(x);
 // GELU_tanh(x) = x sigma(2u), u = sqrt(2/pi) (x + 0.044715 x^3), using 1 + tanh(u) = 2 sigma(2u).
 // Only the exp2 and reciprocal units are used, no tanh.
@@ -127,10 +134,6 @@ __device__ __forceinline__ void store4(void* base, size_t idx, float a, float b,
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Buffer resource over the rows of one (sequence, head) slice of a [T, H, D] bf16 tensor: `base`
-// points at row 0 of the slice, rows are `rs` elements apart and `rows` of them are valid. Loads
-// past the last valid row fall outside the resource's byte range and return zeros, so tails of
-// jagged sequences need no branch and never read a neighbouring sequence.
 // A work record (item or split group), read through the constant address space: the list is never
 // written while a kernel runs, and the promise lets the compiler fetch the record with scalar loads.
 struct WorkRec {
@@ -180,6 +183,10 @@ __device__ __forceinline__ int band_row_hi(int j, int Lq, Band b) {
   return hi;
 }
 
+// Buffer resource over the rows of one (sequence, head) slice of a [T, H, D] bf16 tensor: `base`
+// points at row 0 of the slice, rows are `rs` elements apart and `rows` of them are valid. Loads
+// past the last valid row fall outside the resource's byte range and return zeros, so tails of
+// jagged sequences need no branch and never read a neighbouring sequence.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const uint16_t* base, int rows, int rs, int D) {
   const uint32_t bytes = rows > 0 ? (uint32_t)((rows - 1) * rs + D) * 2u : 0u;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)bytes, 0x00020000);
@@ -247,6 +254,18 @@ struct DbiasLane {
     const int ulo = rel_bucket(d), uhi = rel_bucket(d + 7);
     if ((d >= 0 || d + 7 <= 0) && ulo == uhi) {
       add(bins, ulo, ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7])));
+    } else if (d >= 32) {
+      // Buckets are at least 8 wide from distance 32 on, so the run crosses exactly one bucket edge:
+      // distances below the first distance of bucket uhi go to ulo, the rest to uhi.
+      const int k = rel_bucket_start(uhi) - d;  // 1..7
+      float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lo += j < k ? v[j] : 0.0f;
+        hi += j < k ? 0.0f : v[j];
+      }
+      add(bins, ulo, lo);
+      add(bins, uhi, hi);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) add(bins, rel_bucket(d + j), v[j]);
