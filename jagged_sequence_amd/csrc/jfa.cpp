@@ -70,7 +70,9 @@ void finish(const std::vector<Raw>& raw, int slots, bool split, List& out) {
   int next = 0;
   for (const Raw& r : raw) {
     const int64_t cost = r.hi - r.lo;
-    if (split && cost > target) {
+    // With less than one tile of work per slot nothing is split: merging the pieces would cost a
+    // launch of its own, more than the tiles it saves.
+    if (split && total > s && cost > target) {
       const int64_t R = (cost + target - 1) / target;
       out.groups.insert(out.groups.end(), {r.b, r.h, r.t, next, (int32_t)R});
       for (int64_t k = 0; k < R; ++k)

@@ -28,8 +28,10 @@ B floor(c1 / B) + B - 1)]; the item covers the tiles from the one holding the lo
 the one holding the upper bound (none when the interval is empty: key tiles [0, 0), query tiles
 [lo, lo)). Without a window or block the rules above apply unchanged.
 splitting (both lists), given the number of concurrent workgroups ``slots``:
-  target = max(1, ceil(sum(cost) / slots)); an item with cost > target becomes
-  R = ceil(cost / target) pieces, piece r covering [lo + floor(r cost / R), lo + floor((r+1) cost / R));
+  target = max(1, ceil(sum(cost) / slots)); when sum(cost) > slots, an item with cost > target becomes
+  R = ceil(cost / target) pieces, piece r covering [lo + floor(r cost / R), lo + floor((r+1) cost / R))
+  (with less than one tile of work per slot nothing is split: merging the pieces would cost a launch
+  of its own, more than the tiles it saves);
   split groups are numbered in the lexicographic order above and own partial slots
   slot0 .. slot0 + R - 1 (piece r -> slot0 + r); unsplit items carry slot -1
 order: by (piece length descending, b, h, tile, range start) ascending.
@@ -50,7 +52,7 @@ def _finish(raw, slots: int, split: bool):
     next_slot = 0
     for (b, h, t, lo, hi) in raw:
         cost = hi - lo
-        if split and cost > target:
+        if split and total > max(1, slots) and cost > target:
             R = _ceil_div(cost, target)
             groups.append((b, h, t, next_slot, R))
             for r in range(R):
