@@ -332,9 +332,10 @@ void fwd_kernel2(FwdArgs a) {
   auto tile = [&](const int kt, auto st_tag) {
     constexpr int ST = decltype(st_tag)::value;
     const int key0 = kt * BN;
-    // A tile with no visible pair for this wave's rows (past the diagonal, or outside the band)
-    // contributes nothing to them.
-    const bool wskip = CAUSAL ? key0 > row0 + 31 : (BAND ? (key0 > whi || key0 + BN - 1 < wlo) : false);
+    // A tile with no visible pair for this wave's rows (past the diagonal, or outside the band), or a
+    // wave whose rows all lie past the sequence's end, contributes nothing.
+    const bool wskip =
+        row0 >= Lq || (CAUSAL ? key0 > row0 + 31 : (BAND ? (key0 > whi || key0 + BN - 1 < wlo) : false));
     wait_vm();
     // Bias of score (qi, key) sits at diag[qi - key + 31 - (row0 - key0)] = diag[31 - l32 + key - key0]:
     // ascending in the accumulator's register order.
