@@ -37,6 +37,14 @@ Masked pairs contribute exactly nothing in both modes: the pages describe maskin
 subtraction" (kerneldigest.dev page, "Arquitectura del Sistema") — a device mechanism, read here
 as exclusion.
 
+Under the causal mask a sequence may have more queries than keys (Lq_b >= Lkv_b): the fused self +
+target pass of in-kernel broadcast inference (itsolotime.com IKBO page, table of contents section
+3.3, "Self + Target attention fused through model co-design"). Rows i < Lkv_b are the user's history
+attending causally to itself; rows i >= Lkv_b are target (candidate) rows, and j <= i then holds for
+every key, so each target sees the whole history and nothing else — the same result as a separate
+cross-attention of the targets on the history (positions, and hence a relative-position bias, still
+count from the sequence start).
+
 The backward pass is the gradient of <O, dO> (plus nothing from lse) with respect to q, k, v and
 the bias parameters, written out:
 
@@ -314,3 +322,93 @@ def rows(q, k, v, q_off, kv_off, b, h, rows_, dout=None, *, mask="none", act="so
                 dS = np.where(vis, (dout[qs + i:qs + i + 1, h] @ V.T) * inv_l * fprime(S), 0.0)
                 dq[r] = scale * (dS @ K)[0]
     return out, lse, dq
+
+
+def key_cols(q, k, v, q_off, kv_off, b, h, keys, dout, *, mask="none", act="softmax", bias_kind="none", bias=None,
+             window=0, block=0, scale: Optional[float] = None):
+    """dK and dV of selected keys of one sequence and head, each from its own column of scores.
+
+    The same definition as :func:`backward`, evaluated per key j: with the row statistics of every
+    query i that sees j (softmax: lse_i and Delta_i = sum_j' P_ij' dP_ij' over the whole row),
+
+      softmax: P_ij = exp(s_ij - lse_i), dS_ij = P_ij (<dO_i, V_j> - Delta_i)
+      GDPA:    P_ij = act(s_ij) / Lkv,   dS_ij = <dO_i, V_j> act'(s_ij) / Lkv
+      dK_j = scale sum_i dS_ij Q_i,      dV_j = sum_i P_ij dO_i
+
+    so that single keys of very long sequences can be checked without all of dK. The row statistics
+    come from the full score rows, processed in chunks of query rows. Returns ``(dk [n, D], dv [n, D])``.
+    """
+    q_off, kv_off = _check(q, k, v, q_off, kv_off, mask, act, bias_kind, bias, window, block)
+    D = q.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    qs, qe, ks, ke = q_off[b], q_off[b + 1], kv_off[b], kv_off[b + 1]
+    lq, lkv = qe - qs, ke - ks
+    K, V = k[ks:ke, h], v[ks:ke, h]
+    keys = np.asarray(keys, dtype=np.int64)
+    bias_h = None if bias is None else np.asarray(bias, dtype=np.float64)[h]
+    dk = np.zeros((len(keys), D))
+    dv = np.zeros((len(keys), D))
+    for i0, i1 in _chunks(lq, lkv):
+        Qc = q[qs + i0:qs + i1, h]
+        dOc = dout[qs + i0:qs + i1, h]
+        # full rows: the statistics each query row contributes to every key column
+        S, vis, _ = _scores(Qc, K, i0, scale, mask, bias_kind, bias_h, window, block)
+        if act == "softmax":
+            P, lse = _softmax_rows(S, vis)
+            delta = (P * (dOc @ V.T)).sum(axis=1)
+        del S, vis
+        # the selected key columns, at their positions j in the sequence
+        Sk = scale * (Qc @ K[keys].T)
+        i = i0 + np.arange(i1 - i0)[:, None]
+        j = keys[None, :]
+        if bias_kind == "scalar":
+            Sk = Sk + bias_h
+        elif bias_kind == "bucket":
+            Sk = Sk + bias_h[bucket(i - j)]
+        visk = visible(i, j, mask, window, block) & (j < lkv)
+        dPk = dOc @ V[keys].T
+        if act == "softmax":
+            with np.errstate(invalid="ignore"):
+                Pk = np.where(visk & np.isfinite(lse)[:, None], np.exp(Sk - np.where(np.isfinite(lse), lse, 0.0)[:, None]), 0.0)
+            dSk = Pk * (dPk - delta[:, None])
+        else:
+            f, fprime = _ACTS[act]
+            inv_l = 1.0 / lkv if lkv > 0 else 0.0
+            Pk = np.where(visk, f(Sk), 0.0) * inv_l
+            dSk = np.where(visk, dPk * inv_l * fprime(Sk), 0.0)
+        dk += scale * (dSk.T @ Qc)
+        dv += Pk.T @ dOc
+    return dk, dv
+
+
+def replicate_shared_q(q_shared, num_seqs: int):
+    """Query rows of every sequence when one set of ``Ls`` query rows is shared by all of them.
+
+    Pooling by multihead attention (PMA), which the pages list beside self- and cross-attention as the
+    same two-product structure (aihot.vn GEM page, "Generalized Dot-Product Attention (GDPA)"), attends
+    from one learned set of seed queries to each sequence's keys: sequence b's queries are the seeds
+    themselves. Returns the explicit copy ``[B * Ls, H, D]`` and its offsets ``b * Ls``; the device
+    reads the shared rows without making it.
+    """
+    q_shared = np.asarray(q_shared)
+    Ls = q_shared.shape[0]
+    return np.tile(q_shared, (num_seqs, 1, 1)), np.arange(num_seqs + 1, dtype=np.int64) * Ls
+
+
+def forward_shared_q(q_shared, k, v, kv_off, **kw):
+    """:func:`forward` with the query rows shared by every sequence (see :func:`replicate_shared_q`)."""
+    B = len(kv_off) - 1
+    q_rep, q_off = replicate_shared_q(q_shared, B)
+    return forward(q_rep, k, v, q_off, kv_off, **kw)
+
+
+def backward_shared_q(q_shared, k, v, kv_off, dout, **kw):
+    """:func:`backward` with shared query rows: the gradient of a query row used by every sequence is
+    the sum of its gradients in each sequence (the chain rule over its B uses). Returns
+    ``(dq [Ls, H, D], dk, dv, dbias)``."""
+    B = len(kv_off) - 1
+    q_rep, q_off = replicate_shared_q(q_shared, B)
+    dq, dk, dv, db = backward(q_rep, k, v, q_off, kv_off, dout, **kw)
+    Ls = np.asarray(q_shared).shape[0]
+    return dq.reshape(B, Ls, *dq.shape[1:]).sum(axis=0), dk, dv, db

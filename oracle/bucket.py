@@ -26,13 +26,11 @@ def bucket(d) -> np.ndarray:
     big = d >= 16
     if np.any(big):
         db = d[big]
-        # floor(log2 db) for db >= 16, exact in integers
-        e = np.zeros_like(db)
-        x = db.copy()
-        while np.any(x > 1):
-            step = x > 1
-            e[step] += 1
-            x[step] >>= 1
+        # floor(log2 db) for db >= 16: the binary exponent of db as a float64, exact for db < 2^53
+        # (frexp gives db = m 2^x with 0.5 <= m < 1, so floor(log2 db) = x - 1)
+        if db.max() >= 2 ** 53:
+            raise ValueError("distance too large")
+        e = np.frexp(db.astype(np.float64))[1].astype(np.int64) - 1
         quarter = (db >> (e - 2)) & 3
         out[big] = np.minimum(NUM_BUCKETS - 1, 16 + 4 * (e - 4) + quarter)
     return out.reshape(d_in.shape)

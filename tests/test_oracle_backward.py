@@ -118,3 +118,41 @@ def test_empty_sequences_give_zero_gradients():
         np.testing.assert_array_equal(dk[:4], 0.0)
         np.testing.assert_array_equal(dv[:4], 0.0)
         assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk))
+
+
+@pytest.mark.parametrize("mask,act,bias_kind", MODES)
+@pytest.mark.parametrize("window", [0, 5])
+def test_key_columns_match_library_autograd(mask, act, bias_kind, window):
+    """oracle.key_cols evaluates dK_j and dV_j of single keys from their own score columns (the row
+    statistics from whole rows); against torch autograd of padded dense attention, keys in any order."""
+    lq, lkv = ([9, 17, 2, 30], [9, 17, 2, 30]) if mask == "causal" else ([9, 17, 2, 6], [12, 3, 20, 25])
+    x, q, k, v, do, bias = _case(lq, lkv, 2, 16, 13, mask, act, bias_kind)
+    scale = 1 / math.sqrt(16)
+    if act == "softmax":
+        _, _, _, rk, rv, _ = dense_softmax(q, k, v, x.q_off, x.kv_off, mask, bias_kind, bias, scale, want_grad=True,
+                                           dout=do, window=window)
+    else:
+        _, _, rk, rv, _ = dense_gdpa(q, k, v, x.q_off, x.kv_off, mask, act, bias_kind, bias, scale, want_grad=True,
+                                     dout=do, window=window)
+    rng = np.random.default_rng(3)
+    for b in range(4):
+        L = lkv[b]
+        keys = rng.permutation(L)[: max(1, L // 2)] if L else []
+        for h in range(2):
+            gk, gv = A.key_cols(q, k, v, x.q_off, x.kv_off, b, h, keys, do, mask=mask, act=act, bias_kind=bias_kind,
+                                bias=bias, window=window)
+            s = int(x.kv_off[b])
+            np.testing.assert_allclose(gk, rk[s + np.asarray(keys, dtype=np.int64), h], rtol=0, atol=1e-11)
+            np.testing.assert_allclose(gv, rv[s + np.asarray(keys, dtype=np.int64), h], rtol=0, atol=1e-11)
+
+
+def test_key_columns_with_empty_rows_and_long_rows_in_chunks():
+    """Rows that see no key contribute nothing; rows longer than one chunk give the same columns."""
+    x, q, k, v, do, _ = _case([0, 3000], [5, 3000], 1, 8, 14, "none", "softmax", "none")
+    keys = [0, 1, 2999, 1500]
+    gk, gv = A.key_cols(q, k, v, x.q_off, x.kv_off, 1, 0, keys, do)
+    _, dk, dv, _ = A.backward(q, k, v, x.q_off, x.kv_off, do, seqs=[1])
+    np.testing.assert_allclose(gk, dk[5 + np.array(keys), 0], rtol=0, atol=1e-10)
+    np.testing.assert_allclose(gv, dv[5 + np.array(keys), 0], rtol=0, atol=1e-10)
+    gk0, gv0 = A.key_cols(q, k, v, x.q_off, x.kv_off, 0, 0, [0, 4], do)
+    assert not gk0.any() and not gv0.any()

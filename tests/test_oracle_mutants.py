@@ -146,3 +146,58 @@ def test_real_oracle_passes_band_pins():
 @pytest.mark.parametrize("name,old,new", BAND_MUTATIONS, ids=[m[0] for m in BAND_MUTATIONS])
 def test_planted_band_mistake_is_caught(name, old, new):
     assert not _band_pins_pass(_mutant(old, new)), name
+
+
+def _keycols_pins_pass(mod):
+    """True when the mutated oracle's per-key gradients pass library autograd pins."""
+    D = 8
+    scale = 1 / math.sqrt(D)
+    for mask, act, bias_kind in [("causal", "softmax", "bucket"), ("none", "softmax", "scalar"),
+                                 ("causal", "silu", "bucket"), ("none", "gelu_tanh", "none")]:
+        lq = [5, 19, 2]
+        lkv = lq if mask == "causal" else [7, 3, 22]
+        x = ji.make_inputs(lq, lkv, 2, D, wid=23, mask=mask, act=act, bias_kind=bias_kind, bias_sigma=0.5)
+        f = A.bf16_bits_to_f64
+        q, k, v, do = f(x.q), f(x.k), f(x.v), f(x.do)
+        bias = None if x.bias is None else x.bias.astype(np.float64)
+        if act == "softmax":
+            _, _, _, rk, rv, _ = dense_softmax(q, k, v, x.q_off, x.kv_off, mask, bias_kind, bias, scale, True, do)
+        else:
+            _, _, rk, rv, _ = dense_gdpa(q, k, v, x.q_off, x.kv_off, mask, act, bias_kind, bias, scale, True, do)
+        for b in range(3):
+            keys = np.arange(lkv[b])[::-2]  # a subset of the keys, in reverse order
+            s = int(x.kv_off[b])
+            for h in range(2):
+                try:
+                    gk, gv = mod.key_cols(q, k, v, x.q_off, x.kv_off, b, h, keys, do, mask=mask, act=act,
+                                          bias_kind=bias_kind, bias=bias)
+                except Exception:
+                    return False
+                if not (np.allclose(gk, rk[s + keys, h], rtol=0, atol=1e-10)
+                        and np.allclose(gv, rv[s + keys, h], rtol=0, atol=1e-10)):
+                    return False
+    return True
+
+
+KEYCOL_MUTATIONS = [
+    ("Delta from the selected columns only", "delta = (P * (dOc @ V.T)).sum(axis=1)",
+     "delta = (P[:, keys] * (dOc @ V[keys].T)).sum(axis=1)"),
+    ("bias at the column index instead of the key position", "Sk = Sk + bias_h[bucket(i - j)]",
+     "Sk = Sk + bias_h[bucket(i - np.arange(len(keys))[None, :])]"),
+    ("probabilities without the row's lse", "np.exp(Sk - np.where(np.isfinite(lse), lse, 0.0)[:, None])",
+     "np.exp(Sk)"),
+    ("visibility of the column index", "visk = visible(i, j, mask, window, block) & (j < lkv)",
+     "visk = visible(i, np.arange(len(keys))[None, :], mask, window, block) & (j < lkv)"),
+    ("per-key dK without scale", "dk += scale * (dSk.T @ Qc)", "dk += dSk.T @ Qc"),
+    ("per-key dV from Q", "dv += Pk.T @ dOc", "dv += Pk.T @ Qc"),
+    ("GDPA per-key normaliser dropped", "Pk = np.where(visk, f(Sk), 0.0) * inv_l", "Pk = np.where(visk, f(Sk), 0.0)"),
+]
+
+
+def test_real_oracle_passes_key_column_pins():
+    assert _keycols_pins_pass(A)
+
+
+@pytest.mark.parametrize("name,old,new", KEYCOL_MUTATIONS, ids=[m[0] for m in KEYCOL_MUTATIONS])
+def test_planted_key_column_mistake_is_caught(name, old, new):
+    assert not _keycols_pins_pass(_mutant(old, new)), name
