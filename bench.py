@@ -4,9 +4,13 @@
 A step is one pass of the whole hot path over one batch: the forward pass (work-list driven
 forward kernel and, when the plan split items, the combine kernel) and the backward pass
 (dQ kernel, which also forms Delta = rowsum(dO * O), dK/dV kernel, partial reduces), all through
-the C ABI. The plan
-(offset validation and the longest-first work lists) is built once per batch of offsets before
-the timed region; its host time is reported as ``plan_ms``.
+the C ABI. The plan (offset validation and the longest-first work lists) is built once per batch
+of offsets before the timed region; its host time is reported as ``plan_ms`` (first plan of the
+process) and ``plan_ms_steady`` (a plan for a reordered batch built while a step runs, as a
+training loop would build the next batch's plan).
+
+``value`` is useful FLOPs per step over the wall time of the K timed steps (bracketed by device
+synchronisations); ``median_step_ms`` is the median of the per-step HIP-event times.
 
 Useful FLOPs per visible (query, key) pair and head: 4 D forward + 10 D backward. Inputs are the
 seeded synthetic workload from ``jfa_inputs``, resident in HBM before timing starts.
@@ -29,7 +33,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 METRIC = "useful (unpadded) attention TFLOPS fwd+bwd and % of bf16 MFMA peak, 1×MI355X"
-DEFAULT_WORKLOAD = "causal_bucket"
+DEFAULT_WORKLOAD = "longtail"  # the long-tail production-like workload (B = 512, 333,877 tokens)
 # FLOPs each kernel must execute per visible pair and head (its own matrix products):
 #   forward: S = QK^T, O = PV; dK/dV: S, dP = dO V^T, dV = P^T dO, dK = dS^T Q; dQ: S, dP, dQ = dS K
 KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dkdv": 8, "dq": 6}
@@ -83,6 +87,63 @@ def counter_traffic(kernel: str, workload: str):
     return float(t.group(1))
 
 
+def host_cpu():
+    """(model name, cores this process may run on) of the host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return model, n
+
+
+def _parse_clock(tool: str, text: str):
+    if tool == "amd-smi":  # sections "GFX_<n>:" followed by "CLK: <v> MHz"
+        vals = [int(m.group(1)) for m in re.finditer(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", text)]
+    else:
+        vals = [int(v) for v in re.findall(r"sclk[^(]*\((\d+)\s*Mhz\)", text, re.I)]
+    if not vals:
+        return None
+    return {"mhz_max": max(vals), "mhz_mean": round(sum(vals) / len(vals), 1), "source": tool}
+
+
+def gpu_clock_under_load(step, seconds: float, median_ms: float):
+    """Shader (GFX) clock in MHz as the SMI tool samples it while about ``seconds`` of steps run.
+
+    The tool is started first (it takes a second or two to sample) and the steps are queued behind
+    it, so the sample falls inside the busy period; these steps are outside the timed region. Not
+    run under a profiler (the tool is a script whose interpreter the profiler's preload would
+    follow)."""
+    import subprocess
+    if any("ROCPROF" in k for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return None
+    for tool, cmd in (("amd-smi", ["amd-smi", "metric", "--clock"]), ("rocm-smi", ["rocm-smi", "--showclocks"])):
+        try:
+            proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+        except OSError:
+            continue
+        for _ in range(max(1, min(5000, int(seconds * 1e3 / max(median_ms, 1e-3))))):
+            step()
+        try:
+            text = proc.communicate(timeout=60)[0]
+        except subprocess.SubprocessError:
+            proc.kill()
+            continue
+        res = _parse_clock(tool, text)
+        if res:
+            res["sampled_during_steps"] = True
+            return res
+    return None
+
+
 def cpu_baseline(x, workload, seconds_target=15.0):
     """Time the fp64 oracle (as it stands) on a bounded sample of the workload's sequences."""
     import numpy as np
@@ -91,9 +152,11 @@ def cpu_baseline(x, workload, seconds_target=15.0):
 
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        blas_threads = None
+    model, nproc = host_cpu()
+    cores = blas_threads or nproc
     from jagged_sequence_amd.flops import useful_flops
     f = A.bf16_bits_to_f64
     lq = np.diff(x.q_off.astype(np.int64))
@@ -116,18 +179,26 @@ def cpu_baseline(x, workload, seconds_target=15.0):
     krows = np.concatenate([np.arange(x.kv_off[b], x.kv_off[b + 1]) for b in seqs])
     sq = np.concatenate([[0], np.cumsum(lq[seqs])])
     sk = np.concatenate([[0], np.cumsum(lkv[seqs])])
-    q, k, v = f(x.q[rows]), f(x.k[krows]), f(x.v[krows])
+    k, v = f(x.k[krows]), f(x.v[krows])
     bias = None if x.bias is None else x.bias.astype(np.float64)
     kw = dict(mask=x.mask, act=x.act, bias_kind=x.bias_kind, bias=bias, window=x.window, block=x.block)
     t0 = time.perf_counter()
-    A.forward(q, k, v, sq, sk, **kw)
-    if workload_backward(workload):
-        A.backward(q, k, v, sq, sk, f(x.do[rows]), **kw)
+    if x.shared_q:  # the seed rows are shared by every sequence
+        A.forward_shared_q(f(x.q), k, v, sk, **kw)
+        if workload_backward(workload):
+            A.backward_shared_q(f(x.q), k, v, sk, f(x.do[rows]), **kw)
+    else:
+        q = f(x.q[rows])
+        A.forward(q, k, v, sq, sk, **kw)
+        if workload_backward(workload):
+            A.backward(q, k, v, sq, sk, f(x.do[rows]), **kw)
     dt = time.perf_counter() - t0
     fw, bw = useful_flops(sq, sk, x.H, x.D, causal, workload_backward(workload), x.window, x.block)
     return {"value": (fw + bw) / dt / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
+            "nproc": nproc, "cpu_model": model, "blas_threads": blas_threads,
             "sample": f"{len(seqs)} of {len(lq)} sequences (the first ones), all {x.H} heads, "
-                      f"fwd{'+bwd' if workload_backward(workload) else ''}, {dt:.1f} s, numpy float64"}
+                      f"fwd{'+bwd' if workload_backward(workload) else ''}, {dt:.1f} s, numpy float64 "
+                      f"(matrix products in BLAS with {cores} threads, elementwise steps on one)"}
 
 
 def workload_backward(name: str) -> bool:
@@ -142,6 +213,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the SMI clock sample after the timed region")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--dbias", action="store_true",
                     help="also compute the bias gradient in every backward pass (a learned bias needs it)")
@@ -183,18 +255,19 @@ def main() -> int:
     bias = torch.from_numpy(x.bias).cuda() if x.bias is not None else None
     torch.cuda.synchronize()
 
+    plan_kw = dict(mask=w.mask, act=w.act, bias=w.bias, window=w.window, block=w.block, out_dtype=args.out_dtype,
+                   grad_dtype=args.out_dtype, shared_q=x.shared_q)
     t0 = time.perf_counter()
-    plan = J.Plan(x.q_off, x.kv_off, w.H, w.D, mask=w.mask, act=w.act, bias=w.bias, window=w.window, block=w.block,
-                  out_dtype=args.out_dtype,
-                  grad_dtype=args.out_dtype)
+    plan = J.Plan(x.q_off, x.kv_off, w.H, w.D, **plan_kw)
     plan_ms = (time.perf_counter() - t0) * 1e3
     fwd_ws, bwd_ws = plan.workspace_bytes()
     ws_f = torch.empty(max(fwd_ws, 1), dtype=torch.uint8, device="cuda")
     ws_b = torch.empty(max(bwd_ws, 1), dtype=torch.uint8, device="cuda")
     odt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
-    out = torch.empty((x.q.shape[0], w.H, w.D), dtype=odt, device="cuda")
-    lse = torch.empty((w.H, x.q.shape[0]), dtype=torch.float32, device="cuda")
-    dq = torch.empty_like(out)
+    Tq = int(x.q_off[-1])
+    out = torch.empty((Tq, w.H, w.D), dtype=odt, device="cuda")
+    lse = torch.empty((w.H, Tq), dtype=torch.float32, device="cuda") if w.act == "softmax" else None
+    dq = torch.empty((x.q.shape[0], w.H, w.D), dtype=odt, device="cuda")  # shared queries: one set of rows
     dk = torch.empty((x.k.shape[0], w.H, w.D), dtype=odt, device="cuda")
     dv = torch.empty_like(dk)
     want_db = args.dbias and bias is not None and w.backward
@@ -210,22 +283,48 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    # Planning in steady state: offsets change with every batch, so the next batch's plan is built
+    # while the GPU runs the current step. Here a batch with the same lengths in another order (new
+    # offsets) is planned while a step runs; the host time of that call is reported.
+    perm = np.random.default_rng(1).permutation(w.B)
+    lq_b, lkv_b = np.diff(x.q_off)[perm], np.diff(x.kv_off)[perm]
+    qo2, ko2 = ji.offsets(lq_b), ji.offsets(lkv_b)
+    steady = []
+    for _ in range(3):
+        step()
+        t1 = time.perf_counter()
+        p2 = J.Plan(qo2, ko2, w.H, w.D, **plan_kw)
+        steady.append((time.perf_counter() - t1) * 1e3)
+        del p2
+    torch.cuda.synchronize()
+
     plan.timing_enable(True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for e0, e1 in ev:
+        e0.record(stream)
         step()
+        e1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
     kernels = {}
     for name in J.KERNELS:
         ms, n = plan.timing_read(name)
         if n:
             kernels[name] = {"avg_ms": ms / n, "launches_per_step": n / args.steps, "total_ms": ms}
     plan.timing_enable(False)
+    clock = None if args.no_clock else gpu_clock_under_load(step, 4.0, median_ms)
+    torch.cuda.synchronize()
 
     fw, bw = useful_flops(x.q_off, x.kv_off, w.H, w.D, causal, w.backward, w.window, w.block)
     ms_per_step = elapsed / args.steps * 1e3
+    props = torch.cuda.get_device_properties(0)
+    with open(J.LIB_PATH, "rb") as fh:
+        lib_hash = hashlib.sha256(fh.read()).hexdigest()[:16]
     value = (fw + bw) / (elapsed / args.steps) / 1e12
     pairs = visible_pairs(x.q_off, x.kv_off, causal, w.window, w.block) * w.H
 
@@ -266,7 +365,13 @@ def main() -> int:
                    "visible_pairs_x_heads": int(pairs), "out_dtype": args.out_dtype, "bias_gradient": bool(want_db),
                    "description": w.description},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "median_step_ms": round(median_ms, 4),
+        "value_at_median_step": round((fw + bw) / (median_ms * 1e-3) / 1e12, 2),
         "plan_ms": round(plan_ms, 3),
+        "plan_ms_steady": round(min(steady), 3),
+        "gpu": {"name": props.name, "arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+                "clock_during_run": clock},
+        "library": {"path": os.path.relpath(J.LIB_PATH, ROOT), "sha256": lib_hash},
         "kernels": {kk: {"avg_ms": round(vv["avg_ms"], 5), "per_step": vv["launches_per_step"]}
                     for kk, vv in kernels.items()},
         "roofline": roofline,

@@ -15,7 +15,7 @@
  * query i < Lq, key j < Lkv:
  *   s_ij = scale * <q_i, k_j> + beta_h(i, j),  beta = 0 | c_h | T[h][bucket(|i - j|)]
  *   visible(i, j) = base && window && block
- *     base   = (mask == NONE) || (j <= i)
+ *     base   = (mask == NONE) || (j <= i)     (causal with Lq > Lkv: rows i >= Lkv see every key)
  *     window = (W == 0) || (i - j < W && (mask == CAUSAL || j - i < W))
  *     block  = (Bk == 0) || (i / Bk == j / Bk)
  *   softmax: out_i = sum_j P_ij v_j with P the softmax of s_i over visible j; lse_i = ln sum exp
@@ -33,10 +33,14 @@
  *   Every tensor pointer must be 16-byte aligned (JFA_ERR_MISALIGNED otherwise).
  *
  * Ownership: the caller owns every tensor, both copies of the offsets and the workspace. A plan
- * owns its host schedule and its device copy of the work lists and frees them in
+ * owns its host schedule and its device copy of the work lists and returns them in
  * jfa_plan_destroy. A plan is immutable after jfa_plan and may be used on several streams at
  * once when each call gets its own workspace. jfa_forward / jfa_backward allocate nothing, never
  * synchronise the stream, and only enqueue kernels on the stream they are given.
+ *
+ * Limits: a (sequence, head) slice is addressed with 32-bit offsets, so (L + 128) * H * D must not
+ * exceed 2^30 for every sequence, L = max(Lq, Lkv) (JFA_ERR_BAD_SHAPE otherwise; e.g. H = 8,
+ * D = 128 allows L up to 1,048,448). The scale must be finite and >= 0.
  *
  * Errors: every call returns a jfa_status; nothing aborts and no exception crosses the ABI. All
  * argument checks run before the first launch, so on error no output has been touched.
@@ -60,9 +64,11 @@ typedef enum {
   JFA_OK = 0,
   JFA_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
   JFA_ERR_BAD_OFFSETS = 2,  /* offsets[0] != 0, decreasing offsets, or a total beyond int32 */
-  JFA_ERR_BAD_SHAPE = 3,    /* B < 1, H < 1, D not 64/128, causal with some Lq != Lkv,
-                               window or block < 0 */
-  JFA_ERR_UNSUPPORTED = 4,  /* enum out of range, or a feature this build does not provide */
+  JFA_ERR_BAD_SHAPE = 3,    /* B < 1, H < 1, D not 64/128, causal with some Lq < Lkv, shared
+                               queries with unequal Lq,
+                               window or block < 0, a sequence beyond the 32-bit slice limit */
+  JFA_ERR_UNSUPPORTED = 4,  /* enum out of range, negative or non-finite scale, or a feature this
+                               build does not provide */
   JFA_ERR_MISALIGNED = 5,   /* a tensor pointer is not 16-byte aligned */
   JFA_ERR_WORKSPACE = 6,    /* workspace smaller than jfa_workspace_bytes reports */
   JFA_ERR_HIP = 7,          /* a HIP runtime call or launch failed */
@@ -77,6 +83,14 @@ typedef enum { JFA_BF16 = 0, JFA_F32 = 1 } jfa_dtype;
 /* jfa_problem.flags */
 #define JFA_PLAN_HOST_ONLY 0x1u /* build the schedule on the host only: no HIP call, no launches */
 #define JFA_PLAN_NO_SPLIT 0x2u  /* never split a work item into key (or query) ranges */
+/* Shared queries: one set of Ls query rows serves every sequence, as the learned seed queries of
+ * pooling by multihead attention (PMA), which the pages list beside self- and cross-attention as
+ * the same two-product structure (aihot.vn GEM page, "Generalized Dot-Product Attention (GDPA)").
+ * Every Lq_b must equal Ls (q_offsets_host = b * Ls); q and dq are [Ls, H, D] and are read (resp.
+ * written) once for all sequences, with no copy per sequence; out, lse and dout stay per sequence
+ * ([B * Ls, H, D], [H, B * Ls]). dq is the sum over sequences of each sequence's query gradient,
+ * taken in a fixed order (deterministic). */
+#define JFA_PLAN_SHARED_Q 0x4u
 
 typedef struct {
   int32_t num_seqs;               /* B >= 1 */
@@ -84,7 +98,9 @@ typedef struct {
   int32_t head_dim;               /* D in {64, 128} */
   const int32_t* q_offsets_host;  /* [B+1] host array, read during jfa_plan only */
   const int32_t* kv_offsets_host; /* [B+1] host array, read during jfa_plan only */
-  int32_t mask;                   /* jfa_mask; causal requires Lq == Lkv for every sequence */
+  int32_t mask;                   /* jfa_mask; causal requires Lq >= Lkv for every sequence: rows
+                                     i >= Lkv are target rows that see every key (fused self + target
+                                     pass, itsolotime.com IKBO page, table of contents section 3.3) */
   int32_t act;                    /* jfa_act */
   int32_t bias;                   /* jfa_bias */
   float scale;                    /* score scale; 0 means 1/sqrt(D) */
@@ -106,7 +122,15 @@ typedef struct {
 } jfa_problem;
 
 /* Validate the problem, build the longest-first work lists (jagged tile scheduler) and, unless
- * JFA_PLAN_HOST_ONLY, upload them to device memory with an asynchronous copy on `stream`. */
+ * JFA_PLAN_HOST_ONLY, upload them to device memory with an asynchronous copy on `stream`.
+ * The pages place the cost that remains once padding is gone in tile scheduling and load balance
+ * (vibekk.com GEM page, section on moving from padding to jagged kernels; aihot.vn GEM page,
+ * "Jagged Sequence Flash Attention": compute units idle when short sequences finish early), and
+ * offsets change with every batch, so planning never waits for the device: the records are written
+ * into pinned host memory and copied asynchronously, and the pinned and device buffers come from
+ * a process-wide cache that hands a buffer out again only after the device has finished with it
+ * (the upload and the last pass on every stream that used the plan). The host offsets are read
+ * during this call only. On error *plan_out is NULL and nothing was enqueued. */
 jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t* plan_out);
 
 /* Device bytes of workspace each pass needs (0 when nothing is split and no scratch is used).
@@ -116,16 +140,22 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
  * kernel runs. Either pointer may be NULL. */
 jfa_status jfa_workspace_bytes(jfa_plan_t plan, size_t* fwd_bytes, size_t* bwd_bytes);
 
-/* Forward pass. `bias` may be NULL only without bias; `lse` may be NULL only for GDPA (it is
- * not defined there). `q_offsets` / `kv_offsets` are device copies equal to the host offsets
- * given to jfa_plan. `workspace` may be NULL when its size is 0. */
+/* Forward pass: out (and lse for softmax) of the attention defined above, computed straight on
+ * the jagged values with no padded tensor (aihot.vn GEM page, "Jagged Sequence Flash Attention";
+ * "Generalized Dot-Product Attention (GDPA)" for the pointwise activations). `bias` may be NULL
+ * only without bias; `lse` may be NULL only for GDPA (it is not defined there). `q_offsets` /
+ * `kv_offsets` are optional device copies of the offsets given to jfa_plan (NULL allowed): the
+ * kernels take every sequence's offsets from the plan's work records, and with JFA_DEBUG=1 in the
+ * environment the copies are read back and compared with the plan (JFA_ERR_BAD_OFFSETS on a
+ * mismatch; a synchronising check). `workspace` may be NULL when its size is 0. */
 jfa_status jfa_forward(jfa_plan_t plan, const void* q, const void* k, const void* v,
                        const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias,
                        void* out, float* lse, void* workspace, size_t workspace_bytes,
                        jfa_stream_t stream);
 
 /* Backward pass: gradients of <out, dout> with respect to q, k and v, and optionally the bias.
- * `out` and `lse` are the forward results (softmax only; they may be NULL for GDPA).
+ * `out` and `lse` are the forward results (softmax only; they may be NULL for GDPA). The optional
+ * device offsets are treated as in jfa_forward.
  * `dbias` is NULL (no bias gradient) or a device fp32 array of the bias shape, [H] for
  * JFA_BIAS_HEAD_SCALAR and [H][64] for JFA_BIAS_REL_BUCKET64 (16-byte aligned), that receives
  * dL/dbias: for the table, entry (h, u) is the sum of dS over the visible scores of head h whose

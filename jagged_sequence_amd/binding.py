@@ -17,8 +17,7 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# JFA_LIBRARY selects another build of the same library (for A/B measurements of kernel variants)
-LIB_PATH = os.environ.get("JFA_LIBRARY") or os.path.join(_HERE, "libjfa.so")
+LIB_PATH = os.path.join(_HERE, "libjfa.so")
 
 JFA_OK = 0
 STATUS_NAMES = {0: "JFA_OK", 1: "JFA_ERR_NULL_ARG", 2: "JFA_ERR_BAD_OFFSETS", 3: "JFA_ERR_BAD_SHAPE",
@@ -30,6 +29,7 @@ BIASES = {"none": 0, "scalar": 1, "bucket": 2}
 DTYPES = {"bf16": 0, "f32": 1}
 PLAN_HOST_ONLY = 0x1
 PLAN_NO_SPLIT = 0x2
+PLAN_SHARED_Q = 0x4
 KERNELS = {"forward": 0, "combine": 1, "dkdv": 3, "dq": 4, "reduce": 5, "dbias": 6}
 SYMBOLS = ["jfa_plan", "jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_plan_schedule", "jfa_plan_info",
            "jfa_timing_enable", "jfa_timing_read", "jfa_plan_destroy", "jfa_status_string", "jfa_last_error"]
@@ -82,6 +82,34 @@ def _check(status: int):
         raise JfaError(status, LIB.jfa_last_error().decode())
 
 
+def _check_tensors(specs):
+    """Raise ValueError unless every ``(name, tensor, shape, dtype)`` names a contiguous tensor of that
+    shape and dtype, all on one GPU.
+
+    The library sees bare pointers: a tensor of the wrong size, type or layout would make the kernels
+    read or write past it, so every tensor is checked here, before the call. Shapes, dtypes and layouts
+    are checked for all tensors first and devices last, so the structural checks also run on CPU
+    tensors."""
+    for name, t, shape, dtype in specs:
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    dev = specs[0][1].device
+    for name, t, _, _ in specs:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (it is on {t.device})")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, {specs[0][0]} on {dev}")
+    return dev
+
+
 def _ptr(t) -> Optional[int]:
     """Device pointer of a torch tensor (or None)."""
     if t is None:
@@ -105,7 +133,7 @@ class Plan:
     def __init__(self, q_offsets, kv_offsets, num_heads: int, head_dim: int, *, mask: str = "none",
                  act: str = "softmax", bias: str = "none", scale: float = 0.0, out_dtype: str = "bf16",
                  grad_dtype: str = "bf16", num_slots: int = 0, host_only: bool = False, no_split: bool = False,
-                 window: int = 0, block: int = 0, stream=None):
+                 window: int = 0, block: int = 0, shared_q: bool = False, stream=None):
         self._q_off = _i32(q_offsets)
         self._kv_off = _i32(kv_offsets)
         self.B = len(self._q_off) - 1
@@ -128,7 +156,11 @@ class Plan:
         p.out_dtype = DTYPES[out_dtype]
         p.grad_dtype = DTYPES[grad_dtype]
         p.num_slots = int(num_slots)
-        p.flags = (PLAN_HOST_ONLY if host_only else 0) | (PLAN_NO_SPLIT if no_split else 0)
+        p.flags = (PLAN_HOST_ONLY if host_only else 0) | (PLAN_NO_SPLIT if no_split else 0) | \
+            (PLAN_SHARED_Q if shared_q else 0)
+        self.shared_q = bool(shared_q)
+        # rows of q and dq: one shared set of Ls rows, or one set per sequence
+        self.Tq_src = (int(self._q_off[1]) if self.B >= 1 else 0) if shared_q else self.Tq
         p.window = self.window
         p.block = self.block
         handle = ctypes.c_void_p()
@@ -179,14 +211,53 @@ class Plan:
             ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         return ws
 
+    # ------------------------------------------------------------------ argument checks
+    def _dtype(self, name: str):
+        return torch.float32 if name == "f32" else torch.bfloat16
+
+    def _common_specs(self, q, k, v, q_offsets, kv_offsets, bias):
+        bf = torch.bfloat16
+        specs = [("q", q, (self.Tq_src, self.H, self.D), bf), ("k", k, (self.Tkv, self.H, self.D), bf),
+                 ("v", v, (self.Tkv, self.H, self.D), bf)]
+        for name, off in (("q_offsets", q_offsets), ("kv_offsets", kv_offsets)):
+            if off is not None:
+                specs.append((name, off, (self.B + 1,), torch.int32))
+        if self.bias_kind == "none":
+            if bias is not None:
+                raise ValueError("bias given to a plan without bias")
+        else:
+            specs.append(("bias", bias, (self.H, 64) if self.bias_kind == "bucket" else (self.H,), torch.float32))
+        return specs
+
+    def _check_workspace(self, ws, nbytes: int, dev):
+        if nbytes == 0 or ws is None:
+            return
+        if not isinstance(ws, torch.Tensor) or not ws.is_contiguous() or ws.device != dev:
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, the plan needs {nbytes}")
+
     def forward(self, q, k, v, q_offsets, kv_offsets, bias=None, out=None, lse=None, workspace=None, stream=None):
-        """Forward pass; returns (out, lse). Tensors are torch device tensors in the ABI layouts."""
+        """Forward pass; returns (out, lse). Tensors are torch device tensors in the ABI layouts.
+
+        ``q_offsets`` / ``kv_offsets`` are optional device copies of the planned offsets (checked
+        against the plan only with JFA_DEBUG=1); every tensor is checked for shape, dtype, layout and
+        device before the library is called."""
+        specs = self._common_specs(q, k, v, q_offsets, kv_offsets, bias)
+        if out is not None:
+            specs.append(("out", out, (self.Tq, self.H, self.D), self._dtype(self.out_dtype)))
+        if lse is not None:
+            if self.act != "softmax":
+                raise ValueError("lse is defined for softmax only")
+            specs.append(("lse", lse, (self.H, self.Tq), torch.float32))
+        dev = _check_tensors(specs)
         if out is None:
             out = torch.empty((self.Tq, self.H, self.D), device=q.device,
                               dtype=torch.float32 if self.out_dtype == "f32" else torch.bfloat16)
         if lse is None and self.act == "softmax":
             lse = torch.empty((self.H, self.Tq), device=q.device, dtype=torch.float32)
         fwd_bytes, _ = self.workspace_bytes()
+        self._check_workspace(workspace, fwd_bytes, dev)
         ws = self._workspace(fwd_bytes, workspace)
         _check(LIB.jfa_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias),
                                _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
@@ -200,9 +271,24 @@ class Plan:
         ``dbias`` is None (no bias gradient), True (allocate it) or an fp32 device tensor of the
         bias shape that receives the gradient.
         """
-        gdt = torch.float32 if self.grad_dtype == "f32" else torch.bfloat16
+        specs = self._common_specs(q, k, v, q_offsets, kv_offsets, bias)
+        specs.append(("dout", dout, (self.Tq, self.H, self.D), torch.bfloat16))
+        if self.act == "softmax":
+            specs += [("out", out, (self.Tq, self.H, self.D), self._dtype(self.out_dtype)),
+                      ("lse", lse, (self.H, self.Tq), torch.float32)]
+        gdt = self._dtype(self.grad_dtype)
+        for name, t, T in (("dq", dq, self.Tq_src), ("dk", dk, self.Tkv), ("dv", dv, self.Tkv)):
+            if t is not None:
+                specs.append((name, t, (T, self.H, self.D), gdt))
+        if dbias is not None and dbias is not False:
+            if self.bias_kind == "none":
+                raise ValueError("dbias requested from a plan without bias")
+            if isinstance(dbias, torch.Tensor):
+                specs.append(("dbias", dbias, (self.H, 64) if self.bias_kind == "bucket" else (self.H,),
+                              torch.float32))
+        dev = _check_tensors(specs)
         if dq is None:
-            dq = torch.empty((self.Tq, self.H, self.D), device=q.device, dtype=gdt)
+            dq = torch.empty((self.Tq_src, self.H, self.D), device=q.device, dtype=gdt)
         if dk is None:
             dk = torch.empty((self.Tkv, self.H, self.D), device=q.device, dtype=gdt)
         if dv is None:
@@ -212,6 +298,7 @@ class Plan:
             shape = (self.H, 64) if self.bias_kind == "bucket" else (self.H,)
             dbias = torch.empty(shape, device=q.device, dtype=torch.float32)
         _, bwd_bytes = self.workspace_bytes()
+        self._check_workspace(workspace, bwd_bytes, dev)
         ws = self._workspace(bwd_bytes, workspace)
         _check(LIB.jfa_backward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias),
                                 _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -236,3 +323,4 @@ def jfa_backward(plan: Plan, q, k, v, q_offsets, kv_offsets, bias, out, lse, dou
                  workspace=None, stream=None, dbias=None):
     """``jfa_backward``: returns (dq, dk, dv), plus dbias when it is requested."""
     return plan.backward(q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq, dk, dv, workspace, stream, dbias)
+

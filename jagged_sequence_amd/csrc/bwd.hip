@@ -1,10 +1,16 @@
 // Backward pass of jagged attention on gfx950 (aihot.vn GEM page, "Jagged Sequence Flash
 // Attention": efficient backward passes; kerneldigest.dev page, "Arquitectura del Sistema":
-// backward-pass parallelisation). Two independent kernels, neither uses atomics:
-//   dK/dV: one workgroup per (sequence, head, 128-key tile), looping over 64-query tiles;
-//   dQ:    one workgroup per (sequence, head, 128-query tile), looping over 64-key tiles.
-// Both recompute the scores from Q, K and the forward log-sum-exp. Split items write fp32
-// partials that a fixed-order reduce sums, so results do not depend on scheduling.
+// backward-pass parallelisation). Two attention kernels, run in this order:
+//   dQ:    one workgroup per (sequence, head, 128-query tile) work item, looping over 64-key tiles;
+//          it also forms Delta = <dO_i, O_i> for the dK/dV kernel;
+//   dK/dV: at head dim 128 a persistent kernel (one workgroup per CU) that takes (sequence, head,
+//          128-key tile) items from per-XCD work queues and loops over 64-query tiles; at head dim 64,
+//          or when every sequence has a single query tile, one workgroup per item.
+// Both recompute the scores from Q, K and the forward log-sum-exp. dQ needs no atomics: each query
+// tile has one owner. Split items write fp32 partials that fixed-order sums combine, so results do
+// not depend on scheduling. The only atomics are the queue counters (which item runs where, never
+// what is computed) and, for the optional bias gradient, 64-bit fixed-point sums whose integer
+// additions give the same total in any order.
 //
 // Gradients (per visible pair, s = scale <q_i, k_j> + bias):
 //   softmax: P = exp(s - lse_i), dP = <dO_i, v_j>, dS = P (dP - Delta_i), Delta_i = <dO_i, O_i>
@@ -145,7 +151,7 @@ void bwd_dq_kernel(BwdArgs a) {
 
   bf16x8 qf[NKB], df[NKB];
   {
-    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)(a.q_shared ? 0 : qs) * rs + h * D, Lq, rs, D);
     const __amdgpu_buffer_rsrc_t gr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -262,7 +268,7 @@ void bwd_dq_kernel(BwdArgs a) {
           store4(a.dq, base + 32 * db + 8 * g + 4 * hh, qacc[db][4 * g] * sc, qacc[db][4 * g + 1] * sc,
                  qacc[db][4 * g + 2] * sc, qacc[db][4 * g + 3] * sc, a.grad_f32);
     }
-  } else {
+  } else if (qi < Lq) {  // the fixed-order sums read the rows of the sequence only
     float* po = a.part_dq + ((size_t)slot * BM + wave * 32 + l32) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -331,7 +337,7 @@ void bwd_dq_kernel2(BwdArgs a) {
 
   bf16x8 qf[NKB], df[NKB];
   {
-    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)(a.q_shared ? 0 : qs) * rs + h * D, Lq, rs, D);
     const __amdgpu_buffer_rsrc_t gr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -479,7 +485,7 @@ void bwd_dq_kernel2(BwdArgs a) {
           store4(a.dq, base + 32 * db + 8 * g + 4 * hh, qacc[db][4 * g] * sc, qacc[db][4 * g + 1] * sc,
                  qacc[db][4 * g + 2] * sc, qacc[db][4 * g + 3] * sc, a.grad_f32);
     }
-  } else {
+  } else if (qi < Lq) {  // the fixed-order sums read the rows of the sequence only
     float* po = a.part_dq + ((size_t)slot * BM + wave * 32 + l32) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -562,7 +568,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
     dv[db] = f32x16{};
   }
 
-  const __amdgpu_buffer_rsrc_t qsr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+  const __amdgpu_buffer_rsrc_t qsr = slice_rsrc(a.q + (size_t)(a.q_shared ? 0 : qs) * rs + h * D, Lq, rs, D);
   const __amdgpu_buffer_rsrc_t gsr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
   Units<D, kKvBM> uq, ug;
   float pl = 0.0f, pd = 0.0f;
@@ -873,7 +879,7 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-  const __amdgpu_buffer_rsrc_t qsr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+  const __amdgpu_buffer_rsrc_t qsr = slice_rsrc(a.q + (size_t)(a.q_shared ? 0 : qs) * rs + h * D, Lq, rs, D);
   const __amdgpu_buffer_rsrc_t gsr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
   const uint32_t raddr = row_operand_base(kappa(l32), hh);
   uint32_t T[2];

@@ -110,7 +110,7 @@ void fwd_kernel(FwdArgs a) {
 
   bf16x8 qf[NKB];
   {
-    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)(a.q_shared ? 0 : qs) * rs + h * D, Lq, rs, D);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) qf[kb] = as_bf16x8(buf_load16(qr, (uint32_t)(qi * rs + kb * 16 + hh * 8) * 2u));
   }
@@ -300,7 +300,7 @@ void fwd_kernel2(FwdArgs a) {
 
   bf16x8 qf[NKB];
   {
-    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+    const __amdgpu_buffer_rsrc_t qr = slice_rsrc(a.q + (size_t)(a.q_shared ? 0 : qs) * rs + h * D, Lq, rs, D);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) qf[kb] = as_bf16x8(buf_load16(qr, (uint32_t)(qi * rs + kb * 16 + hh * 8) * 2u));
   }
@@ -466,7 +466,7 @@ void fwd_kernel2(FwdArgs a) {
           store4(a.out, base + 32 * db + 8 * g + 4 * hh, o[db][4 * g] * inv, o[db][4 * g + 1] * inv,
                  o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv, a.out_f32);
     }
-  } else {
+  } else if (qi < Lq) {  // the combine reads the rows of the sequence only
     const int prow = wave * 32 + l32;
     float* po = a.part_o + ((size_t)slot * BM + prow) * D;
 #pragma unroll

@@ -16,6 +16,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <tuple>
 #include <new>
 #include <string>
 #include <vector>
@@ -44,6 +46,7 @@ enum ListId { kFwd = 0, kDq = 1, kKv = 2 };
 struct List {
   std::vector<int32_t> items;   // 6 ints per item: b, h, tile, lo, hi, slot
   std::vector<int32_t> groups;  // 5 ints per group: b, h, tile, slot0, R
+  std::vector<char> first;      // per item: the first piece of its tile (unsplit items included)
   std::vector<int> order;       // dispatch order: device item p is items[order[p]]
   int nslots = 0;
   int slots = 0;                // concurrency the split rule balanced for
@@ -59,39 +62,50 @@ struct Raw {
 
 void finish(const std::vector<Raw>& raw, int slots, bool split, List& out) {
   int64_t total = 0;
-  for (const Raw& r : raw) total += r.hi - r.lo;
+  int max_cost = 0;
+  for (const Raw& r : raw) {
+    total += r.hi - r.lo;
+    max_cost = std::max(max_cost, r.hi - r.lo);
+  }
   const int64_t s = std::max(1, slots);
   const int64_t target = std::max<int64_t>(1, (total + s - 1) / s);
+  // With less than one tile of work per slot nothing is split: merging the pieces would cost a
+  // launch of its own, more than the tiles it saves.
+  const bool do_split = split && total > s;
+  // Pieces in generation order, which is ascending (b, h, tile, range start).
   struct Item {
     int b, h, t, lo, hi, slot;
+    bool first;
   };
   std::vector<Item> items;
   items.reserve(raw.size());
   int next = 0;
   for (const Raw& r : raw) {
     const int64_t cost = r.hi - r.lo;
-    // With less than one tile of work per slot nothing is split: merging the pieces would cost a
-    // launch of its own, more than the tiles it saves.
-    if (split && total > s && cost > target) {
+    if (do_split && cost > target) {
       const int64_t R = (cost + target - 1) / target;
       out.groups.insert(out.groups.end(), {r.b, r.h, r.t, next, (int32_t)R});
       for (int64_t k = 0; k < R; ++k)
-        items.push_back({r.b, r.h, r.t, (int)(r.lo + (k * cost) / R), (int)(r.lo + ((k + 1) * cost) / R), next + (int)k});
+        items.push_back({r.b, r.h, r.t, (int)(r.lo + (k * cost) / R), (int)(r.lo + ((k + 1) * cost) / R), next + (int)k,
+                         k == 0});
       next += (int)R;
     } else {
-      items.push_back({r.b, r.h, r.t, r.lo, r.hi, -1});
+      items.push_back({r.b, r.h, r.t, r.lo, r.hi, -1, true});
     }
   }
-  std::sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
-    const int cx = x.hi - x.lo, cy = y.hi - y.lo;
-    if (cx != cy) return cx > cy;
-    if (x.b != y.b) return x.b < y.b;
-    if (x.h != y.h) return x.h < y.h;
-    if (x.t != y.t) return x.t < y.t;
-    return x.lo < y.lo;
-  });
-  out.items.reserve(items.size() * 6);
-  for (const Item& i : items) out.items.insert(out.items.end(), {i.b, i.h, i.t, i.lo, i.hi, i.slot});
+  // Longest first, ties in generation order: a stable counting sort by cost (descending) gives the
+  // order of the key (cost desc, b, h, tile, range start) in linear time.
+  std::vector<int> start(max_cost + 2, 0);
+  for (const Item& i : items) ++start[max_cost - (i.hi - i.lo) + 1];
+  for (int c = 0; c <= max_cost; ++c) start[c + 1] += start[c];
+  out.items.assign(items.size() * 6, 0);
+  out.first.assign(items.size(), 0);
+  for (const Item& i : items) {
+    const size_t p = (size_t)start[max_cost - (i.hi - i.lo)]++;
+    int32_t* o = &out.items[p * 6];
+    o[0] = i.b, o[1] = i.h, o[2] = i.t, o[3] = i.lo, o[4] = i.hi, o[5] = i.slot;
+    out.first[p] = i.first;
+  }
   out.nslots = next;
   out.slots = slots;
 }
@@ -251,7 +265,139 @@ void key_tile_list(const std::vector<int>& lq, const std::vector<int>& lkv, int 
   finish(raw, slots, split, out);
 }
 
+// Shared queries: the gradient of a query row is the sum over every sequence that uses it, so each
+// dQ piece writes an fp32 partial and one group per (head, query tile) sums the pieces of all
+// sequences in a fixed order (sequence, then range start). Group records name sequence 0, whose
+// offsets (row 0, Ls rows) address the shared dQ.
+void share_query_slots(List& L) {
+  const size_t n = L.n_items();
+  std::vector<int> idx(n);
+  for (size_t i = 0; i < n; ++i) idx[i] = (int)i;
+  auto key = [&](int i) { return std::make_tuple(L.items[i * 6 + 1], L.items[i * 6 + 2], L.items[i * 6], L.items[i * 6 + 3]); };
+  std::sort(idx.begin(), idx.end(), [&](int x, int y) { return key(x) < key(y); });
+  L.groups.clear();
+  int slot = 0;
+  for (size_t k = 0; k < n; ++k) {
+    const int i = idx[k];
+    const int h = L.items[i * 6 + 1], t = L.items[i * 6 + 2];
+    if (k == 0 || h != L.items[idx[k - 1] * 6 + 1] || t != L.items[idx[k - 1] * 6 + 2])
+      L.groups.insert(L.groups.end(), {0, h, t, slot, 0});
+    L.groups.back() += 1;  // R
+    L.items[i * 6 + 5] = slot++;
+  }
+  L.nslots = slot;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------- buffer cache
+// Work lists change with every batch of offsets, so planning sits on the training step's critical
+// path (vibekk.com GEM page, section on moving from padding to jagged kernels: once padding is gone,
+// time moves to tile scheduling). A plan therefore never synchronises: its records are written into
+// pinned host memory and uploaded with an asynchronous copy, and both buffers come from a small
+// process-wide cache. A cached buffer carries the events after which the device no longer uses it
+// (the upload, and the last forward / backward call on every stream that used the plan); it is
+// handed out again only once all of them have completed, so no wait is ever needed.
+struct CachedBuf {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  int device = -1;
+  bool pinned = false;
+  std::vector<hipEvent_t> pending;  // owned; the buffer is free once every one has completed
+};
+
+struct BufCache {
+  std::mutex mu;
+  std::vector<CachedBuf> free_bufs;
+  std::vector<hipEvent_t> free_events;
+};
+
+BufCache& buf_cache() {
+  static BufCache* c = new BufCache();  // never destroyed: plans may outlive static destructors
+  return *c;
+}
+
+hipEvent_t cache_event() {
+  BufCache& c = buf_cache();
+  {
+    std::lock_guard<std::mutex> lk(c.mu);
+    if (!c.free_events.empty()) {
+      hipEvent_t e = c.free_events.back();
+      c.free_events.pop_back();
+      return e;
+    }
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+  return e;
+}
+
+// A buffer of at least `bytes` (pinned host memory or device memory of `device`); rounded up to a
+// power of two from 64 KiB so that plans of similar size reuse each other's buffers.
+hipError_t cache_acquire(size_t bytes, bool pinned, int device, CachedBuf& out) {
+  size_t want = 65536;
+  while (want < bytes) want <<= 1;
+  BufCache& c = buf_cache();
+  {
+    std::lock_guard<std::mutex> lk(c.mu);
+    for (size_t i = 0; i < c.free_bufs.size(); ++i) {
+      CachedBuf& b = c.free_bufs[i];
+      if (b.pinned != pinned || b.device != device || b.bytes != want) continue;
+      bool done = true;
+      for (hipEvent_t e : b.pending)
+        if (hipEventQuery(e) != hipSuccess) done = false;
+      if (!done) continue;
+      for (hipEvent_t e : b.pending) c.free_events.push_back(e);
+      b.pending.clear();
+      out = b;
+      c.free_bufs.erase(c.free_bufs.begin() + (long)i);
+      return hipSuccess;
+    }
+  }
+  out = CachedBuf{};
+  out.bytes = want;
+  out.device = device;
+  out.pinned = pinned;
+  return pinned ? hipHostMalloc(&out.ptr, want, hipHostMallocDefault) : hipMalloc(&out.ptr, want);
+}
+
+void cache_release(CachedBuf& b) {
+  if (!b.ptr) return;
+  BufCache& c = buf_cache();
+  std::lock_guard<std::mutex> lk(c.mu);
+  c.free_bufs.push_back(b);
+  b = CachedBuf{};
+}
+
+// Device properties and kernel occupancies, queried once per device and kernel shape.
+struct DeviceInfo {
+  int cus = 0;
+  int occ[2][2][3] = {};  // [D == 128][kv_short][forward, dQ, dK/dV]; 0 = not yet queried
+};
+
+hipError_t device_info(int dev, const Modes& m, int& cus, int occ[3]) {
+  static std::mutex mu;
+  static std::vector<DeviceInfo> infos;
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)infos.size() <= dev) infos.resize(dev + 1);
+  DeviceInfo& d = infos[dev];
+  if (d.cus == 0) {
+    hipError_t e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) {
+      d.cus = 0;
+      return e;
+    }
+  }
+  int* o = d.occ[m.D == 128][m.kv_short];
+  if (o[0] == 0) {
+    o[0] = occupancy_forward(m);
+    o[1] = occupancy_dq(m);
+    o[2] = occupancy_dkdv(m);
+  }
+  cus = d.cus;
+  std::copy_n(o, 3, occ);
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -262,11 +408,16 @@ struct jfa_plan_s {
   Band band{};
   float scale = 0.0f;
   int out_f32 = 0, grad_f32 = 0;
+  int q_shared = 0;  // JFA_PLAN_SHARED_Q
   uint32_t flags = 0;
   std::vector<int32_t> q_off, kv_off;
   List lists[3];
-  void* dev = nullptr;  // device copy of all work lists
+  CachedBuf dev;        // device copy of all work lists (from the buffer cache)
   int device = -1;
+  // Last use of the device lists on each stream (the upload's stream included): the buffer goes back
+  // to the cache with these events and is not handed out again before they have all completed.
+  std::mutex use_mu;
+  std::vector<std::pair<hipStream_t, hipEvent_t>> uses;
   // workspace layout
   size_t ws_fwd = 0, off_part_lse = 0;
   size_t ws_bwd = 0, off_delta = 0, off_part_dq = 0, off_part_dk = 0, off_part_dv = 0, off_dbias = 0;
@@ -297,8 +448,11 @@ jfa_status check_problem(const jfa_problem* p, std::vector<int>& lq, std::vector
   if (p->out_dtype < 0 || p->out_dtype > 1 || p->grad_dtype < 0 || p->grad_dtype > 1)
     return fail(JFA_ERR_UNSUPPORTED, "unknown dtype");
   if (p->num_slots < 0) return fail(JFA_ERR_BAD_SHAPE, "num_slots must be >= 0");
-  if (!std::isfinite(p->scale)) return fail(JFA_ERR_UNSUPPORTED, "scale must be finite");
-  if ((p->flags & ~(JFA_PLAN_HOST_ONLY | JFA_PLAN_NO_SPLIT)) != 0) return fail(JFA_ERR_UNSUPPORTED, "unknown flags");
+  // A negative scale would flip the order of the scores that the masks rely on (-inf stays the
+  // smallest score only for a non-negative multiplier).
+  if (!std::isfinite(p->scale) || p->scale < 0.0f) return fail(JFA_ERR_UNSUPPORTED, "scale must be finite and >= 0");
+  if ((p->flags & ~(JFA_PLAN_HOST_ONLY | JFA_PLAN_NO_SPLIT | JFA_PLAN_SHARED_Q)) != 0)
+    return fail(JFA_ERR_UNSUPPORTED, "unknown flags");
   if (p->window < 0 || p->block < 0) return fail(JFA_ERR_BAD_SHAPE, "window and block must be >= 0");
   const int B = p->num_seqs;
   if (p->q_offsets_host[0] != 0 || p->kv_offsets_host[0] != 0) return fail(JFA_ERR_BAD_OFFSETS, "offsets[0] must be 0");
@@ -310,12 +464,25 @@ jfa_status check_problem(const jfa_problem* p, std::vector<int>& lq, std::vector
     if (a < 0 || c < 0) return fail(JFA_ERR_BAD_OFFSETS, "offsets must be non-decreasing (sequence " + std::to_string(b) + ")");
     lq[b] = (int)a;
     lkv[b] = (int)c;
-    if (p->mask == JFA_MASK_CAUSAL && a != c)
-      return fail(JFA_ERR_BAD_SHAPE, "causal mask needs Lq == Lkv (sequence " + std::to_string(b) + ")");
+    // Causal: j <= i. With more queries than keys, the rows past the keys are target rows that see
+    // every key (the fused self + target pass); fewer queries than keys has no such reading.
+    if (p->mask == JFA_MASK_CAUSAL && a < c)
+      return fail(JFA_ERR_BAD_SHAPE, "causal mask needs Lq >= Lkv (sequence " + std::to_string(b) + ")");
+    if ((p->flags & JFA_PLAN_SHARED_Q) && a != lq[0])
+      return fail(JFA_ERR_BAD_SHAPE, "shared queries need the same Lq for every sequence (sequence " + std::to_string(b) + ")");
   }
   const int64_t tq = p->q_offsets_host[B], tkv = p->kv_offsets_host[B];
   if (tq * p->num_heads * (int64_t)p->head_dim >= ((int64_t)1 << 40) || tkv * p->num_heads * (int64_t)p->head_dim >= ((int64_t)1 << 40))
     return fail(JFA_ERR_BAD_SHAPE, "tensor too large");
+  // The kernels address a (sequence, head) slice with signed 32-bit byte offsets from its first row,
+  // up to one tile (at most 128 rows) past its end where ragged tails read zeros: (L + 128) rows of
+  // H * D elements must stay within 2^30 elements (2^31 bytes).
+  for (int b = 0; b < B; ++b) {
+    const int64_t L = std::max(lq[b], lkv[b]);
+    if (L > 0 && (L + 128) * p->num_heads * (int64_t)p->head_dim > kMaxSliceElems)
+      return fail(JFA_ERR_BAD_SHAPE, "sequence " + std::to_string(b) + " spans more than 2^30 elements of a [T, H, D] "
+                                     "tensor (its length times H times D); split it or shard the heads");
+  }
   return JFA_OK;
 }
 
@@ -349,19 +516,161 @@ jfa_status timed(jfa_plan_s* P, int kernel, hipStream_t s, F fn, const char* wha
   return JFA_OK;
 }
 
+// With JFA_DEBUG=1 in the environment, device offsets passed to a pass are copied back (a
+// synchronising check) and compared with the offsets the plan was built from.
 jfa_status debug_check_offsets(jfa_plan_s* P, const int32_t* dq, const int32_t* dkv, hipStream_t s) {
-  static const bool on = [] {
-    const char* v = std::getenv("JFA_DEBUG");
-    return v && v[0] == '1';
-  }();
-  if (!on) return JFA_OK;
+  const char* env = std::getenv("JFA_DEBUG");
+  if (!env || env[0] != '1' || (!dq && !dkv)) return JFA_OK;
   std::vector<int32_t> a(P->B + 1), b(P->B + 1);
   if (hipStreamSynchronize(s) != hipSuccess) return fail(JFA_ERR_HIP, "JFA_DEBUG sync failed");
-  if (hipMemcpy(a.data(), dq, a.size() * 4, hipMemcpyDeviceToHost) != hipSuccess ||
-      hipMemcpy(b.data(), dkv, b.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+  if ((dq && hipMemcpy(a.data(), dq, a.size() * 4, hipMemcpyDeviceToHost) != hipSuccess) ||
+      (dkv && hipMemcpy(b.data(), dkv, b.size() * 4, hipMemcpyDeviceToHost) != hipSuccess))
     return fail(JFA_ERR_HIP, "JFA_DEBUG offset copy failed");
-  if (a != P->q_off || b != P->kv_off) return fail(JFA_ERR_BAD_OFFSETS, "device offsets differ from the planned host offsets");
+  if ((dq && a != P->q_off) || (dkv && b != P->kv_off))
+    return fail(JFA_ERR_BAD_OFFSETS, "device offsets differ from the planned host offsets");
   return JFA_OK;
+}
+
+// ---------------------------------------------------------------- forward / backward
+// Argument checks of one pass (everything but the workspace), before any launch.
+jfa_status check_forward(jfa_plan_s* P, const void* q, const void* k, const void* v, const float* bias,
+                         const void* out, const float* lse) {
+  if (!P) return fail(JFA_ERR_NULL_ARG, "plan is NULL");
+  if (P->flags & JFA_PLAN_HOST_ONLY) return fail(JFA_ERR_HOST_ONLY, "plan was built host-only");
+  const bool softmax = P->modes.act == kSoftmax;
+  if (!q || !k || !v || !out) return fail(JFA_ERR_NULL_ARG, "a tensor pointer is NULL");
+  if (P->modes.bias != kBiasNone && !bias) return fail(JFA_ERR_NULL_ARG, "bias is NULL");
+  if (softmax && !lse) return fail(JFA_ERR_NULL_ARG, "lse is NULL (required for softmax)");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)) ||
+      (bias && !aligned16(bias)))
+    return fail(JFA_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
+  return JFA_OK;
+}
+
+jfa_status check_backward(jfa_plan_s* P, const void* q, const void* k, const void* v, const float* bias,
+                          const void* out, const float* lse, const void* dout, const void* dq, const void* dk,
+                          const void* dv, const float* dbias) {
+  if (!P) return fail(JFA_ERR_NULL_ARG, "plan is NULL");
+  if (P->flags & JFA_PLAN_HOST_ONLY) return fail(JFA_ERR_HOST_ONLY, "plan was built host-only");
+  const bool softmax = P->modes.act == kSoftmax;
+  if (dbias && P->modes.bias == kBiasNone) return fail(JFA_ERR_UNSUPPORTED, "dbias requested without a bias");
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return fail(JFA_ERR_NULL_ARG, "a tensor pointer is NULL");
+  if (P->modes.bias != kBiasNone && !bias) return fail(JFA_ERR_NULL_ARG, "bias is NULL");
+  if (softmax && (!out || !lse)) return fail(JFA_ERR_NULL_ARG, "out and lse are required for softmax");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || (out && !aligned16(out)) || (lse && !aligned16(lse)) || (bias && !aligned16(bias)) ||
+      (dbias && !aligned16(dbias)))
+    return fail(JFA_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
+  return JFA_OK;
+}
+
+// Launches of one pass on stream s with a checked workspace of the plan's size.
+jfa_status run_forward(jfa_plan_s* P, const void* q, const void* k, const void* v, const float* bias, void* out,
+                       float* lse, void* workspace, hipStream_t s) {
+  FwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.bias = bias;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + P->off_part_lse) : nullptr;
+  a.items = P->lists[kFwd].d_items;
+  a.groups = P->lists[kFwd].d_groups;
+  a.H = P->H;
+  a.Tq = P->Tq;
+  a.scale = P->scale;
+  a.out_f32 = P->out_f32;
+  a.band = P->band;
+  a.q_shared = P->q_shared;
+  const List& L = P->lists[kFwd];
+  jfa_status st = timed(P, 0, s, [&] { return launch_forward(a, P->modes, (int)L.n_items(), s); }, "forward launch");
+  if (st != JFA_OK) return st;
+  if (L.n_groups() > 0)
+    st = timed(P, 1, s, [&] { return launch_forward_combine(a, P->modes, (int)L.n_groups(), s); }, "combine launch");
+  return st;
+}
+
+jfa_status run_backward(jfa_plan_s* P, const void* q, const void* k, const void* v, const float* bias,
+                        const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        float* dbias, void* workspace, hipStream_t s) {
+  char* ws = static_cast<char*>(workspace);
+  BwdArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.bias = bias;
+  a.out = out;
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = ws ? reinterpret_cast<float*>(ws + P->off_delta) : nullptr;
+  a.part_dq = ws ? reinterpret_cast<float*>(ws + P->off_part_dq) : nullptr;
+  a.part_dk = ws ? reinterpret_cast<float*>(ws + P->off_part_dk) : nullptr;
+  a.part_dv = ws ? reinterpret_cast<float*>(ws + P->off_part_dv) : nullptr;
+  a.dbias_acc = (ws && dbias) ? reinterpret_cast<unsigned long long*>(ws + P->off_dbias) : nullptr;
+  a.dbias = dbias;
+  a.dq_items = P->lists[kDq].d_items;
+  a.dq_groups = P->lists[kDq].d_groups;
+  a.kv_items = P->lists[kKv].d_items;
+  a.kv_groups = P->lists[kKv].d_groups;
+  a.H = P->H;
+  a.Tq = P->Tq;
+  a.Tkv = P->Tkv;
+  a.scale = P->scale;
+  a.out_f32 = P->out_f32;
+  a.band = P->band;
+  a.grad_f32 = P->grad_f32;
+  a.kv_bn = P->kv_bn;
+  a.kv_queue = (ws && P->D == 128) ? reinterpret_cast<int*>(ws + P->off_queue) : nullptr;
+  a.kv_n = (int)P->lists[kKv].n_items();
+  a.q_shared = P->q_shared;
+  Modes m = P->modes;
+  m.dbias = dbias ? 1 : 0;
+  jfa_status st = JFA_OK;
+  // The queue counters are zeroed by the dQ kernel, or here when there is no dQ item.
+  if (dbias || (a.kv_queue && P->lists[kDq].n_items() == 0 && a.kv_n > 0)) {
+    st = timed(P, 6, s, [&] { return launch_bwd_dbias_clear(a, m, s); }, "bias-gradient clear launch");
+    if (st != JFA_OK) return st;
+  }
+  // dQ first: it also computes Delta = rowsum(dO * O) (softmax) for the dK/dV kernel.
+  st = timed(P, 4, s, [&] { return launch_bwd_dq(a, m, (int)P->lists[kDq].n_items(), s); }, "dQ launch");
+  if (st != JFA_OK) return st;
+  // The persistent dK/dV kernel (D = 128, full-width items) takes the dQ partial sums once its items
+  // are exhausted; otherwise a reduce kernel does.
+  const int dq_groups = (int)P->lists[kDq].n_groups();
+  const bool dq_in_kv = P->D == 128 && !P->modes.kv_short && a.kv_n > 0 && dq_groups > 0;
+  a.dq_reduce_n = dq_in_kv ? dq_groups : 0;
+  if (dq_groups > 0 && !dq_in_kv) {
+    st = timed(P, 5, s, [&] { return launch_bwd_reduce_dq(a, m, dq_groups, s); }, "dQ reduce launch");
+    if (st != JFA_OK) return st;
+  }
+  st = timed(P, 3, s, [&] { return launch_bwd_dkdv(a, m, a.kv_n, P->kv_resident, s); }, "dK/dV launch");
+  if (st != JFA_OK) return st;
+  if (P->lists[kKv].n_groups() > 0) {
+    st = timed(P, 5, s, [&] { return launch_bwd_reduce_dkdv(a, m, (int)P->lists[kKv].n_groups(), s); }, "dK/dV reduce launch");
+    if (st != JFA_OK) return st;
+  }
+  if (dbias) st = timed(P, 6, s, [&] { return launch_bwd_dbias_finish(a, m, s); }, "bias-gradient finish launch");
+  return st;
+}
+
+// Record that the plan's device lists are read by work enqueued on stream s (up to this point).
+jfa_status note_use(jfa_plan_s* P, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(P->use_mu);
+  for (auto& u : P->uses)
+    if (u.first == s) {
+      const hipError_t e = hipEventRecord(u.second, s);
+      return e == hipSuccess ? JFA_OK : hip_fail(e, "event record");
+    }
+  hipEvent_t ev = cache_event();
+  if (!ev) return fail(JFA_ERR_HIP, "event creation failed");
+  const hipError_t e = hipEventRecord(ev, s);
+  P->uses.push_back({s, ev});  // kept even on failure, so that the event is recycled with the plan
+  return e == hipSuccess ? JFA_OK : hip_fail(e, "event record");
 }
 
 }  // namespace
@@ -402,36 +711,26 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   const bool split = (p.flags & JFA_PLAN_NO_SPLIT) == 0;
 
   int slots[3] = {p.num_slots, p.num_slots, p.num_slots};
-  if (p.num_slots == 0) {
-    if (host_only) {
-      slots[0] = slots[1] = slots[2] = 512;
-    } else {
-      int dev = 0, cus = 0;
-      hipError_t e = hipGetDevice(&dev);
-      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      if (e != hipSuccess) {
-        delete P;
-        return hip_fail(e, "device query");
-      }
-      slots[kFwd] = cus * occupancy_forward(P->modes);
-      slots[kDq] = cus * occupancy_dq(P->modes);
-      slots[kKv] = cus * occupancy_dkdv(P->modes);
-    }
-  }
   if (!host_only) {
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0, occ[3] = {1, 1, 1};
+    hipError_t e = hipGetDevice(&P->device);
+    if (e == hipSuccess) e = device_info(P->device, P->modes, cus, occ);
     if (e != hipSuccess) {
       delete P;
       return hip_fail(e, "device query");
     }
-    P->kv_resident = std::max(1, cus * occupancy_dkdv(P->modes));
+    if (p.num_slots == 0)
+      for (int l = 0; l < 3; ++l) slots[l] = cus * occ[l];
+    P->kv_resident = std::max(1, cus * occ[kKv]);
+  } else if (p.num_slots == 0) {
+    slots[0] = slots[1] = slots[2] = 512;
   }
   const Limits lim{P->modes.causal != 0, p.window, p.block};
   query_tile_list(lq, lkv, P->H, lim, kFwdBM, kFwdBN, slots[kFwd], split, P->lists[kFwd]);
   query_tile_list(lq, lkv, P->H, lim, kDqBM, kDqBN, slots[kDq], split, P->lists[kDq]);
   key_tile_list(lq, lkv, P->H, lim, kKvBM, P->kv_bn, slots[kKv], split, P->lists[kKv]);
+  P->q_shared = (p.flags & JFA_PLAN_SHARED_Q) ? 1 : 0;
+  if (P->q_shared) share_query_slots(P->lists[kDq]);
   for (auto& L : P->lists) L.order = dispatch_order(L, P->B, P->H);
 
   // workspace layout
@@ -456,11 +755,22 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   if (P->lists[kFwd].nslots == 0) P->ws_fwd = 0;
 
   if (!host_only) {
-    // device records (kItemInts / kGroupInts int32 each): the list fields followed by the
-    // sequence's offsets and lengths, so that a workgroup needs no second, dependent load
+    // Device records (kItemInts / kGroupInts int32 each): the list fields followed by the sequence's
+    // offsets and lengths, so that a workgroup needs no second, dependent load. They are written
+    // straight into pinned staging memory and uploaded asynchronously; nothing waits for the copy.
     size_t total = 0;
     for (auto& L : P->lists) total += L.n_items() * kItemInts + L.n_groups() * kGroupInts;
-    std::vector<int32_t> host(std::max<size_t>(total, kItemInts), 0);
+    total = std::max<size_t>(total, kItemInts);
+    CachedBuf stage;
+    hipError_t e = cache_acquire(total * 4, true, P->device, stage);
+    if (e == hipSuccess) e = cache_acquire(total * 4, false, P->device, P->dev);
+    if (e != hipSuccess) {
+      cache_release(stage);
+      cache_release(P->dev);
+      delete P;
+      return hip_fail(e, "plan buffer allocation");
+    }
+    int32_t* host = static_cast<int32_t*>(stage.ptr);
     auto put_seq = [&](int32_t* r, int b) {
       r[0] = P->q_off[b];
       r[1] = P->q_off[b + 1] - P->q_off[b];
@@ -472,38 +782,45 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
     for (int l = 0; l < 3; ++l) {
       List& L = P->lists[l];
       offs[l][0] = pos;
-      std::vector<char> first_slot(L.nslots, 0);  // slot of the first piece of each split item
-      for (size_t g = 0; g < L.n_groups(); ++g) first_slot[L.groups[g * 5 + 3]] = 1;
       for (size_t i = 0; i < L.n_items(); ++i, pos += kItemInts) {
         const int32_t* it = &L.items[(size_t)L.order[i] * 6];
-        std::copy_n(it, 6, &host[pos]);
-        put_seq(&host[pos + 6], it[0]);
-        host[pos + 10] = (it[5] < 0 || first_slot[it[5]]) ? 1 : 0;
+        int32_t* r = host + pos;
+        std::copy_n(it, 6, r);
+        put_seq(r + 6, it[0]);
+        r[10] = L.first[(size_t)L.order[i]] ? 1 : 0;
+        std::fill(r + 11, r + kItemInts, 0);
       }
       offs[l][1] = pos;
       for (size_t g = 0; g < L.n_groups(); ++g, pos += kGroupInts) {
         const int32_t* gr = &L.groups[g * 5];
-        std::copy_n(gr, 5, &host[pos]);
-        put_seq(&host[pos + 5], gr[0]);
+        int32_t* r = host + pos;
+        std::copy_n(gr, 5, r);
+        put_seq(r + 5, gr[0]);
+        std::fill(r + 9, r + kGroupInts, 0);
       }
     }
-    hipError_t e = hipGetDevice(&P->device);
-    if (e == hipSuccess) e = hipMalloc(&P->dev, host.size() * 4);
+    if (pos == 0) std::fill(host, host + kItemInts, 0);
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t copied = cache_event(), used = cache_event();
+    e = (copied && used) ? hipMemcpyAsync(P->dev.ptr, host, total * 4, hipMemcpyHostToDevice, s) : hipErrorOutOfMemory;
+    if (e == hipSuccess) e = hipEventRecord(copied, s);
+    if (e == hipSuccess) e = hipEventRecord(used, s);
     if (e != hipSuccess) {
-      delete P;
-      return hip_fail(e, "plan device allocation");
-    }
-    // synchronous copy: the host staging vector dies with this call
-    e = hipMemcpyAsync(P->dev, host.data(), host.size() * 4, hipMemcpyHostToDevice, (hipStream_t)stream);
-    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
-    if (e != hipSuccess) {
-      (void)hipFree(P->dev);
+      // the copy may be in flight: wait for the stream before the buffers can be reused
+      (void)hipStreamSynchronize(s);
+      for (hipEvent_t x : {copied, used})
+        if (x) (void)hipEventDestroy(x);
+      cache_release(stage);
+      cache_release(P->dev);
       delete P;
       return hip_fail(e, "plan upload");
     }
+    stage.pending.push_back(copied);  // the staging memory is reusable once the copy has run
+    cache_release(stage);
+    P->uses.push_back({s, used});
     for (int l = 0; l < 3; ++l) {
-      P->lists[l].d_items = static_cast<int32_t*>(P->dev) + offs[l][0];
-      P->lists[l].d_groups = static_cast<int32_t*>(P->dev) + offs[l][1];
+      P->lists[l].d_items = static_cast<int32_t*>(P->dev.ptr) + offs[l][0];
+      P->lists[l].d_groups = static_cast<int32_t*>(P->dev.ptr) + offs[l][1];
     }
   }
   *plan_out = P;
@@ -520,130 +837,34 @@ jfa_status jfa_workspace_bytes(jfa_plan_t P, size_t* fwd_bytes, size_t* bwd_byte
 jfa_status jfa_forward(jfa_plan_t P, const void* q, const void* k, const void* v, const int32_t* q_offsets,
                        const int32_t* kv_offsets, const float* bias, void* out, float* lse, void* workspace,
                        size_t workspace_bytes, jfa_stream_t stream) {
-  if (!P) return fail(JFA_ERR_NULL_ARG, "plan is NULL");
-  if (P->flags & JFA_PLAN_HOST_ONLY) return fail(JFA_ERR_HOST_ONLY, "plan was built host-only");
-  const bool softmax = P->modes.act == kSoftmax;
-  if (!q || !k || !v || !q_offsets || !kv_offsets || !out) return fail(JFA_ERR_NULL_ARG, "a tensor or offsets pointer is NULL");
-  if (P->modes.bias != kBiasNone && !bias) return fail(JFA_ERR_NULL_ARG, "bias is NULL");
-  if (softmax && !lse) return fail(JFA_ERR_NULL_ARG, "lse is NULL (required for softmax)");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)) ||
-      (bias && !aligned16(bias)) || !aligned16(workspace))
-    return fail(JFA_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
+  jfa_status st = check_forward(P, q, k, v, bias, out, lse);
+  if (st != JFA_OK) return st;
+  if (!aligned16(workspace)) return fail(JFA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   if (workspace_bytes < P->ws_fwd || (P->ws_fwd > 0 && !workspace))
     return fail(JFA_ERR_WORKSPACE, "forward workspace needs " + std::to_string(P->ws_fwd) + " bytes");
   hipStream_t s = (hipStream_t)stream;
-  jfa_status st = debug_check_offsets(P, q_offsets, kv_offsets, s);
+  st = debug_check_offsets(P, q_offsets, kv_offsets, s);
   if (st != JFA_OK) return st;
-
-  FwdArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.q_off = q_offsets;
-  a.kv_off = kv_offsets;
-  a.bias = bias;
-  a.out = out;
-  a.lse = lse;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + P->off_part_lse) : nullptr;
-  a.items = P->lists[kFwd].d_items;
-  a.groups = P->lists[kFwd].d_groups;
-  a.H = P->H;
-  a.Tq = P->Tq;
-  a.scale = P->scale;
-  a.out_f32 = P->out_f32;
-  a.band = P->band;
-  const List& L = P->lists[kFwd];
-  st = timed(P, 0, s, [&] { return launch_forward(a, P->modes, (int)L.n_items(), s); }, "forward launch");
-  if (st != JFA_OK) return st;
-  if (L.n_groups() > 0)
-    st = timed(P, 1, s, [&] { return launch_forward_combine(a, P->modes, (int)L.n_groups(), s); }, "combine launch");
-  return st;
+  st = run_forward(P, q, k, v, bias, out, lse, workspace, s);
+  const jfa_status su = note_use(P, s);
+  return st != JFA_OK ? st : su;
 }
 
 jfa_status jfa_backward(jfa_plan_t P, const void* q, const void* k, const void* v, const int32_t* q_offsets,
                         const int32_t* kv_offsets, const float* bias, const void* out, const float* lse,
                         const void* dout, void* dq, void* dk, void* dv, float* dbias, void* workspace,
                         size_t workspace_bytes, jfa_stream_t stream) {
-  if (!P) return fail(JFA_ERR_NULL_ARG, "plan is NULL");
-  if (P->flags & JFA_PLAN_HOST_ONLY) return fail(JFA_ERR_HOST_ONLY, "plan was built host-only");
-  const bool softmax = P->modes.act == kSoftmax;
-  if (dbias && P->modes.bias == kBiasNone) return fail(JFA_ERR_UNSUPPORTED, "dbias requested without a bias");
-  if (!q || !k || !v || !q_offsets || !kv_offsets || !dout || !dq || !dk || !dv)
-    return fail(JFA_ERR_NULL_ARG, "a tensor or offsets pointer is NULL");
-  if (P->modes.bias != kBiasNone && !bias) return fail(JFA_ERR_NULL_ARG, "bias is NULL");
-  if (softmax && (!out || !lse)) return fail(JFA_ERR_NULL_ARG, "out and lse are required for softmax");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
-      !aligned16(dv) || (out && !aligned16(out)) || (lse && !aligned16(lse)) || (bias && !aligned16(bias)) ||
-      (dbias && !aligned16(dbias)) || !aligned16(workspace))
-    return fail(JFA_ERR_MISALIGNED, "tensor pointers must be 16-byte aligned");
+  jfa_status st = check_backward(P, q, k, v, bias, out, lse, dout, dq, dk, dv, dbias);
+  if (st != JFA_OK) return st;
+  if (!aligned16(workspace)) return fail(JFA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   if (workspace_bytes < P->ws_bwd || (P->ws_bwd > 0 && !workspace))
     return fail(JFA_ERR_WORKSPACE, "backward workspace needs " + std::to_string(P->ws_bwd) + " bytes");
   hipStream_t s = (hipStream_t)stream;
-  jfa_status st = debug_check_offsets(P, q_offsets, kv_offsets, s);
+  st = debug_check_offsets(P, q_offsets, kv_offsets, s);
   if (st != JFA_OK) return st;
-
-  char* ws = static_cast<char*>(workspace);
-  BwdArgs a{};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.q_off = q_offsets;
-  a.kv_off = kv_offsets;
-  a.bias = bias;
-  a.out = out;
-  a.lse = lse;
-  a.dout = static_cast<const uint16_t*>(dout);
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.delta = ws ? reinterpret_cast<float*>(ws + P->off_delta) : nullptr;
-  a.part_dq = ws ? reinterpret_cast<float*>(ws + P->off_part_dq) : nullptr;
-  a.part_dk = ws ? reinterpret_cast<float*>(ws + P->off_part_dk) : nullptr;
-  a.part_dv = ws ? reinterpret_cast<float*>(ws + P->off_part_dv) : nullptr;
-  a.dbias_acc = (ws && dbias) ? reinterpret_cast<unsigned long long*>(ws + P->off_dbias) : nullptr;
-  a.dbias = dbias;
-  a.dq_items = P->lists[kDq].d_items;
-  a.dq_groups = P->lists[kDq].d_groups;
-  a.kv_items = P->lists[kKv].d_items;
-  a.kv_groups = P->lists[kKv].d_groups;
-  a.H = P->H;
-  a.Tq = P->Tq;
-  a.Tkv = P->Tkv;
-  a.scale = P->scale;
-  a.out_f32 = P->out_f32;
-  a.band = P->band;
-  a.grad_f32 = P->grad_f32;
-  a.kv_bn = P->kv_bn;
-  a.kv_queue = (ws && P->D == 128) ? reinterpret_cast<int*>(ws + P->off_queue) : nullptr;
-  a.kv_n = (int)P->lists[kKv].n_items();
-  Modes m = P->modes;
-  m.dbias = dbias ? 1 : 0;
-  // The queue counters are zeroed by the dQ kernel, or here when there is no dQ item.
-  if (dbias || (a.kv_queue && P->lists[kDq].n_items() == 0 && a.kv_n > 0)) {
-    st = timed(P, 6, s, [&] { return launch_bwd_dbias_clear(a, m, s); }, "bias-gradient clear launch");
-    if (st != JFA_OK) return st;
-  }
-  // dQ first: it also computes Delta = rowsum(dO * O) (softmax) for the dK/dV kernel.
-  st = timed(P, 4, s, [&] { return launch_bwd_dq(a, m, (int)P->lists[kDq].n_items(), s); }, "dQ launch");
-  if (st != JFA_OK) return st;
-  // The persistent dK/dV kernel (D = 128, full-width items) takes the dQ partial sums once its items
-  // are exhausted; otherwise a reduce kernel does.
-  const int dq_groups = (int)P->lists[kDq].n_groups();
-  const bool dq_in_kv = P->D == 128 && !P->modes.kv_short && a.kv_n > 0 && dq_groups > 0;
-  a.dq_reduce_n = dq_in_kv ? dq_groups : 0;
-  if (dq_groups > 0 && !dq_in_kv) {
-    st = timed(P, 5, s, [&] { return launch_bwd_reduce_dq(a, m, dq_groups, s); }, "dQ reduce launch");
-    if (st != JFA_OK) return st;
-  }
-  st = timed(P, 3, s, [&] { return launch_bwd_dkdv(a, m, a.kv_n, P->kv_resident, s); }, "dK/dV launch");
-  if (st != JFA_OK) return st;
-  if (P->lists[kKv].n_groups() > 0) {
-    st = timed(P, 5, s, [&] { return launch_bwd_reduce_dkdv(a, m, (int)P->lists[kKv].n_groups(), s); }, "dK/dV reduce launch");
-    if (st != JFA_OK) return st;
-  }
-  if (dbias) st = timed(P, 6, s, [&] { return launch_bwd_dbias_finish(a, m, s); }, "bias-gradient finish launch");
-  return st;
+  st = run_backward(P, q, k, v, bias, out, lse, dout, dq, dk, dv, dbias, workspace, s);
+  const jfa_status su = note_use(P, s);
+  return st != JFA_OK ? st : su;
 }
 
 jfa_status jfa_plan_schedule(jfa_plan_t P, int32_t which, int32_t* out, size_t cap, size_t* count) {
@@ -700,7 +921,12 @@ jfa_status jfa_timing_read(jfa_plan_t P, int32_t kernel, float* total_ms, int32_
 
 void jfa_plan_destroy(jfa_plan_t P) {
   if (!P) return;
-  if (P->dev) (void)hipFree(P->dev);
+  if (P->dev.ptr) {
+    // The lists go back to the cache with the last use on every stream; no wait here.
+    for (auto& u : P->uses) P->dev.pending.push_back(u.second);
+    P->uses.clear();
+    cache_release(P->dev);
+  }
   for (hipEvent_t e : P->pool) (void)hipEventDestroy(e);
   delete P;
 }

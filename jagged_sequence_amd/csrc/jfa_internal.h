@@ -26,6 +26,8 @@ constexpr int kThreads = 256;
 constexpr int kItemInts = 16;
 constexpr int kGroupInts = 16;
 constexpr int kBuckets = 64;
+// Largest (sequence, head) slice of a [T, H, D] tensor the kernels address with 32-bit offsets.
+constexpr long long kMaxSliceElems = 1ll << 30;
 // Work queues of the persistent dK/dV kernel (D = 128): one per XCD, then one counter of the dQ
 // partial-sum tasks that the same kernel takes once its items are exhausted.
 constexpr int kQueues = 8;
@@ -49,8 +51,6 @@ struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const int32_t* q_off;
-  const int32_t* kv_off;
   const float* bias;
   void* out;
   float* lse;
@@ -63,14 +63,13 @@ struct FwdArgs {
   float scale;
   int out_f32;
   Band band;
+  int q_shared;  // every sequence reads query rows from row 0 of q (shared queries); out and lse stay per sequence
 };
 
 struct BwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const int32_t* q_off;
-  const int32_t* kv_off;
   const float* bias;
   const void* out;
   const float* lse;
@@ -99,6 +98,7 @@ struct BwdArgs {
   int kv_n;       // dK/dV items
   int dq_reduce_n;  // dQ split groups whose fixed-order sums the persistent dK/dV kernel takes (else 0)
   Band band;
+  int q_shared;  // query rows shared by every sequence (read from row 0 of q); dq is summed over sequences
 };
 
 struct Modes {

@@ -52,6 +52,8 @@ class Workload:
     description: str = ""
     window: int = 0               # sliding-window limit (0 = off)
     block: int = 0                # block-attention limit (0 = off)
+    q_extra_law: Optional[tuple] = None  # target rows appended to each sequence's queries (fused self + target)
+    shared_q: int = 0             # > 0: that many query rows shared by every sequence (PMA seeds)
 
 
 WORKLOADS = {
@@ -85,6 +87,23 @@ WORKLOADS = {
         Workload("longtail_swa", 5, 512, 8, 128, ("pareto", 1.2, 128, 32768), None, "causal", "softmax",
                  "bucket", 0.5, window=1024,
                  description="as longtail with a causal sliding window of 1024 keys"),
+        # Fused self + target attention (in-kernel broadcast inference co-designed with the model): each
+        # user's history attends causally to itself and the user's candidates, appended after the
+        # history, attend to the whole history, in one pass over one K/V copy per user. The pages give
+        # no sizes; the history law is the causal workload's, the candidate count that of the
+        # target-attention workload.
+        Workload("self_target", 6, 256, 8, 128, ("lognormal", 512, 64, 4096), None, "causal", "softmax", "scalar",
+                 0.1, q_extra_law=("uniform", 1, 64),
+                 description="fused self + target: B=256 users, history~lognormal(512,1) in [64,4096] "
+                             "(causal self-attention), then U[1,64] candidate rows that see the whole history; "
+                             "H=8, D=128, scalar bias ~N(0,0.1)"),
+        # Pooling by multihead attention: 32 learned seed queries shared by every sequence, attending
+        # with a GDPA activation (the pages list PMA with self- and cross-attention under GDPA). The
+        # pages give no sizes; the sequence law is the target-attention workload's history.
+        Workload("pma_seeds", 7, 512, 8, 128, ("uniform", 32, 32), ("lognormal", 1024, 64, 16384), "none", "silu",
+                 "none", shared_q=32,
+                 description="PMA: 32 seed queries shared by B=512 sequences, Lkv~lognormal(1024,1) in "
+                             "[64,16384], GDPA SiLU/Lkv, H=8, D=128"),
     ]
 }
 
@@ -108,8 +127,12 @@ def _draw(law: tuple, n: int, rng: np.random.Generator) -> np.ndarray:
 def lengths(w: Workload) -> tuple[np.ndarray, np.ndarray]:
     """Per-sequence (Lq, Lkv) as int64 arrays, drawn from ``default_rng(0)``."""
     rng = np.random.default_rng(0)
+    if w.shared_q:
+        return np.full(w.B, w.shared_q, dtype=np.int64), _draw(w.kv_law, w.B, rng)
     lq = _draw(w.q_law, w.B, rng)
     lkv = lq.copy() if w.kv_law is None else _draw(w.kv_law, w.B, rng)
+    if w.q_extra_law is not None:  # queries = keys' rows followed by extra (target) rows
+        lq = lq + _draw(w.q_extra_law, w.B, rng)
     return lq, lkv
 
 
@@ -156,6 +179,7 @@ class Inputs:
     bias_kind: str
     window: int = 0
     block: int = 0
+    shared_q: bool = False        # q holds one set of Lq rows shared by every sequence
 
     @property
     def B(self) -> int:
@@ -164,15 +188,21 @@ class Inputs:
 
 def make_inputs(lq, lkv, H: int, D: int, *, wid: int, mask: str = "none", act: str = "softmax",
                 bias_kind: str = "none", bias_sigma: float = 0.5, with_do: bool = True, window: int = 0,
-                block: int = 0) -> Inputs:
-    """Operands for arbitrary per-sequence lengths, from the value streams of id ``wid``."""
+                block: int = 0, shared_q: bool = False) -> Inputs:
+    """Operands for arbitrary per-sequence lengths, from the value streams of id ``wid``.
+
+    ``shared_q``: every Lq must be equal and ``q`` holds that many rows once, shared by all sequences
+    (``dout`` stays per sequence)."""
     if mask not in MASKS or act not in ACTS or bias_kind not in BIASES:
         raise ValueError("bad mode")
     lq = np.asarray(lq, dtype=np.int64)
     lkv = np.asarray(lkv, dtype=np.int64)
     q_off, kv_off = offsets(lq), offsets(lkv)
     tq, tkv = int(q_off[-1]), int(kv_off[-1])
-    q = bf16_normal_bits((wid, _T_Q), tq * H * D).reshape(tq, H, D)
+    if shared_q and len(set(lq.tolist())) > 1:
+        raise ValueError("shared queries need equal Lq")
+    nq = int(lq[0]) if shared_q and len(lq) else tq
+    q = bf16_normal_bits((wid, _T_Q), nq * H * D).reshape(nq, H, D)
     k = bf16_normal_bits((wid, _T_K), tkv * H * D).reshape(tkv, H, D)
     v = bf16_normal_bits((wid, _T_V), tkv * H * D).reshape(tkv, H, D)
     do = bf16_normal_bits((wid, _T_DO), tq * H * D).reshape(tq, H, D) if with_do else None
@@ -181,7 +211,8 @@ def make_inputs(lq, lkv, H: int, D: int, *, wid: int, mask: str = "none", act: s
         shape = (H,) if bias_kind == "scalar" else (H, NUM_BUCKETS)
         rng = np.random.default_rng([wid, _T_BIAS])
         bias = (rng.standard_normal(int(np.prod(shape)), dtype=np.float32) * np.float32(bias_sigma)).reshape(shape)
-    return Inputs(q, k, v, do, bias, q_off, kv_off, H, D, mask, act, bias_kind, int(window), int(block))
+    return Inputs(q, k, v, do, bias, q_off, kv_off, H, D, mask, act, bias_kind, int(window), int(block),
+                  bool(shared_q))
 
 
 def workload_inputs(name: str, with_do: Optional[bool] = None) -> Inputs:
@@ -191,4 +222,5 @@ def workload_inputs(name: str, with_do: Optional[bool] = None) -> Inputs:
     if with_do is None:
         with_do = w.backward
     return make_inputs(lq, lkv, w.H, w.D, wid=w.wid, mask=w.mask, act=w.act, bias_kind=w.bias,
-                       bias_sigma=w.bias_sigma, with_do=with_do, window=w.window, block=w.block)
+                       bias_sigma=w.bias_sigma, with_do=with_do, window=w.window, block=w.block,
+                       shared_q=w.shared_q > 0)

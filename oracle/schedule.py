@@ -35,6 +35,10 @@ splitting (both lists), given the number of concurrent workgroups ``slots``:
   split groups are numbered in the lexicographic order above and own partial slots
   slot0 .. slot0 + R - 1 (piece r -> slot0 + r); unsplit items carry slot -1
 order: by (piece length descending, b, h, tile, range start) ascending.
+shared queries (one set of query rows for every sequence, dQ summed over sequences), dQ list only:
+  after the rules above every piece owns a partial slot; slots are numbered by (h, tile, b, range
+  start) ascending, and one group per (h, tile) - written (0, h, tile, slot0, R) - sums its R pieces
+  in slot order.
 
 Each item is the tuple (b, h, tile, lo, hi, slot); each split group is (b, h, tile, slot0, R).
 """
@@ -172,3 +176,18 @@ def dispatch_order(items, n_xcd: int = 8):
         out.append(items[queues[x][taken[x]]])
         taken[x] += 1
     return out
+
+
+def share_query_slots(items):
+    """(items, groups, n_partial_slots) of a dQ list under shared queries (see the module rules)."""
+    order = sorted(range(len(items)), key=lambda i: (items[i][1], items[i][2], items[i][0], items[i][3]))
+    slot = {}
+    groups = []
+    for n, i in enumerate(order):
+        b, h, t = items[i][:3]
+        if not groups or tuple(groups[-1][1:3]) != (h, t):
+            groups.append([0, h, t, n, 0])
+        groups[-1][4] += 1
+        slot[i] = n
+    new_items = [(b, h, t, lo, hi, slot[i]) for i, (b, h, t, lo, hi, _s) in enumerate(items)]
+    return new_items, [tuple(g) for g in groups], len(items)

@@ -209,3 +209,98 @@ def test_raw_abi_null_and_enum_errors():
     assert lib.jfa_forward(None, *([None] * 8), None, 0, None) == 1
     lib.jfa_plan_destroy(h)
     lib.jfa_plan_destroy(None)
+
+
+def test_negative_scale_rejected():
+    # A negative multiplier would turn the -inf of a masked score into the row maximum.
+    assert _status_of(lambda: _host_plan([3, 4], [3, 4], 2, scale=-0.5)) == "JFA_ERR_UNSUPPORTED"
+    assert _status_of(lambda: _host_plan([3, 4], [3, 4], 2, scale=float("inf"))) == "JFA_ERR_UNSUPPORTED"
+    _host_plan([3, 4], [3, 4], 2, scale=0.25)
+
+
+def test_slice_limit_for_32bit_addressing():
+    # (L + 128) * H * D <= 2^30: with H = 64, D = 128 the longest sequence may hold 130,944 rows.
+    H, D = 64, 128
+    L = (1 << 30) // (H * D) - 128
+    _host_plan([L], [L], H, D, no_split=True)
+    assert _status_of(lambda: _host_plan([L + 1], [L + 1], H, D)) == "JFA_ERR_BAD_SHAPE"
+    assert _status_of(lambda: _host_plan([5, 3], [5, L + 1], H, D)) == "JFA_ERR_BAD_SHAPE"
+    assert b"2^30" in B.LIB.jfa_last_error()
+
+
+def _cpu_tensors(plan, out_dtype="bf16", grad_dtype="bf16"):
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    t = dict(q=torch.zeros(plan.Tq, plan.H, plan.D, dtype=bf), k=torch.zeros(plan.Tkv, plan.H, plan.D, dtype=bf),
+             v=torch.zeros(plan.Tkv, plan.H, plan.D, dtype=bf), dout=torch.zeros(plan.Tq, plan.H, plan.D, dtype=bf),
+             out=torch.zeros(plan.Tq, plan.H, plan.D, dtype=f32 if out_dtype == "f32" else bf),
+             lse=torch.zeros(plan.H, plan.Tq, dtype=f32),
+             bias=torch.zeros(plan.H, 64, dtype=f32) if plan.bias_kind == "bucket" else None)
+    return t
+
+
+def test_binding_checks_every_tensor_before_the_call():
+    """Shape, dtype, layout and device of each tensor are checked in the binding (the library only sees
+    pointers); CPU tensors reach the device check last, so each mismatch below is caught first."""
+    import torch
+    plan = _host_plan([5, 9], [5, 9], 2, mask="causal", bias="bucket")
+    t = _cpu_tensors(plan)
+    fwd = lambda **kw: plan.forward(kw.get("q", t["q"]), kw.get("k", t["k"]), kw.get("v", t["v"]), None, None,
+                                    kw.get("bias", t["bias"]), out=kw.get("out"), lse=kw.get("lse"))
+    bwd = lambda **kw: plan.backward(t["q"], t["k"], t["v"], None, None, t["bias"], kw.get("out", t["out"]),
+                                     kw.get("lse", t["lse"]), kw.get("dout", t["dout"]), dq=kw.get("dq"),
+                                     dk=kw.get("dk"), dv=kw.get("dv"), dbias=kw.get("dbias"))
+    cases = [
+        (fwd, dict(q=t["q"][:-1]), "shape"),
+        (fwd, dict(k=t["k"].float()), "dtype"),
+        (fwd, dict(v=t["v"].transpose(0, 1).contiguous().transpose(0, 1)), "contiguous"),
+        (fwd, dict(bias=t["bias"][:, :32]), "shape"),
+        (fwd, dict(bias=None), "required"),
+        (fwd, dict(out=torch.zeros(14, 2, 128, dtype=torch.float32)), "dtype"),
+        (fwd, dict(lse=torch.zeros(14, 2)), "shape"),
+        (bwd, dict(dout=t["dout"].float()), "dtype"),
+        (bwd, dict(dq=torch.zeros(14, 2, 128, dtype=torch.float32)), "dtype"),
+        (bwd, dict(dk=torch.zeros(13, 2, 128, dtype=torch.bfloat16)), "shape"),
+        (bwd, dict(out=None), "required"),
+        (bwd, dict(dbias=torch.zeros(2, 63)), "shape"),
+        (fwd, dict(), "GPU tensor"),
+        (bwd, dict(), "GPU tensor"),
+    ]
+    for fn, kw, what in cases:
+        with pytest.raises(ValueError, match=what):
+            fn(**kw)
+    nob = _host_plan([5], [7], 2)
+    t2 = _cpu_tensors(nob)
+    with pytest.raises(ValueError, match="without bias"):
+        nob.forward(t2["q"], t2["k"], t2["v"], None, None, torch.zeros(2, 64))
+
+
+def test_fused_self_target_lists_match_spec():
+    """Causal with more queries than keys (target rows past the history): the lists follow the same
+    rules; fewer queries than keys is refused."""
+    lh, lc = [130, 5, 700, 64], [40, 0, 129, 200]
+    lq = [a + b for a, b in zip(lh, lc)]
+    for slots, split in [(512, True), (16, True), (16, False)]:
+        plan = _host_plan(lq, lh, 2, mask="causal", num_slots=slots, no_split=not split)
+        _compare(plan, lq, lh, 2, True, slots, split)
+    assert _status_of(lambda: _host_plan([3, 4], [3, 5], 2, mask="causal")) == "JFA_ERR_BAD_SHAPE"
+
+
+def test_shared_query_dq_groups_match_spec():
+    """Shared queries: every dQ piece gets a partial slot and one group per (head, query tile) sums the
+    pieces of all sequences; the forward and dK/dV lists are unchanged."""
+    Ls, lkv = 150, [300, 1, 77, 1000, 0]
+    lq = [Ls] * len(lkv)
+    for slots, split in [(512, True), (8, True)]:
+        plan = B.Plan(ji.offsets(lq), ji.offsets(lkv), 2, 128, host_only=True, num_slots=slots, no_split=not split,
+                      shared_q=True)
+        info = plan.info()
+        qi, _, _ = S.query_tile_items(lq, lkv, 2, False, info["dq_bm"], info["dq_bn"], slots, split)
+        items, groups, n = S.share_query_slots(qi)
+        np.testing.assert_array_equal(plan.schedule(2), np.array(items, dtype=np.int32).reshape(-1, 6))
+        np.testing.assert_array_equal(plan.schedule(3), np.array(groups, dtype=np.int32).reshape(-1, 5))
+        assert sorted(g[2] for g in groups) == [0, 0, 1, 1] and sum(g[4] for g in groups) == len(items)
+        fi, fg, _ = S.query_tile_items(lq, lkv, 2, False, info["fwd_bm"], info["fwd_bn"], slots, split)
+        np.testing.assert_array_equal(plan.schedule(0), np.array(fi, dtype=np.int32).reshape(-1, 6))
+    assert _status_of(lambda: B.Plan(ji.offsets([3, 4]), ji.offsets([3, 4]), 2, 64, host_only=True,
+                                     shared_q=True)) == "JFA_ERR_BAD_SHAPE"

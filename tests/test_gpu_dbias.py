@@ -7,11 +7,12 @@ gradient is 0: softmax is invariant to a shift of the whole row).
 """
 import numpy as np
 import pytest
+import torch
 
 import jfa_inputs as ji
 from jagged_sequence_amd import binding as J
 from oracle.bucket import bucket
-from tests.gpu_util import GRAD_REL_L2, oracle, rel_l2, run_gpu, say, to_np
+from tests.gpu_util import GRAD_REL_L2, oracle, rel_l2, run_gpu, say, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -81,11 +82,21 @@ def test_dbias_deterministic_and_split_invariant():
 
 
 def test_dbias_requires_a_bias():
+    """The binding refuses a bias gradient without a bias, and so does the library itself (called
+    directly), before any launch."""
+    import ctypes
     x = ji.make_inputs([40], [40], 1, 64, wid=44, mask="causal", act="softmax", bias_kind="none")
     say("case dbias without bias")
-    with pytest.raises(J.JfaError) as e:
+    with pytest.raises(ValueError, match="without bias"):
         run_gpu(x, dbias=True)
-    assert e.value.status == 4  # JFA_ERR_UNSUPPORTED
+    g = run_gpu(x)
+    plan = g["plan"]
+    t = torch.zeros(64, dtype=torch.float32, device="cuda")
+    p = lambda a: ctypes.c_void_p(a.data_ptr())
+    q = to_dev(x.q)
+    st = J.LIB.jfa_backward(plan._h, p(q), p(q), p(q), None, None, None, p(g["out"]), p(g["lse"]), p(q), p(g["dq"]),
+                            p(g["dk"]), p(g["dv"]), p(t), None, 0, None)
+    assert st == 4  # JFA_ERR_UNSUPPORTED
 
 
 def test_dbias_full_causal_bucket_workload():

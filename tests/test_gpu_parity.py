@@ -204,19 +204,26 @@ def _sub_inputs(x, seqs):
     return sub, torch.from_numpy(qr).cuda(), torch.from_numpy(kr).cuda()
 
 
-def test_full_size_longtail_max_length():
-    """The long-tail workload at full size (B = 512, two sequences of 32,768 tokens) in the benchmark's
-    launch configuration. Whole short sequences go to the oracle; for the 32,768-token sequences the
-    oracle evaluates sampled query rows one by one (output, lse, dQ), and dK / dV are checked through
-    identities that hold at any size: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i per head."""
+def _check_longtail_full_size(name):
+    """The long-tail workload at full size in the benchmark's launch configuration (bf16 outputs and
+    gradients). Whole short sequences go to the oracle. For each 32,768-token sequence the oracle
+    evaluates sampled query rows one by one (output, lse, dQ) and the stored oracle values of sampled
+    keys give dK / dV element by element (``tests/golden/longtail_keycols.npz``, written by
+    ``make_longtail_keycols.py`` from ``oracle.key_cols`` alone); sum_j dK_j = 0 and
+    sum_j dV_j = sum_i dO_i per head are checked over every key as well."""
+    import os
     from oracle import attention as A
     from tests.gpu_util import LSE_MAX_ABS, OUT_MAX_ABS, rel_l2
-    name = "longtail"
     w = ji.WORKLOADS[name]
     x = ji.workload_inputs(name)
     lq, _ = ji.lengths(w)
     short = [int(b) for b in np.argsort(lq, kind="stable")[:1]] + [int(b) for b in np.flatnonzero(lq <= 2048)[[5, 77]]]
+    if name == "longtail_1m":
+        short += [int(b) for b in np.flatnonzero(lq <= 2048)[[-1]]]  # one of the sequences past the first 512
     longest = [int(b) for b in np.flatnonzero(lq == lq.max())]
+    golden = np.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "longtail_keycols.npz"))
+    gseqs = [int(b) for b in golden["seqs"]]
+    assert set(gseqs) <= set(longest) and len(gseqs) == 2
     say(f"case workload {name} full size; short seqs {short}, longest {longest}")
     gpu = run_gpu(x, out_dtype="bf16", grad_dtype="bf16")
     sub, qr, kr = _sub_inputs(x, short)
@@ -249,8 +256,19 @@ def test_full_size_longtail_max_length():
             assert np.abs(lg - l).max() <= LSE_MAX_ABS, (b, h, np.abs(lg - l).max())
             err = rel_l2(gg[uniform], g[uniform])
             assert err <= 2e-2, (b, h, err)
-            say(f"  seq {b} head {h}: out max-abs {np.abs(og - o).max():.2e}, lse {np.abs(lg - l).max():.2e}, "
-                f"dQ rel-L2 (sampled rows) {err:.2e}")
+            msg = (f"  seq {b} head {h}: out max-abs {np.abs(og - o).max():.2e}, lse {np.abs(lg - l).max():.2e}, "
+                   f"dQ rel-L2 (sampled rows) {err:.2e}")
+            if b in gseqs:
+                keys = golden[f"keys_{b}"]
+                dkg = gpu["dk"][ks + torch.from_numpy(keys).cuda(), h].double().cpu().numpy()
+                dvg = gpu["dv"][ks + torch.from_numpy(keys).cuda(), h].double().cpu().numpy()
+                ek = rel_l2(dkg, golden[f"dk_{b}_{h}"].astype(np.float64))
+                ev = rel_l2(dvg, golden[f"dv_{b}_{h}"].astype(np.float64))
+                first = keys < 128
+                ek0 = rel_l2(dkg[first], golden[f"dk_{b}_{h}"][first].astype(np.float64))
+                assert ek <= 2e-2 and ev <= 2e-2 and ek0 <= 2e-2, (b, h, ek, ev, ek0)
+                msg += f", dK / dV rel-L2 (sampled keys) {ek:.2e} / {ev:.2e}, first key tile dK {ek0:.2e}"
+            say(msg)
         dk = gpu["dk"][ks:ks + L].double()
         dv = gpu["dv"][ks:ks + L].double()
         dO = torch.from_numpy(do).to(dk.device)
@@ -259,4 +277,15 @@ def test_full_size_longtail_max_length():
             assert s_dk <= 1e-3 * dk[:, hh].norm(dim=1).sum().item(), (b, hh, s_dk)
             err = (dv[:, hh].sum(0) - dO[:, hh].sum(0)).norm().item()
             assert err <= 1e-2 * dO[:, hh].sum(0).norm().item(), (b, hh, err)
-    say("  longest sequences: sampled rows and gradient identities within bounds")
+    say("  longest sequences: sampled rows, sampled keys and gradient identities within bounds")
+
+
+def test_full_size_longtail_max_length():
+    """Long-tail workload, B = 512 (333,877 tokens)."""
+    _check_longtail_full_size("longtail")
+
+
+def test_full_size_longtail_1m():
+    """Long-tail workload at about a million tokens (B = 1652, 1,000,301 tokens, four 32,768-token
+    sequences)."""
+    _check_longtail_full_size("longtail_1m")
