@@ -171,6 +171,21 @@ jfa_status jfa_backward(jfa_plan_t plan, const void* q, const void* k, const voi
                         void* dv, float* dbias, void* workspace, size_t workspace_bytes,
                         jfa_stream_t stream);
 
+/* Allocation-free backward pass, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. Same arguments and results
+ * as jfa_backward without the workspace: the library uses a static device array of
+ * JFA_NOALLOC_SCRATCH_BYTES per GPU (held until the process ends) instead, and calls no allocating
+ * routine. A plan whose backward workspace (jfa_workspace_bytes) exceeds that size is refused with
+ * JFA_ERR_WORKSPACE before any launch. All calls on one GPU share its array: calls that overlap in
+ * time (several streams or threads) race and must be ordered by the caller. No per-kernel timing
+ * is recorded, and the plan must stay alive until the work this call enqueued has finished (the
+ * call records no event for the plan's buffer cache). */
+#define JFA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+jfa_status jfa_backward_noalloc(jfa_plan_t plan, const void* q, const void* k, const void* v,
+                                const int32_t* q_offsets, const int32_t* kv_offsets, const float* bias,
+                                const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                                void* dv, float* dbias, jfa_stream_t stream);
+
 /* Work lists, for inspection and tests. `which`: 0 forward items, 1 forward split groups,
  * 2 dQ items, 3 dQ split groups, 4 dK/dV items, 5 dK/dV split groups (longest first), and
  * 6 forward, 7 dQ, 8 dK/dV items in dispatch order: the order in which the kernels' workgroups

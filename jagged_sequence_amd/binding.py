@@ -31,8 +31,10 @@ PLAN_HOST_ONLY = 0x1
 PLAN_NO_SPLIT = 0x2
 PLAN_SHARED_Q = 0x4
 KERNELS = {"forward": 0, "combine": 1, "dkdv": 3, "dq": 4, "reduce": 5, "dbias": 6}
-SYMBOLS = ["jfa_plan", "jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_plan_schedule", "jfa_plan_info",
-           "jfa_timing_enable", "jfa_timing_read", "jfa_plan_destroy", "jfa_status_string", "jfa_last_error"]
+SYMBOLS = ["jfa_plan", "jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_backward_noalloc",
+           "jfa_plan_schedule", "jfa_plan_info", "jfa_timing_enable", "jfa_timing_read", "jfa_plan_destroy",
+           "jfa_status_string", "jfa_last_error"]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # JFA_NOALLOC_SCRATCH_BYTES
 
 
 class JfaError(RuntimeError):
@@ -58,6 +60,7 @@ def _load():
     lib.jfa_workspace_bytes.argtypes = [vp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.jfa_forward.argtypes = [vp] * 9 + [vp, sz, vp]
     lib.jfa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.jfa_backward_noalloc.argtypes = [vp] * 15
     lib.jfa_plan_schedule.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int32), sz, ctypes.POINTER(sz)]
     lib.jfa_plan_info.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), sz]
     lib.jfa_timing_enable.argtypes = [vp, i32]
@@ -68,8 +71,8 @@ def _load():
     lib.jfa_status_string.restype = ctypes.c_char_p
     lib.jfa_last_error.argtypes = []
     lib.jfa_last_error.restype = ctypes.c_char_p
-    for name in ["jfa_plan", "jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_plan_schedule",
-                 "jfa_plan_info", "jfa_timing_enable", "jfa_timing_read"]:
+    for name in ["jfa_plan", "jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_backward_noalloc",
+                 "jfa_plan_schedule", "jfa_plan_info", "jfa_timing_enable", "jfa_timing_read"]:
         getattr(lib, name).restype = st
     return lib
 
@@ -307,6 +310,27 @@ class Plan:
         return (dq, dk, dv, dbias) if want_db else (dq, dk, dv)
 
 
+def _backward_noalloc(plan: "Plan", q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq=None, dk=None, dv=None,
+                      stream=None, dbias=None):
+    specs = plan._common_specs(q, k, v, q_offsets, kv_offsets, bias)
+    specs.append(("dout", dout, (plan.Tq, plan.H, plan.D), torch.bfloat16))
+    if plan.act == "softmax":
+        specs += [("out", out, (plan.Tq, plan.H, plan.D), plan._dtype(plan.out_dtype)),
+                  ("lse", lse, (plan.H, plan.Tq), torch.float32)]
+    gdt = plan._dtype(plan.grad_dtype)
+    for name, t, T in (("dq", dq, plan.Tq_src), ("dk", dk, plan.Tkv), ("dv", dv, plan.Tkv)):
+        specs.append((name, t, (T, plan.H, plan.D), gdt))
+    if dbias is not None:
+        if plan.bias_kind == "none":
+            raise ValueError("dbias requested from a plan without bias")
+        specs.append(("dbias", dbias, (plan.H, 64) if plan.bias_kind == "bucket" else (plan.H,), torch.float32))
+    _check_tensors(specs)
+    _check(LIB.jfa_backward_noalloc(plan._h, _ptr(q), _ptr(k), _ptr(v), _ptr(q_offsets), _ptr(kv_offsets), _ptr(bias),
+                                    _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias),
+                                    _stream_handle(stream)))
+    return (dq, dk, dv, dbias) if dbias is not None else (dq, dk, dv)
+
+
 # ---------------------------------------------------------------------- C-named entry points
 def jfa_plan(q_offsets, kv_offsets, num_heads: int, head_dim: int, **kw) -> Plan:
     """``jfa_plan``: validate the problem and build the device work lists (see :class:`Plan`)."""
@@ -324,3 +348,9 @@ def jfa_backward(plan: Plan, q, k, v, q_offsets, kv_offsets, bias, out, lse, dou
     """``jfa_backward``: returns (dq, dk, dv), plus dbias when it is requested."""
     return plan.backward(q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq, dk, dv, workspace, stream, dbias)
 
+
+def jfa_backward_noalloc(plan: Plan, q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq, dk, dv, stream=None,
+                         dbias=None):
+    """``jfa_backward_noalloc``: the backward pass into caller-given dq / dk / dv (and dbias) with the
+    library's static scratch array as workspace; allocates nothing. Returns (dq, dk, dv[, dbias])."""
+    return _backward_noalloc(plan, q, k, v, q_offsets, kv_offsets, bias, out, lse, dout, dq, dk, dv, stream, dbias)

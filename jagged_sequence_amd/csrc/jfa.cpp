@@ -594,7 +594,15 @@ jfa_status run_forward(jfa_plan_s* P, const void* q, const void* k, const void* 
 
 jfa_status run_backward(jfa_plan_s* P, const void* q, const void* k, const void* v, const float* bias,
                         const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                        float* dbias, void* workspace, hipStream_t s) {
+                        float* dbias, void* workspace, hipStream_t s, bool allow_timing = true) {
+  // Timing records events it may have to create; callers that cannot allocate switch it off.
+  const bool timing = P->timing;
+  P->timing = timing && allow_timing;
+  struct Restore {
+    jfa_plan_s* p;
+    bool t;
+    ~Restore() { p->timing = t; }
+  } restore{P, timing};
   char* ws = static_cast<char*>(workspace);
   BwdArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -674,6 +682,27 @@ jfa_status note_use(jfa_plan_s* P, hipStream_t s) {
 }
 
 }  // namespace
+
+namespace jfa {
+
+// jfa_backward with a workspace the library provides itself (the allocation-free entry point):
+// the same checks and launches, no timing events, no use-tracking event.
+jfa_status backward_into(jfa_plan_s* P, const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                         const int32_t* kv_offsets, const float* bias, const void* out, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* dbias, void* (*workspace)(size_t, jfa_status*),
+                         hipStream_t s) {
+  jfa_status st = check_backward(P, q, k, v, bias, out, lse, dout, dq, dk, dv, dbias);
+  if (st != JFA_OK) return st;
+  void* ws = workspace(P->ws_bwd, &st);
+  if (st != JFA_OK) return st;
+  st = debug_check_offsets(P, q_offsets, kv_offsets, s);
+  if (st != JFA_OK) return st;
+  return run_backward(P, q, k, v, bias, out, lse, dout, dq, dk, dv, dbias, ws, s, false);
+}
+
+jfa_status set_error(jfa_status s, const char* msg) { return fail(s, msg); }
+
+}  // namespace jfa
 
 extern "C" {
 

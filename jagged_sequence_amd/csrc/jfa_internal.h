@@ -129,6 +129,21 @@ hipError_t launch_bwd_reduce_dkdv(const BwdArgs& a, const Modes& m, int n_groups
 hipError_t launch_bwd_dbias_clear(const BwdArgs& a, const Modes& m, hipStream_t s);
 hipError_t launch_bwd_dbias_finish(const BwdArgs& a, const Modes& m, hipStream_t s);
 
+}  // namespace jfa
+
+#include "jfa.h"
+
+namespace jfa {
+
+// jfa_backward with a workspace obtained from `workspace(bytes, &status)` after the argument checks
+// (which may refuse the size with a status); no timing and no use-tracking events are recorded.
+jfa_status backward_into(jfa_plan_s* P, const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                         const int32_t* kv_offsets, const float* bias, const void* out, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* dbias,
+                         void* (*workspace)(size_t, jfa_status*), hipStream_t s);
+// Sets the thread's last-error text and returns s.
+jfa_status set_error(jfa_status s, const char* msg);
+
 // Resident workgroups per CU of each kernel for the given modes (occupancy query).
 int occupancy_forward(const Modes& m);
 int occupancy_dq(const Modes& m);
