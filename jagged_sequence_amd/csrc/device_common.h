@@ -75,7 +75,8 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Relative-distance bucket: exact below 16, then four equal-width buckets per octave, capped at 63.
-__device__ __forceinline__ int rel_bucket(int d) {
+// (Also built for the host, where a test compares it with the reference bucket over every distance.)
+__host__ __device__ __forceinline__ int rel_bucket(int d) {
   d = d < 0 ? -d : d;
   const int e = 31 - __builtin_clz(d | 16);  // floor(log2 d) for d >= 16; the select below covers d < 16
   const int b = 16 + 4 * (e - 4) + ((d >> (e - 2)) & 3);
@@ -84,7 +85,7 @@ __device__ __forceinline__ int rel_bucket(int d) {
 
 // First distance of bucket u >= 16: 2^e + m 2^(e - 2) with e = 4 + (u - 16) / 4, m = (u - 16) % 4
 // (the inverse of rel_bucket on its logarithmic part; bucket 63 also takes every larger distance).
-__device__ __forceinline__ int rel_bucket_start(int u) {
+__host__ __device__ __forceinline__ int rel_bucket_start(int u) {
   const int e = 4 + ((u - 16) >> 2), m = (u - 16) & 3;
   return (1 << e) + (m << (e - 2));
 }

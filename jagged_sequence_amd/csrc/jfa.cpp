@@ -505,12 +505,14 @@ jfa_status timed(jfa_plan_s* P, int kernel, hipStream_t s, F fn, const char* wha
     a = take_event(P);
     b = take_event(P);
     if (!a || !b) return fail(JFA_ERR_HIP, "hipEventCreate failed");
-    hipEventRecord(a, s);
+    const hipError_t e = hipEventRecord(a, s);
+    if (e != hipSuccess) return hip_fail(e, "timing event record");
   }
   hipError_t e = fn();
   if (e != hipSuccess) return hip_fail(e, what);
   if (P->timing) {
-    hipEventRecord(b, s);
+    e = hipEventRecord(b, s);
+    if (e != hipSuccess) return hip_fail(e, "timing event record");
     P->recs.push_back({kernel, a, b});
   }
   return JFA_OK;
