@@ -413,13 +413,29 @@ void bwd_dq_kernel2(BwdArgs a) {
         for (int r = 0; r < 16; ++r) sacc[sb][r] = acc0;
       }
       pacc[sb] = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const uint32_t off = (raddr ^ (uint32_t)(kb << 5)) + sb * 32 * kRowBytes;
-        sacc[sb] = mfma32(lds_read16(Kt, off), qf[kb], sacc[sb]);
-        pacc[sb] = mfma32(lds_read16(Vt, off), df[kb], pacc[sb]);
-      }
     }
+    // K and V operands are requested two steps ahead of their products (a step is one S and one dP
+    // product), so each product finds its operand loaded instead of waiting for a read issued just
+    // before it.
+    bf16x8 kop[2 * NKB], vop[2 * NKB];
+#pragma unroll
+    for (int s = 0; s < 2 * NKB; ++s) {
+      const uint32_t off = (raddr ^ (uint32_t)((s % NKB) << 5)) + (s / NKB) * 32 * kRowBytes;
+      kop[s] = lds_read16(Kt, off);
+      vop[s] = lds_read16(Vt, off);
+    }
+#pragma unroll
+    for (int s = 0; s < 2 * NKB; ++s) {
+      sacc[s / NKB] = mfma32(kop[s], qf[s % NKB], sacc[s / NKB]);
+      pacc[s / NKB] = mfma32(vop[s], df[s % NKB], pacc[s / NKB]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + (BIAS == kBiasBucket ? 16 : 0), 0);
+#pragma unroll
+    for (int s = 0; s < 2 * NKB - 2; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
     const bool need_mask = BAND ? (wlo_all > key0 || whi_all < key0 + BN - 1)
                                 : (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);
