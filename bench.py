@@ -157,6 +157,7 @@ def cpu_baseline(x, workload, seconds_target=15.0):
         blas_threads = None
     model, nproc = host_cpu()
     cores = blas_threads or nproc
+    import jfa_inputs as ji
     from jagged_sequence_amd.flops import useful_flops
     f = A.bf16_bits_to_f64
     lq = np.diff(x.q_off.astype(np.int64))
@@ -183,7 +184,11 @@ def cpu_baseline(x, workload, seconds_target=15.0):
     bias = None if x.bias is None else x.bias.astype(np.float64)
     kw = dict(mask=x.mask, act=x.act, bias_kind=x.bias_kind, bias=bias, window=x.window, block=x.block)
     t0 = time.perf_counter()
-    if x.shared_q:  # the seed rows are shared by every sequence
+    if ji.WORKLOADS[workload].mxfp8:  # the MXFP8 forward oracle
+        from oracle import mx
+        mx.forward(f(x.q[rows]), k, v, sq, sk, mask=x.mask, bias_kind=x.bias_kind, bias=bias, window=x.window,
+                   block=x.block)
+    elif x.shared_q:  # the seed rows are shared by every sequence
         A.forward_shared_q(f(x.q), k, v, sk, **kw)
         if workload_backward(workload):
             A.backward_shared_q(f(x.q), k, v, sk, f(x.do[rows]), **kw)
@@ -221,7 +226,7 @@ def main() -> int:
                     help="only run 3 device-to-device copies of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs on one GPU only "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the benchmark runs on one GPU only "
               f"(the attention shards by heads or sequences with no exchange; see the design notes)",
               file=sys.stderr)
         return 2
@@ -256,7 +261,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     plan_kw = dict(mask=w.mask, act=w.act, bias=w.bias, window=w.window, block=w.block, out_dtype=args.out_dtype,
-                   grad_dtype=args.out_dtype, shared_q=x.shared_q)
+                   grad_dtype=args.out_dtype, shared_q=x.shared_q, mxfp8=w.mxfp8)
     t0 = time.perf_counter()
     plan = J.Plan(x.q_off, x.kv_off, w.H, w.D, **plan_kw)
     plan_ms = (time.perf_counter() - t0) * 1e3
@@ -358,7 +363,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8 (e4m3 + e8m0 block scales)" if w.mxfp8 else "bf16",
         "data": "synthetic (seeded jagged lengths and N(0,1) bf16 values; no dataset)",
         "config": {"workload": args.workload, "B": w.B, "H": w.H, "D": w.D, "mask": w.mask, "act": w.act,
                    "bias": w.bias, "window": w.window, "block": w.block, "tokens_q": int(x.q_off[-1]), "tokens_kv": int(x.kv_off[-1]),

@@ -91,6 +91,18 @@ typedef enum { JFA_BF16 = 0, JFA_F32 = 1 } jfa_dtype;
  * ([B * Ls, H, D], [H, B * Ls]). dq is the sum over sequences of each sequence's query gradient,
  * taken in a fixed order (deterministic). */
 #define JFA_PLAN_SHARED_Q 0x4u
+/* MXFP8 forward pass (kerneldigest.dev page, "Arquitectura del Sistema": attention in MXFP8 with
+ * block quantisation and online conversion of P). jfa_forward quantises Q and K (blocks of 32
+ * features of a row), V (blocks of 32 consecutive keys of a feature, from the sequence's first key)
+ * into the forward workspace and computes both products on FP8 E4M3 values with E8M0 block scales
+ * (scale 2^(floor(log2 amax) - 8), elements rounded to nearest even, saturated at 448), fp32
+ * accumulation. P is quantised the same way per row in blocks of 32 consecutive keys, taken
+ * against an integer running maximum (in log2 units) so that rescaling commutes with the
+ * quantisation: out_i = sum_j P^_ij V^_j / sum_j P~_ij with P~ = 2^(s log2(e) - M_i); lse is the
+ * log-sum-exp of the scores from the quantised Q and K. Softmax, head dim 128, no shared queries;
+ * forward only (jfa_backward refuses the plan with JFA_ERR_UNSUPPORTED). The inputs and outputs
+ * keep their bf16 / fp32 layouts. */
+#define JFA_PLAN_MXFP8 0x8u
 
 typedef struct {
   int32_t num_seqs;               /* B >= 1 */

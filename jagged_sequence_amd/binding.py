@@ -30,7 +30,8 @@ DTYPES = {"bf16": 0, "f32": 1}
 PLAN_HOST_ONLY = 0x1
 PLAN_NO_SPLIT = 0x2
 PLAN_SHARED_Q = 0x4
-KERNELS = {"forward": 0, "combine": 1, "dkdv": 3, "dq": 4, "reduce": 5, "dbias": 6}
+PLAN_MXFP8 = 0x8
+KERNELS = {"forward": 0, "combine": 1, "dkdv": 3, "dq": 4, "reduce": 5, "dbias": 6, "mx_quantize": 7}
 SYMBOLS = ["jfa_plan", "jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_backward_noalloc",
            "jfa_plan_schedule", "jfa_plan_info", "jfa_timing_enable", "jfa_timing_read", "jfa_plan_destroy",
            "jfa_status_string", "jfa_last_error"]
@@ -136,7 +137,7 @@ class Plan:
     def __init__(self, q_offsets, kv_offsets, num_heads: int, head_dim: int, *, mask: str = "none",
                  act: str = "softmax", bias: str = "none", scale: float = 0.0, out_dtype: str = "bf16",
                  grad_dtype: str = "bf16", num_slots: int = 0, host_only: bool = False, no_split: bool = False,
-                 window: int = 0, block: int = 0, shared_q: bool = False, stream=None):
+                 window: int = 0, block: int = 0, shared_q: bool = False, mxfp8: bool = False, stream=None):
         self._q_off = _i32(q_offsets)
         self._kv_off = _i32(kv_offsets)
         self.B = len(self._q_off) - 1
@@ -160,8 +161,9 @@ class Plan:
         p.grad_dtype = DTYPES[grad_dtype]
         p.num_slots = int(num_slots)
         p.flags = (PLAN_HOST_ONLY if host_only else 0) | (PLAN_NO_SPLIT if no_split else 0) | \
-            (PLAN_SHARED_Q if shared_q else 0)
+            (PLAN_SHARED_Q if shared_q else 0) | (PLAN_MXFP8 if mxfp8 else 0)
         self.shared_q = bool(shared_q)
+        self.mxfp8 = bool(mxfp8)
         # rows of q and dq: one shared set of Ls rows, or one set per sequence
         self.Tq_src = (int(self._q_off[1]) if self.B >= 1 else 0) if shared_q else self.Tq
         p.window = self.window

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libjfa.so")
-SOURCES = ["fwd.hip", "bwd.hip", "noalloc.hip", "jfa.cpp"]
+SOURCES = ["fwd.hip", "bwd.hip", "mx.hip", "noalloc.hip", "jfa.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU instructions.

@@ -409,6 +409,12 @@ struct jfa_plan_s {
   float scale = 0.0f;
   int out_f32 = 0, grad_f32 = 0;
   int q_shared = 0;  // JFA_PLAN_SHARED_Q
+  int mx = 0;        // JFA_PLAN_MXFP8
+  int n_vtiles = 0;  // MXFP8: 64-key tiles over all sequences (transposed quantised V)
+  std::vector<int32_t> vtiles;  // [n_vtiles][2]: first key row, keys in the tile
+  std::vector<int32_t> vtile0;  // per sequence: its first tile
+  size_t off_qq = 0, off_qs = 0, off_kq = 0, off_ks = 0, off_vq = 0, off_vs = 0;
+  int32_t* d_vtiles = nullptr;
   uint32_t flags = 0;
   std::vector<int32_t> q_off, kv_off;
   List lists[3];
@@ -451,8 +457,13 @@ jfa_status check_problem(const jfa_problem* p, std::vector<int>& lq, std::vector
   // A negative scale would flip the order of the scores that the masks rely on (-inf stays the
   // smallest score only for a non-negative multiplier).
   if (!std::isfinite(p->scale) || p->scale < 0.0f) return fail(JFA_ERR_UNSUPPORTED, "scale must be finite and >= 0");
-  if ((p->flags & ~(JFA_PLAN_HOST_ONLY | JFA_PLAN_NO_SPLIT | JFA_PLAN_SHARED_Q)) != 0)
+  if ((p->flags & ~(JFA_PLAN_HOST_ONLY | JFA_PLAN_NO_SPLIT | JFA_PLAN_SHARED_Q | JFA_PLAN_MXFP8)) != 0)
     return fail(JFA_ERR_UNSUPPORTED, "unknown flags");
+  if (p->flags & JFA_PLAN_MXFP8) {
+    if (p->head_dim != 128) return fail(JFA_ERR_BAD_SHAPE, "MXFP8 needs head_dim 128");
+    if (p->act != JFA_ACT_SOFTMAX) return fail(JFA_ERR_UNSUPPORTED, "MXFP8 supports the softmax activation only");
+    if (p->flags & JFA_PLAN_SHARED_Q) return fail(JFA_ERR_UNSUPPORTED, "MXFP8 does not take shared queries");
+  }
   if (p->window < 0 || p->block < 0) return fail(JFA_ERR_BAD_SHAPE, "window and block must be >= 0");
   const int B = p->num_seqs;
   if (p->q_offsets_host[0] != 0 || p->kv_offsets_host[0] != 0) return fail(JFA_ERR_BAD_OFFSETS, "offsets[0] must be 0");
@@ -556,6 +567,7 @@ jfa_status check_backward(jfa_plan_s* P, const void* q, const void* k, const voi
   if (P->flags & JFA_PLAN_HOST_ONLY) return fail(JFA_ERR_HOST_ONLY, "plan was built host-only");
   const bool softmax = P->modes.act == kSoftmax;
   if (dbias && P->modes.bias == kBiasNone) return fail(JFA_ERR_UNSUPPORTED, "dbias requested without a bias");
+  if (P->mx) return fail(JFA_ERR_UNSUPPORTED, "MXFP8 plans are forward only");
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return fail(JFA_ERR_NULL_ARG, "a tensor pointer is NULL");
   if (P->modes.bias != kBiasNone && !bias) return fail(JFA_ERR_NULL_ARG, "bias is NULL");
   if (softmax && (!out || !lse)) return fail(JFA_ERR_NULL_ARG, "out and lse are required for softmax");
@@ -587,7 +599,24 @@ jfa_status run_forward(jfa_plan_s* P, const void* q, const void* k, const void* 
   a.band = P->band;
   a.q_shared = P->q_shared;
   const List& L = P->lists[kFwd];
-  jfa_status st = timed(P, 0, s, [&] { return launch_forward(a, P->modes, (int)L.n_items(), s); }, "forward launch");
+  jfa_status st = JFA_OK;
+  if (P->mx) {
+    char* ws = static_cast<char*>(workspace);
+    MxArgs x{};
+    x.f = a;
+    x.qq = reinterpret_cast<uint8_t*>(ws + P->off_qq);
+    x.qs = reinterpret_cast<uint8_t*>(ws + P->off_qs);
+    x.kq = reinterpret_cast<uint8_t*>(ws + P->off_kq);
+    x.ks = reinterpret_cast<uint8_t*>(ws + P->off_ks);
+    x.vq = reinterpret_cast<uint8_t*>(ws + P->off_vq);
+    x.vs = reinterpret_cast<uint8_t*>(ws + P->off_vs);
+    x.vtiles = P->d_vtiles;
+    st = timed(P, 7, s, [&] { return launch_mx_quantize(x, P->Tq, P->Tkv, P->n_vtiles, s); }, "MXFP8 quantise launch");
+    if (st != JFA_OK) return st;
+    st = timed(P, 0, s, [&] { return launch_forward_mx(x, P->modes, (int)L.n_items(), s); }, "MXFP8 forward launch");
+  } else {
+    st = timed(P, 0, s, [&] { return launch_forward(a, P->modes, (int)L.n_items(), s); }, "forward launch");
+  }
   if (st != JFA_OK) return st;
   if (L.n_groups() > 0)
     st = timed(P, 1, s, [&] { return launch_forward_combine(a, P->modes, (int)L.n_groups(), s); }, "combine launch");
@@ -760,6 +789,22 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   query_tile_list(lq, lkv, P->H, lim, kFwdBM, kFwdBN, slots[kFwd], split, P->lists[kFwd]);
   query_tile_list(lq, lkv, P->H, lim, kDqBM, kDqBN, slots[kDq], split, P->lists[kDq]);
   key_tile_list(lq, lkv, P->H, lim, kKvBM, P->kv_bn, slots[kKv], split, P->lists[kKv]);
+  P->mx = (p.flags & JFA_PLAN_MXFP8) ? 1 : 0;
+  if (P->mx) {
+    P->vtile0.assign(P->B + 1, 0);
+    for (int b = 0; b < P->B; ++b) {
+      const int n = ceil_div(lkv[b], kFwdBN);
+      for (int t = 0; t < n; ++t)
+        P->vtiles.insert(P->vtiles.end(), {P->kv_off[b] + t * kFwdBN, std::min(kFwdBN, lkv[b] - t * kFwdBN)});
+      P->vtile0[b + 1] = P->vtile0[b] + n;
+    }
+    P->n_vtiles = P->vtile0[P->B];
+    // the kernels address quantised V tiles with 32-bit byte offsets
+    if ((int64_t)P->n_vtiles * P->H * kFwdBN * 128 >= ((int64_t)1 << 32)) {
+      delete P;
+      return fail(JFA_ERR_BAD_SHAPE, "MXFP8: quantised V beyond 4 GiB");
+    }
+  }
   P->q_shared = (p.flags & JFA_PLAN_SHARED_Q) ? 1 : 0;
   if (P->q_shared) share_query_slots(P->lists[kDq]);
   for (auto& L : P->lists) L.order = dispatch_order(L, P->B, P->H);
@@ -769,6 +814,16 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   P->ws_fwd = align256((size_t)P->lists[kFwd].nslots * kFwdBM * D * 4);
   P->off_part_lse = P->ws_fwd;
   P->ws_fwd += align256((size_t)P->lists[kFwd].nslots * kFwdBM * 4);
+  if (P->mx) {  // quantised copies of Q, K, V and their block scales
+    const size_t H = P->H;
+    P->off_qq = P->ws_fwd;
+    P->off_qs = P->off_qq + align256((size_t)P->Tq * H * D);
+    P->off_kq = P->off_qs + align256((size_t)P->Tq * H * (D / 32));
+    P->off_ks = P->off_kq + align256((size_t)P->Tkv * H * D);
+    P->off_vq = P->off_ks + align256((size_t)P->Tkv * H * (D / 32));
+    P->off_vs = P->off_vq + align256((size_t)P->n_vtiles * H * D * kFwdBN);
+    P->ws_fwd = P->off_vs + align256((size_t)P->n_vtiles * H * 2 * D);
+  }
   size_t o = 0;
   P->off_delta = o;
   if (P->modes.act == kSoftmax) o += align256((size_t)P->H * P->Tq * 4);
@@ -783,7 +838,7 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   P->off_queue = o;
   if (P->D == 128) o += align256(kQueueCounters * 4);
   P->ws_bwd = o;
-  if (P->lists[kFwd].nslots == 0) P->ws_fwd = 0;
+  if (P->lists[kFwd].nslots == 0 && !P->mx) P->ws_fwd = 0;
 
   if (!host_only) {
     // Device records (kItemInts / kGroupInts int32 each): the list fields followed by the sequence's
@@ -791,6 +846,7 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
     // straight into pinned staging memory and uploaded asynchronously; nothing waits for the copy.
     size_t total = 0;
     for (auto& L : P->lists) total += L.n_items() * kItemInts + L.n_groups() * kGroupInts;
+    total += P->vtiles.size();
     total = std::max<size_t>(total, kItemInts);
     CachedBuf stage;
     hipError_t e = cache_acquire(total * 4, true, P->device, stage);
@@ -820,6 +876,7 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
         put_seq(r + 6, it[0]);
         r[10] = L.first[(size_t)L.order[i]] ? 1 : 0;
         std::fill(r + 11, r + kItemInts, 0);
+        if (P->mx) r[11] = P->vtile0[it[0]];  // MXFP8: the sequence's first quantised V tile
       }
       offs[l][1] = pos;
       for (size_t g = 0; g < L.n_groups(); ++g, pos += kGroupInts) {
@@ -830,6 +887,9 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
         std::fill(r + 9, r + kGroupInts, 0);
       }
     }
+    const size_t off_vt = pos;
+    std::copy(P->vtiles.begin(), P->vtiles.end(), host + pos);
+    pos += P->vtiles.size();
     if (pos == 0) std::fill(host, host + kItemInts, 0);
     hipStream_t s = (hipStream_t)stream;
     hipEvent_t copied = cache_event(), used = cache_event();
@@ -853,6 +913,7 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
       P->lists[l].d_items = static_cast<int32_t*>(P->dev.ptr) + offs[l][0];
       P->lists[l].d_groups = static_cast<int32_t*>(P->dev.ptr) + offs[l][1];
     }
+    P->d_vtiles = static_cast<int32_t*>(P->dev.ptr) + off_vt;
   }
   *plan_out = P;
   return JFA_OK;

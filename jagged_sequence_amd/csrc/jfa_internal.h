@@ -101,6 +101,18 @@ struct BwdArgs {
   int q_shared;  // query rows shared by every sequence (read from row 0 of q); dq is summed over sequences
 };
 
+// MXFP8 forward: the forward arguments plus the quantised copies (in the forward workspace).
+struct MxArgs {
+  FwdArgs f;
+  uint8_t* qq;  // [Tq][H][D] E4M3
+  uint8_t* qs;  // [Tq][H][D / 32] E8M0
+  uint8_t* kq;  // [Tkv][H][D] E4M3
+  uint8_t* ks;  // [Tkv][H][D / 32] E8M0
+  uint8_t* vq;  // [tiles][H][D][64] E4M3, transposed 64-key tiles of every sequence
+  uint8_t* vs;  // [tiles][H][2][D] E8M0
+  const int32_t* vtiles;  // [tiles][2]: first key row (absolute) and keys in the tile
+};
+
 struct Modes {
   int D;
   int act;
@@ -143,6 +155,10 @@ jfa_status backward_into(jfa_plan_s* P, const void* q, const void* k, const void
                          void* (*workspace)(size_t, jfa_status*), hipStream_t s);
 // Sets the thread's last-error text and returns s.
 jfa_status set_error(jfa_status s, const char* msg);
+
+// MXFP8 forward (D = 128, softmax): quantisation of Q, K and V, then the attention kernel.
+hipError_t launch_mx_quantize(const MxArgs& a, int Tq, int Tkv, int n_vtiles, hipStream_t s);
+hipError_t launch_forward_mx(const MxArgs& a, const Modes& m, int n_items, hipStream_t s);
 
 // Resident workgroups per CU of each kernel for the given modes (occupancy query).
 int occupancy_forward(const Modes& m);

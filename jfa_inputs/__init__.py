@@ -54,6 +54,7 @@ class Workload:
     block: int = 0                # block-attention limit (0 = off)
     q_extra_law: Optional[tuple] = None  # target rows appended to each sequence's queries (fused self + target)
     shared_q: int = 0             # > 0: that many query rows shared by every sequence (PMA seeds)
+    mxfp8: bool = False           # the forward pass in MXFP8
 
 
 WORKLOADS = {
@@ -97,6 +98,10 @@ WORKLOADS = {
                  description="fused self + target: B=256 users, history~lognormal(512,1) in [64,4096] "
                              "(causal self-attention), then U[1,64] candidate rows that see the whole history; "
                              "H=8, D=128, scalar bias ~N(0,0.1)"),
+        # The long-tail workload's forward pass in MXFP8 (the pages train attention in MXFP8).
+        Workload("longtail_mxfp8", 5, 512, 8, 128, ("pareto", 1.2, 128, 32768), None, "causal", "softmax",
+                 "bucket", 0.5, backward=False, mxfp8=True,
+                 description="as longtail, forward only, in MXFP8 (E4M3 values, E8M0 scales per 32 elements)"),
         # Pooling by multihead attention: 32 learned seed queries shared by every sequence, attending
         # with a GDPA activation (the pages list PMA with self- and cross-attention under GDPA). The
         # pages give no sizes; the sequence law is the target-attention workload's history.

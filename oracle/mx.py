@@ -77,8 +77,11 @@ def _quantize_seq_keys(v_seq):
 
 
 def forward(q, k, v, q_off, kv_off, *, mask="none", bias_kind="none", bias=None, window=0, block=0,
-            scale: Optional[float] = None):
-    """MXFP8 softmax attention forward; returns ``(out [Tq, H, D], lse [H, Tq])``."""
+            scale: Optional[float] = None, magnitude: bool = False):
+    """MXFP8 softmax attention forward; returns ``(out [Tq, H, D], lse [H, Tq])``, and with
+    ``magnitude`` also ``sum_j P^_ij |V^_jd| / sum_j P~_ij`` (the scale of each output element: a
+    probability that rounds to the neighbouring E4M3 value, at most 2^-3 of itself away, moves
+    the element by at most 2^-3 times this)."""
     q_off, kv_off = A._check(q, k, v, q_off, kv_off, mask, "softmax", bias_kind, bias, window, block)
     Tq, H, D = q.shape
     if scale is None:
@@ -86,6 +89,7 @@ def forward(q, k, v, q_off, kv_off, *, mask="none", bias_kind="none", bias=None,
     qh = mx_quantize(q, axis=-1)
     kh = mx_quantize(k, axis=-1)
     out = np.zeros((Tq, H, D))
+    mag = np.zeros((Tq, H, D))
     lse = np.full((H, Tq), -np.inf)
     log2e = 1.0 / math.log(2.0)
     for b in range(len(q_off) - 1):
@@ -107,7 +111,10 @@ def forward(q, k, v, q_off, kv_off, *, mask="none", bias_kind="none", bias=None,
                 Pq = mx_quantize(np.concatenate([Pt, np.zeros((Pt.shape[0], pad))], axis=1), axis=1)[:, :lkv]
                 l = Pt.sum(axis=1)
                 out[qs + i0:qs + i1, h] = np.where(any_vis[:, None], (Pq @ V) / np.where(any_vis, l, 1.0)[:, None], 0.0)
+                if magnitude:
+                    mag[qs + i0:qs + i1, h] = np.where(any_vis[:, None],
+                                                       (Pq @ np.abs(V)) / np.where(any_vis, l, 1.0)[:, None], 0.0)
                 with np.errstate(divide="ignore"):
                     lse[h, qs + i0:qs + i1] = np.where(any_vis, (M + np.log2(np.where(any_vis, l, 1.0))) / log2e,
                                                        -np.inf)
-    return out, lse
+    return (out, lse, mag) if magnitude else (out, lse)

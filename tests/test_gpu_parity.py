@@ -199,7 +199,7 @@ def _sub_inputs(x, seqs):
     import dataclasses
     qr = np.concatenate([np.arange(x.q_off[b], x.q_off[b + 1]) for b in seqs])
     kr = np.concatenate([np.arange(x.kv_off[b], x.kv_off[b + 1]) for b in seqs])
-    sub = dataclasses.replace(x, q=x.q[qr], k=x.k[kr], v=x.v[kr], do=x.do[qr],
+    sub = dataclasses.replace(x, q=x.q[qr], k=x.k[kr], v=x.v[kr], do=None if x.do is None else x.do[qr],
                               q_off=ji.offsets(np.diff(x.q_off)[seqs]), kv_off=ji.offsets(np.diff(x.kv_off)[seqs]))
     return sub, torch.from_numpy(qr).cuda(), torch.from_numpy(kr).cuda()
 

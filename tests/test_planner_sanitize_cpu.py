@@ -26,6 +26,8 @@ hipError_t launch_bwd_reduce_dq(const BwdArgs&, const Modes&, int, hipStream_t) 
 hipError_t launch_bwd_reduce_dkdv(const BwdArgs&, const Modes&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_bwd_dbias_clear(const BwdArgs&, const Modes&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_bwd_dbias_finish(const BwdArgs&, const Modes&, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_mx_quantize(const MxArgs&, int, int, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_forward_mx(const MxArgs&, const Modes&, int, hipStream_t) { return hipErrorNotSupported; }
 int occupancy_forward(const Modes&) { return 1; }
 int occupancy_dq(const Modes&) { return 1; }
 int occupancy_dkdv(const Modes&) { return 1; }
@@ -103,7 +105,7 @@ def test_planner_under_address_and_undefined_behaviour_sanitizers(tmp_path):
         mask = 1 if w.mask == "causal" else 0
         act = ji.ACTS.index(w.act)
         bias = ji.BIASES.index(w.bias)
-        flags = 4 if w.shared_q else 0
+        flags = (4 if w.shared_q else 0) | (8 if w.mxfp8 else 0)
         for slots in (0, 37):
             cases.append(_case(lq, lkv, w.H, w.D, mask, act, bias, flags, slots, w.window, w.block))
     cases += [
