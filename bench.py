@@ -31,26 +31,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA (the scaled MX products run at this rate)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 METRIC = "useful (unpadded) attention TFLOPS fwd+bwd and % of bf16 MFMA peak, 1×MI355X"
 DEFAULT_WORKLOAD = "longtail"  # the long-tail production-like workload (B = 512, 333,877 tokens)
 # FLOPs each kernel must execute per visible pair and head (its own matrix products):
 #   forward: S = QK^T, O = PV; dK/dV: S, dP = dO V^T, dV = P^T dO, dK = dS^T Q; dQ: S, dP, dQ = dS K
 KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dkdv": 8, "dq": 6}
-RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # about 315
 
 
-def kernel_bytes(kernel: str, Tq: int, Tkv: int, H: int, D: int, out_bytes: int, softmax: bool) -> int:
+def kernel_bytes(kernel: str, Tq: int, Tkv: int, H: int, D: int, out_bytes: int, softmax: bool,
+                 mx: bool = False) -> int:
     """Algorithmic HBM bytes of one launch: every tensor the kernel must read or write, once.
 
-    bf16 inputs (2 bytes per element); outputs and gradients in the chosen dtype; lse and Delta fp32.
+    bf16 inputs (2 bytes per element; MXFP8 forward: 1 byte plus one scale byte per 32 elements);
+    outputs and gradients in the chosen dtype; lse and Delta fp32.
     forward: read Q, K, V; write O (and lse). dK/dV: read Q, dO, K, V (lse, Delta); write dK, dV.
     dQ: read Q, dO, K, V (lse, Delta); write dQ.
     """
     q, kv = Tq * H * D, Tkv * H * D
     stats = 2 * Tq * H * 4 if softmax else 0
     if kernel == "forward":
-        return 2 * (q + 2 * kv) + out_bytes * q + (Tq * H * 4 if softmax else 0)
+        ins = (q + 2 * kv) * 33 // 32 if mx else 2 * (q + 2 * kv)
+        return ins + out_bytes * q + (Tq * H * 4 if softmax else 0)
     if kernel == "dkdv":
         return 2 * (2 * q + 2 * kv) + stats + out_bytes * 2 * kv
     return 2 * (2 * q + 2 * kv) + stats + out_bytes * q
@@ -116,13 +119,16 @@ def _parse_clock(tool: str, text: str):
 
 
 def gpu_clock_under_load(step, seconds: float, median_ms: float):
-    """Shader (GFX) clock in MHz as the SMI tool samples it while about ``seconds`` of steps run.
+    """Shader (GFX) clock in MHz as the SMI tool samples it while steps run.
 
-    The tool is started first (it takes a second or two to sample) and the steps are queued behind
-    it, so the sample falls inside the busy period; these steps are outside the timed region. Not
+    The tool is started first and steps keep the GPU busy until it has printed (at most
+    ``seconds``), so its sample falls inside the busy period; these steps are outside the timed
+    region. Not
     run under a profiler (the tool is a script whose interpreter the profiler's preload would
     follow)."""
     import subprocess
+
+    import torch
     if any("ROCPROF" in k for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
         return None
     for tool, cmd in (("amd-smi", ["amd-smi", "metric", "--clock"]), ("rocm-smi", ["rocm-smi", "--showclocks"])):
@@ -130,8 +136,14 @@ def gpu_clock_under_load(step, seconds: float, median_ms: float):
             proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
         except OSError:
             continue
-        for _ in range(max(1, min(5000, int(seconds * 1e3 / max(median_ms, 1e-3))))):
-            step()
+        # steps run until the tool has printed (at most ``seconds``), synchronised every ~50 ms so
+        # that the queue never holds much more than the tool's remaining sampling time
+        per_sync = max(1, int(50.0 / max(median_ms, 1e-3)))
+        t_end = time.perf_counter() + seconds
+        while proc.poll() is None and time.perf_counter() < t_end:
+            for _ in range(per_sync):
+                step()
+            torch.cuda.synchronize()
         try:
             text = proc.communicate(timeout=60)[0]
         except subprocess.SubprocessError:
@@ -163,45 +175,59 @@ def cpu_baseline(x, workload, seconds_target=15.0):
     lq = np.diff(x.q_off.astype(np.int64))
     lkv = np.diff(x.kv_off.astype(np.int64))
     causal = x.mask == "causal"
-    # greedy sample: sequences in order until the estimated oracle work reaches the target
-    est_rate = 8e9  # fp64 useful FLOP/s of the oracle on a 16-core host, for sizing the sample only
-    budget = seconds_target * est_rate
-    seqs, acc = [], 0.0
-    for b in range(len(lq)):
-        # the oracle's cost follows the dense score rows it forms, whatever the window or block
-        n = int(min(lq[b], lkv[b]))
-        pairs = n * (n + 1) // 2 if causal else int(lq[b]) * int(lkv[b])
-        w = (4 + (10 if workload_backward(workload) else 0)) * x.D * pairs * x.H
-        if seqs and acc + w > budget:
-            break
-        seqs.append(b)
-        acc += w
-    rows = np.concatenate([np.arange(x.q_off[b], x.q_off[b + 1]) for b in seqs])
-    krows = np.concatenate([np.arange(x.kv_off[b], x.kv_off[b + 1]) for b in seqs])
-    sq = np.concatenate([[0], np.cumsum(lq[seqs])])
-    sk = np.concatenate([[0], np.cumsum(lkv[seqs])])
-    k, v = f(x.k[krows]), f(x.v[krows])
+    bw_on = workload_backward(workload)
     bias = None if x.bias is None else x.bias.astype(np.float64)
     kw = dict(mask=x.mask, act=x.act, bias_kind=x.bias_kind, bias=bias, window=x.window, block=x.block)
-    t0 = time.perf_counter()
-    if ji.WORKLOADS[workload].mxfp8:  # the MXFP8 forward oracle
-        from oracle import mx
-        mx.forward(f(x.q[rows]), k, v, sq, sk, mask=x.mask, bias_kind=x.bias_kind, bias=bias, window=x.window,
-                   block=x.block)
-    elif x.shared_q:  # the seed rows are shared by every sequence
-        A.forward_shared_q(f(x.q), k, v, sk, **kw)
-        if workload_backward(workload):
-            A.backward_shared_q(f(x.q), k, v, sk, f(x.do[rows]), **kw)
-    else:
-        q = f(x.q[rows])
-        A.forward(q, k, v, sq, sk, **kw)
-        if workload_backward(workload):
-            A.backward(q, k, v, sq, sk, f(x.do[rows]), **kw)
-    dt = time.perf_counter() - t0
+
+    def sample(seqs):
+        rows = np.concatenate([np.arange(x.q_off[b], x.q_off[b + 1]) for b in seqs])
+        krows = np.concatenate([np.arange(x.kv_off[b], x.kv_off[b + 1]) for b in seqs])
+        sq = np.concatenate([[0], np.cumsum(lq[seqs])])
+        sk = np.concatenate([[0], np.cumsum(lkv[seqs])])
+        return rows, krows, sq, sk
+
+    def run(seqs):
+        rows, krows, sq, sk = sample(seqs)
+        k, v = f(x.k[krows]), f(x.v[krows])
+        t0 = time.perf_counter()
+        if ji.WORKLOADS[workload].mxfp8:  # the MXFP8 forward oracle
+            from oracle import mx
+            mx.forward(f(x.q[rows]), k, v, sq, sk, mask=x.mask, bias_kind=x.bias_kind, bias=bias,
+                       window=x.window, block=x.block)
+        elif x.shared_q:  # the seed rows are shared by every sequence
+            A.forward_shared_q(f(x.q), k, v, sk, **kw)
+            if bw_on:
+                A.backward_shared_q(f(x.q), k, v, sk, f(x.do[rows]), **kw)
+        else:
+            q = f(x.q[rows])
+            A.forward(q, k, v, sq, sk, **kw)
+            if bw_on:
+                A.backward(q, k, v, sq, sk, f(x.do[rows]), **kw)
+        return time.perf_counter() - t0
+
+    # the oracle's cost follows the dense score rows it forms, whatever the window or block
+    n = np.minimum(lq, lkv)
+    cost = ((n * (n + 1) // 2) if causal else lq * lkv).astype(np.float64) * (4 + (10 if bw_on else 0)) * x.D * x.H
+    # The sample: the sequences in order, each timed on its own (the oracle handles sequences one
+    # after another), until the timed total reaches the target; a sequence whose predicted time
+    # (its cost at the fastest rate seen so far) would take the total past twice the target is
+    # skipped.
+    seqs, dt, best_rate, skipped = [], 0.0, 0.0, 0
+    for b in range(len(lq)):
+        if dt >= seconds_target:
+            break
+        if best_rate > 0 and dt + cost[b] / best_rate > 2 * seconds_target:
+            skipped += 1
+            continue
+        t = run([b])
+        dt += t
+        seqs.append(b)
+        best_rate = max(best_rate, cost[b] / max(t, 1e-9))
+    _, _, sq, sk = sample(seqs)
     fw, bw = useful_flops(sq, sk, x.H, x.D, causal, workload_backward(workload), x.window, x.block)
     return {"value": (fw + bw) / dt / 1e12, "unit": "TFLOPS", "cores": int(cores), "kind": "oracle",
             "nproc": nproc, "cpu_model": model, "blas_threads": blas_threads,
-            "sample": f"{len(seqs)} of {len(lq)} sequences (the first ones), all {x.H} heads, "
+            "sample": f"{len(seqs)} of {len(lq)} sequences (in order; {skipped} longer ones skipped), all {x.H} heads, "
                       f"fwd{'+bwd' if workload_backward(workload) else ''}, {dt:.1f} s, numpy float64 "
                       f"(matrix products in BLAS with {cores} threads, elementwise steps on one)"}
 
@@ -322,7 +348,7 @@ def main() -> int:
         if n:
             kernels[name] = {"avg_ms": ms / n, "launches_per_step": n / args.steps, "total_ms": ms}
     plan.timing_enable(False)
-    clock = None if args.no_clock else gpu_clock_under_load(step, 4.0, median_ms)
+    clock = None if args.no_clock else gpu_clock_under_load(step, 20.0, median_ms)
     torch.cuda.synchronize()
 
     fw, bw = useful_flops(x.q_off, x.kv_off, w.H, w.D, causal, w.backward, w.window, w.block)
@@ -338,13 +364,17 @@ def main() -> int:
     dom = max((kk for kk in kernels if kk in KERNEL_FLOPS_PER_PAIR_D), key=lambda kk: kernels[kk]["total_ms"])
     per_launch_flops = KERNEL_FLOPS_PER_PAIR_D[dom] * w.D * pairs / kernels[dom]["launches_per_step"]
     out_b = 4 if args.out_dtype == "f32" else 2
-    per_launch_bytes = kernel_bytes(dom, int(x.q_off[-1]), int(x.kv_off[-1]), w.H, w.D, out_b, w.act == "softmax")
+    per_launch_bytes = kernel_bytes(dom, int(x.q_off[-1]), int(x.kv_off[-1]), w.H, w.D, out_b, w.act == "softmax",
+                                    mx=w.mxfp8)
     secs = kernels[dom]["avg_ms"] * 1e-3
     traffic = counter_traffic(dom, args.workload)
-    if per_launch_flops / per_launch_bytes >= RIDGE_FLOP_PER_BYTE:
+    # a contraction is priced at the peak of its own operand type: the MXFP8 forward's products are
+    # scaled fp8 MFMAs
+    peak = PEAK_FP8_TFLOPS if (w.mxfp8 and dom == "forward") else PEAK_BF16_TFLOPS
+    if per_launch_flops / per_launch_bytes >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         achieved = per_launch_flops / secs / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom,
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
                     "algorithmic_flops_per_launch": per_launch_flops, "algorithmic_bytes_per_launch": per_launch_bytes}
     else:
         achieved = per_launch_bytes / secs / 1e9

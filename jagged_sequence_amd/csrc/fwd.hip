@@ -366,10 +366,22 @@ void fwd_kernel2(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[sb][r] = acc0;
       }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        sacc[sb] = mfma32(lds_read16(Kt, (kaddr ^ (uint32_t)(kb << 5)) + sb * 32 * kRowBytes), qf[kb], sacc[sb]);
     }
+    // K operands are requested four products ahead of their MFMAs (the two 32-key blocks alternate),
+    // so each product finds its operand loaded instead of waiting for a read issued just before it.
+    bf16x8 kop[2 * NKB];
+#pragma unroll
+    for (int s = 0; s < 2 * NKB; ++s)
+      kop[s] = lds_read16(Kt, (kaddr ^ (uint32_t)((s >> 1) << 5)) + (s & 1) * 32 * kRowBytes);
+#pragma unroll
+    for (int s = 0; s < 2 * NKB; ++s) sacc[s & 1] = mfma32(kop[s], qf[s >> 1], sacc[s & 1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + (BIAS == kBiasBucket ? 16 : 0), 0);
+#pragma unroll
+    for (int s = 0; s < 2 * NKB - 4; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
     const bool need_mask = BAND ? (wlo_all > key0 || whi_all < key0 + BN - 1)
                                 : (key0 + BN > Lkv) || (CAUSAL && key0 + BN - 1 > row0);

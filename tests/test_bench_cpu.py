@@ -44,3 +44,11 @@ def test_kernel_bytes_counts_each_operand_once():
     Tq, Tkv, H, D = 100, 300, 2, 128
     fwd = bench.kernel_bytes("forward", Tq, Tkv, H, D, out_bytes=2, softmax=True)
     assert fwd == 2 * H * D * (Tq + 2 * Tkv) + 2 * H * D * Tq + 4 * H * Tq
+
+
+def test_kernel_bytes_mx_forward_reads_one_byte_and_a_scale():
+    Tq, Tkv, H, D = 64, 64, 1, 128
+    bf = bench.kernel_bytes("forward", Tq, Tkv, H, D, out_bytes=2, softmax=True)
+    mx = bench.kernel_bytes("forward", Tq, Tkv, H, D, out_bytes=2, softmax=True, mx=True)
+    # inputs: 3 x 64 x 128 elements, 2 bytes each against 1 + 1/32
+    assert bf - mx == 3 * 64 * 128 * 2 - 3 * 64 * 128 * 33 // 32
