@@ -37,7 +37,8 @@ METRIC = "useful (unpadded) attention TFLOPS fwd+bwd and % of bf16 MFMA peak, 1Ã
 DEFAULT_WORKLOAD = "longtail"  # the long-tail production-like workload (B = 512, 333,877 tokens)
 # FLOPs each kernel must execute per visible pair and head (its own matrix products):
 #   forward: S = QK^T, O = PV; dK/dV: S, dP = dO V^T, dV = P^T dO, dK = dS^T Q; dQ: S, dP, dQ = dS K
-KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dkdv": 8, "dq": 6}
+#   fused short-query backward: S, dP, dV, dK and dQ once each
+KERNEL_FLOPS_PER_PAIR_D = {"forward": 4, "dkdv": 8, "dq": 6, "bwd_fused": 10}
 
 
 def kernel_bytes(kernel: str, Tq: int, Tkv: int, H: int, D: int, out_bytes: int, softmax: bool,
@@ -47,7 +48,8 @@ def kernel_bytes(kernel: str, Tq: int, Tkv: int, H: int, D: int, out_bytes: int,
     bf16 inputs (2 bytes per element; MXFP8 forward: 1 byte plus one scale byte per 32 elements);
     outputs and gradients in the chosen dtype; lse and Delta fp32.
     forward: read Q, K, V; write O (and lse). dK/dV: read Q, dO, K, V (lse, Delta); write dK, dV.
-    dQ: read Q, dO, K, V (lse, Delta); write dQ.
+    dQ: read Q, dO, K, V (lse, Delta); write dQ. Fused short-query backward: read Q, dO, K, V, O
+    (for Delta) and lse; write dQ, dK, dV.
     """
     q, kv = Tq * H * D, Tkv * H * D
     stats = 2 * Tq * H * 4 if softmax else 0
@@ -56,12 +58,15 @@ def kernel_bytes(kernel: str, Tq: int, Tkv: int, H: int, D: int, out_bytes: int,
         return ins + out_bytes * q + (Tq * H * 4 if softmax else 0)
     if kernel == "dkdv":
         return 2 * (2 * q + 2 * kv) + stats + out_bytes * 2 * kv
+    if kernel == "bwd_fused":
+        return 2 * (2 * q + 2 * kv) + out_bytes * q + Tq * H * 4 + out_bytes * (2 * kv + q)
     return 2 * (2 * q + 2 * kv) + stats + out_bytes * q
 
 
 KERNEL_SOURCES = {"forward": ["fwd.hip", "device_common.h", "tile_lds.h", "jfa_internal.h"],
                   "dkdv": ["bwd.hip", "device_common.h", "tile_lds.h", "jfa_internal.h"],
-                  "dq": ["bwd.hip", "device_common.h", "tile_lds.h", "jfa_internal.h"]}
+                  "dq": ["bwd.hip", "device_common.h", "tile_lds.h", "jfa_internal.h"],
+                  "bwd_fused": ["bwd.hip", "device_common.h", "tile_lds.h", "jfa_internal.h"]}
 
 
 def source_hash(kernel: str) -> str:

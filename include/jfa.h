@@ -213,13 +213,17 @@ jfa_status jfa_backward_noalloc(jfa_plan_t plan, const void* q, const void* k, c
 jfa_status jfa_plan_schedule(jfa_plan_t plan, int32_t which, int32_t* out, size_t cap, size_t* count);
 
 /* Tile geometry and slot counts the plan used: writes up to `n` of
- * {fwd BM, fwd BN, dq BM, dq BN, dkdv BM, dkdv BN, fwd slots, dq slots, dkdv slots}. */
+ * {fwd BM, fwd BN, dq BM, dq BN, dkdv BM, dkdv BN, fwd slots, dq slots, dkdv slots, fused backward}
+ * (the last is 1 when the backward runs as one fused pass over the dQ items: every sequence has at
+ * most 64 queries, head_dim 128, softmax, no window or block limit, no shared queries, and every
+ * sequence with keys has queries). */
 jfa_status jfa_plan_info(jfa_plan_t plan, int32_t* info, size_t n);
 
 /* Per-kernel timing with HIP events recorded around every launch of this plan (for
  * measurement; adds two event records per launch while on). Kernel ids: 0 forward,
  * 1 forward combine, 3 dK/dV, 4 dQ (which also computes rowsum(dO * O) for dK/dV), 5 backward
- * partial reduce, 6 bias-gradient clear and finish (2 is not used).
+ * partial reduce, 6 bias-gradient clear and finish, 7 MXFP8 quantisation, 8 fused backward of
+ * short query sets (2 is not used).
  * jfa_timing_read waits for the recorded events and returns their summed time and count;
  * jfa_timing_enable(plan, 1) also clears previous records. Not thread safe. */
 jfa_status jfa_timing_enable(jfa_plan_t plan, int32_t enable);

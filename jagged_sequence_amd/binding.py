@@ -31,7 +31,7 @@ PLAN_HOST_ONLY = 0x1
 PLAN_NO_SPLIT = 0x2
 PLAN_SHARED_Q = 0x4
 PLAN_MXFP8 = 0x8
-KERNELS = {"forward": 0, "combine": 1, "dkdv": 3, "dq": 4, "reduce": 5, "dbias": 6, "mx_quantize": 7}
+KERNELS = {"forward": 0, "combine": 1, "dkdv": 3, "dq": 4, "reduce": 5, "dbias": 6, "mx_quantize": 7, "bwd_fused": 8}
 SYMBOLS = ["jfa_plan", "jfa_workspace_bytes", "jfa_forward", "jfa_backward", "jfa_backward_noalloc",
            "jfa_plan_schedule", "jfa_plan_info", "jfa_timing_enable", "jfa_timing_read", "jfa_plan_destroy",
            "jfa_status_string", "jfa_last_error"]
@@ -195,9 +195,10 @@ class Plan:
         return out.reshape(n.value, per)
 
     def info(self) -> dict:
-        buf = (ctypes.c_int32 * 9)()
-        _check(LIB.jfa_plan_info(self._h, buf, 9))
-        keys = ["fwd_bm", "fwd_bn", "dq_bm", "dq_bn", "kv_bm", "kv_bn", "fwd_slots", "dq_slots", "kv_slots"]
+        buf = (ctypes.c_int32 * 10)()
+        _check(LIB.jfa_plan_info(self._h, buf, 10))
+        keys = ["fwd_bm", "fwd_bn", "dq_bm", "dq_bn", "kv_bm", "kv_bn", "fwd_slots", "dq_slots", "kv_slots",
+                "fused_bwd"]
         return dict(zip(keys, list(buf)))
 
     def timing_enable(self, on: bool = True):

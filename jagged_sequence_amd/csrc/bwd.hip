@@ -1338,6 +1338,305 @@ void bwd_dkdv_kernel2(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- fused backward, short query sets
+// D = 128, softmax, every sequence with at most 64 queries (a single query tile). One workgroup per
+// dQ item (sequence, head, range of 64-key tiles) keeps the sequence's Q and dO tiles in LDS for the
+// whole item and streams the range's K and V tiles through a three-stage ring, each tile read once.
+// Per tile: waves 0-1 (A) form S = Q K^T and P for keys 32 a .. 32 a + 31 and dV = P^T dO; waves
+// 2-3 (B) form dP = dO V^T, dS = P (dP - Delta) and dK = dS^T Q for the same keys; all four waves
+// then add dS K to dQ (wave w: dimensions 32 w .. 32 w + 31). Since every query of the sequence is
+// in the tile, a tile's dK and dV are complete and stored at once; only dQ of split ranges needs
+// partial sums. Against separate dQ and dK/dV passes this reads K and V once instead of twice
+// (aihot.vn GEM page, "Generalized Dot-Product Attention (GDPA)": short and asymmetric key / value
+// sets).
+struct alignas(16) FusedSmem {
+  float lse2[kKvBM];                        // -lse in log2 units
+  float dlt[kKvBM];                         // Delta
+  float tab[kBuckets];
+  float diag[2][kDiagLen];                  // per A wave: bias values of its 95 distances
+  unsigned long long dbh[2][kDbiasBins];    // per B wave: bias-gradient bins (fixed point)
+  uint4 xch[2][2][2][64];                   // [key half][query block][8-row half][lane]: P (bf16)
+  unsigned char dst[64 * kRowBytes];        // dS^T: row = key of the tile, 64 queries (swizzled rows)
+  unsigned char qg[2][kKvBM * kRowBytes];   // Q, dO
+  unsigned char kv[3][2][64 * kRowBytes];   // ring: [stage][K, V]
+};
+
+template <int BIASX, int MK>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_fused_kernel(BwdArgs a) {
+  constexpr int D = 128, BM = kKvBM, BN = 64, NKB = D / 16, NDB = D / 32;
+  constexpr int BIAS = BIASX & 3;
+  constexpr bool DBIAS = (BIASX & kBiasGrad) != 0;
+  constexpr bool CAUSAL = MK == kMaskCausal;
+  constexpr int kLoadsPerTile = 8;  // dma16 instructions per wave per K / V tile (4 rows x 4, twice)
+  __shared__ FusedSmem sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool isB = wave >= 2;
+  const int half = wave & 1;  // A / B: key half of the tile
+  const WorkRec w = load_item(a.dq_items, blockIdx.x);
+  const int h = w.h, k0 = w.lo, k1 = w.hi, slot = w.slot;
+  const int qs = w.qs, Lq = w.Lq, ks = w.ks, Lkv = w.Lkv;
+  const int H = a.H, rs = H * D;
+  const float inv_scale = 1.0f / a.scale;
+  const float smul = a.scale * kLog2e;
+  const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
+  const float lse_shift = (BIAS == kBiasScalar) ? bias_c : 0.0f;
+
+  // ---- item prologue: Q and dO tiles, statistics, bias table, first two K / V tiles
+  const __amdgpu_buffer_rsrc_t qsr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+  const __amdgpu_buffer_rsrc_t gsr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
+  const __amdgpu_buffer_rsrc_t ksr = slice_rsrc(a.k + (size_t)ks * rs + h * D, Lkv, rs, D);
+  const __amdgpu_buffer_rsrc_t vsr = slice_rsrc(a.v + (size_t)ks * rs + h * D, Lkv, rs, D);
+  const TileLoader ld = make_loader64(wave, lane, rs);
+  load_tile64(ld, qsr, 0, rs, sm.qg[0], wave);
+  load_tile64(ld, gsr, 0, rs, sm.qg[1], wave);
+  if (wave == 0) {
+    const __amdgpu_buffer_rsrc_t lser = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.lse) + (size_t)h * a.Tq + qs, (short)0, Lq * 4, 0x00020000);
+    dma4(lser, (uint32_t)lane * 4u, sm.lse2);
+  }
+  if (BIAS == kBiasBucket && wave == 1) {
+    const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.bias) + h * kBuckets,
+                                                                        (short)0, kBuckets * 4, 0x00020000);
+    dma4(tr, (uint32_t)lane * 4u, sm.tab);
+  }
+  auto issue = [&](int kt, int stg) {
+    load_tile64(ld, ksr, kt * BN, rs, sm.kv[stg][0], wave);
+    load_tile64(ld, vsr, kt * BN, rs, sm.kv[stg][1], wave);
+  };
+  if (k0 < k1) issue(k0, 0);
+  if (k0 + 1 < k1) issue(k0 + 1, 1);
+  // Delta_i = <dO_i, O_i>: four threads per row, 32 dimensions each.
+  {
+    const int row = tid >> 2, part = tid & 3;
+    float acc = 0.0f;
+    if (row < Lq) {
+      const size_t base = ((size_t)(qs + row) * H + h) * D + part * 32;
+      const uint16_t* gp = a.dout + base;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 g = load16(gp + 8 * c);
+        float gv[8], ov[8];
+        unpack8(g, gv);
+        if (a.out_f32) {
+          const float4 o0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.out) + base + 8 * c);
+          const float4 o1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.out) + base + 8 * c + 4);
+          ov[0] = o0.x; ov[1] = o0.y; ov[2] = o0.z; ov[3] = o0.w; ov[4] = o1.x; ov[5] = o1.y; ov[6] = o1.z; ov[7] = o1.w;
+        } else {
+          unpack8(load16(static_cast<const uint16_t*>(a.out) + base + 8 * c), ov);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += gv[j] * ov[j];
+      }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (part == 0) sm.dlt[row] = acc;
+  }
+  if (DBIAS && isB) sm.dbh[half][lane] = 0ull;
+  wait_vm();
+  if (wave == 0) {
+    const float x = sm.lse2[lane];
+    sm.lse2[lane] = (lane < Lq && x != kNegInf) ? -(x - lse_shift) * kLog2e : kNegInf;
+  }
+  __syncthreads();
+
+  const uint32_t raddr = row_operand_base(kappa(l32), hh);  // Q / dO rows as A operands
+  uint32_t T[2];
+  tr_operand_bases(lane, T);
+  DbiasLane dbl;
+  f32x16 dqa[2];  // dQ^T of dimensions 32 wave .. + 31, query blocks 0 and 1 (unscaled)
+  dqa[0] = f32x16{};
+  dqa[1] = f32x16{};
+
+  f32x16 acc[NDB];  // A: dV, B: dK of the current tile (dK unscaled)
+  auto tile = [&](const int kt, auto st_tag) {
+    constexpr int ST = decltype(st_tag)::value;
+    // Outstanding at this point: tile kt's loads, then tile kt + 1's (and the previous tile's
+    // stores). Loads complete in order, so with at most kLoadsPerTile operations left tile kt has
+    // landed (tile kt + 1 may still be in flight).
+    if (kt + 1 < k1)
+      wait_vm_keep<kLoadsPerTile>();
+    else
+      wait_vm();
+    __syncthreads();  // tile kt is published; every wave is done with the previous tile's LDS data
+    if (kt + 2 < k1) issue(kt + 2, (ST + 2) % 3);
+    const unsigned char* Kt = sm.kv[ST][0];
+    const unsigned char* Vt = sm.kv[ST][1];
+    const int key_w = kt * BN + 32 * half;  // first key of this wave's half
+    const int kj = key_w + l32;
+    // the wave's 32 keys as B operands (lane = key): K for A waves, V for B waves
+    bf16x8 frag[NKB];
+    {
+      const unsigned char* src = isB ? Vt : Kt;
+      const uint32_t fb = row_operand_base(32 * half + l32, hh);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) frag[kb] = lds_read16(src, fb ^ (uint32_t)(kb << 5));
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+    bf16x8 pk[2][2];  // A: P, B: dS, as B operands [query block][16-row step]
+    f32x16 pacc[2];   // B: dP
+    if (!isB) {
+      if (BIAS == kBiasBucket) fill_diag(sm.diag[half], sm.tab, -key_w - 31, inv_scale, lane);
+      const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > 0);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 sacc;
+        if (BIAS == kBiasBucket) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const float* dvp = &sm.diag[half][31 + 32 * qb + 16 * c + 8 * hh - l32];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sacc[8 * c + j] = dvp[j];
+          }
+        } else {
+          sacc = f32x16{};
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          sacc = mfma32(lds_read16(sm.qg[0], (raddr ^ (uint32_t)(kb << 5)) + qb * 32 * kRowBytes), frag[kb], sacc);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int rbase = 32 * qb + 16 * c + 8 * hh;
+          const float4 x0 = *reinterpret_cast<const float4*>(&sm.lse2[rbase]);
+          const float4 x1 = *reinterpret_cast<const float4*>(&sm.lse2[rbase + 4]);
+          const float l8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          float pv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(__builtin_fmaf(sacc[8 * c + j], smul, l8[j]));
+          if (need_mask) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int qi = rbase + j;
+              pv[j] = (kj >= Lkv || (CAUSAL && kj > qi)) ? 0.0f : pv[j];
+            }
+          }
+          pk[qb][c] = pack8(pv);
+          sm.xch[half][qb][c][lane] = __builtin_bit_cast(uint4, pk[qb][c]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        pacc[qb] = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          pacc[qb] = mfma32(lds_read16(sm.qg[1], (raddr ^ (uint32_t)(kb << 5)) + qb * 32 * kRowBytes), frag[kb], pacc[qb]);
+      }
+    }
+    __syncthreads();  // P is published
+    if (!isB) {
+      // dV^T += dO^T P
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t base = (uint32_t)(16 * s * kRowBytes);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = mfma32(lds_read_tr(sm.qg[1], base + (T[0] ^ (uint32_t)(64 * db)), base + (T[1] ^ (uint32_t)(64 * db))),
+                           pk[s >> 1][s & 1], acc[db]);
+      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int rbase = 32 * qb + 16 * c + 8 * hh;
+          float pv[8];
+          unpack8(sm.xch[half][qb][c][lane], pv);
+          const float4 y0 = *reinterpret_cast<const float4*>(&sm.dlt[rbase]);
+          const float4 y1 = *reinterpret_cast<const float4*>(&sm.dlt[rbase + 4]);
+          const float d8[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+          float dsv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dsv[j] = pv[j] * (pacc[qb][8 * c + j] - d8[j]);
+          pk[qb][c] = pack8(dsv);
+          // dS^T row (this lane's key), logical chunk rbase / 8 of the query columns
+          const int r = 32 * half + l32;
+          *reinterpret_cast<uint4*>(&sm.dst[r * kRowBytes + (((rbase >> 3) ^ swz(r)) << 4)]) =
+              __builtin_bit_cast(uint4, pk[qb][c]);
+          if (DBIAS) dbl.add_run<BIAS == kBiasBucket>(sm.dbh[half], rbase - kj, dsv);
+        }
+      // dK^T += Q^T dS
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t base = (uint32_t)(16 * s * kRowBytes);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = mfma32(lds_read_tr(sm.qg[0], base + (T[0] ^ (uint32_t)(64 * db)), base + (T[1] ^ (uint32_t)(64 * db))),
+                           pk[s >> 1][s & 1], acc[db]);
+      }
+    }
+    __syncthreads();  // dS^T is published
+    // dQ^T (dimensions 32 wave ..) += K^T dS^T over the tile's 64 keys
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t base = (uint32_t)(16 * s * kRowBytes);
+      const bf16x8 kop = lds_read_tr(Kt, base + (T[0] ^ (uint32_t)(64 * wave)), base + (T[1] ^ (uint32_t)(64 * wave)));
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        dqa[qb] = mfma32(kop, lds_read_tr(sm.dst, base + (T[0] ^ (uint32_t)(64 * qb)), base + (T[1] ^ (uint32_t)(64 * qb))),
+                         dqa[qb]);
+    }
+    // The tile's dV (A) or dK (B) is complete: store it. bf16 rows go out through LDS as whole
+    // rows (a lane's accumulators hold 4-element pieces of its key's row): once every wave is done
+    // with this stage, its K and V tiles (32 KB) give each wave 8 KB; the stage is reloaded only
+    // after the next tile's first barrier.
+    void* dstp = isB ? a.dk : a.dv;
+    const float sc = isB ? a.scale : 1.0f;
+    if (!a.grad_f32) {
+      __syncthreads();
+      store_rows_staged(sm.kv[ST][0] + wave * (32 * kRowBytes), acc, sc, lane, Lkv - key_w,
+                        [&](int r) { return static_cast<char*>(dstp) + (((size_t)(ks + key_w + r) * H + h) * D) * 2; });
+    } else if (kj < Lkv) {
+      const size_t base = ((size_t)(ks + kj) * H + h) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(dstp, base + 32 * db + 8 * g + 4 * hh, acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc,
+                 acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc, 1);
+    }
+  };
+  for (int kt = k0; kt < k1; kt += 3) {
+    tile(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < k1) tile(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 2 < k1) tile(kt + 2, std::integral_constant<int, 2>{});
+  }
+
+  if (DBIAS && isB) {
+    dbl.flush(sm.dbh[half]);
+    wave_lds_fence();
+    constexpr int NB = BIAS == kBiasBucket ? kDbiasBins : 1;
+    if (lane < NB) {
+      const unsigned long long x = sm.dbh[half][lane];
+      if (x) atomicAdd(a.dbias_acc + (size_t)h * NB + lane, x);
+    }
+  }
+  // dQ: accumulator register r of query block qb holds dimension 32 wave + 8 (r/4) + 4 hh + r%4 of
+  // query row 32 qb + lane % 32.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = 32 * qb + l32;
+    if (qi >= Lq) continue;
+    if (slot < 0) {
+      const size_t base = ((size_t)(qs + qi) * H + h) * D + 32 * wave;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4(a.dq, base + 8 * g + 4 * hh, dqa[qb][4 * g] * a.scale, dqa[qb][4 * g + 1] * a.scale,
+               dqa[qb][4 * g + 2] * a.scale, dqa[qb][4 * g + 3] * a.scale, a.grad_f32);
+    } else {
+      float* pp = a.part_dq + ((size_t)slot * kDqBM + qi) * D + 32 * wave;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(pp + 8 * g + 4 * hh) =
+            make_float4(dqa[qb][4 * g], dqa[qb][4 * g + 1], dqa[qb][4 * g + 2], dqa[qb][4 * g + 3]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fixed-order partial sums
 // One workgroup per split group.
 template <int D>
@@ -1485,6 +1784,26 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n, int resident
     JFA_DISPATCH_ACT_GRAD(dkdv_select, 64, m, go)
   } else {
     JFA_DISPATCH_ACT_GRAD(dkdv_select, 128, m, go)
+  }
+}
+
+hipError_t launch_bwd_fused(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(n), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  };
+  // softmax only: a per-head scalar has a zero gradient, so only the bucket table has a gradient variant
+  const int bx = m.bias == kBiasBucket && m.dbias ? (kBiasBucket | kBiasGrad) : m.bias;
+  auto by_mask = [&](auto bias_tag) {
+    constexpr int BX = decltype(bias_tag)::value;
+    return m.causal ? go(bwd_fused_kernel<BX, kMaskCausal>) : go(bwd_fused_kernel<BX, kMaskNone>);
+  };
+  switch (bx) {
+    case kBiasNone: return by_mask(std::integral_constant<int, kBiasNone>{});
+    case kBiasScalar: return by_mask(std::integral_constant<int, kBiasScalar>{});
+    case kBiasBucket: return by_mask(std::integral_constant<int, kBiasBucket>{});
+    default: return by_mask(std::integral_constant<int, kBiasBucket | kBiasGrad>{});
   }
 }
 

@@ -409,6 +409,10 @@ struct jfa_plan_s {
   float scale = 0.0f;
   int out_f32 = 0, grad_f32 = 0;
   int q_shared = 0;  // JFA_PLAN_SHARED_Q
+  // Backward as one fused pass over the dQ items (every sequence has at most kKvBM queries, D = 128,
+  // softmax, no band limits, no shared queries, and every sequence with keys has queries, so that
+  // the dQ items cover every key)
+  int fused_bwd = 0;
   int mx = 0;        // JFA_PLAN_MXFP8
   int n_vtiles = 0;  // MXFP8: 64-key tiles over all sequences (transposed quantised V)
   std::vector<int32_t> vtiles;  // [n_vtiles][2]: first key row, keys in the tile
@@ -670,6 +674,21 @@ jfa_status run_backward(jfa_plan_s* P, const void* q, const void* k, const void*
   Modes m = P->modes;
   m.dbias = dbias ? 1 : 0;
   jfa_status st = JFA_OK;
+  if (P->fused_bwd) {
+    // one pass over the dQ items: dQ (or its partial sums) and the dK / dV of every key
+    if (dbias) {
+      st = timed(P, 6, s, [&] { return launch_bwd_dbias_clear(a, m, s); }, "bias-gradient clear launch");
+      if (st != JFA_OK) return st;
+    }
+    st = timed(P, 8, s, [&] { return launch_bwd_fused(a, m, (int)P->lists[kDq].n_items(), s); }, "fused backward launch");
+    if (st != JFA_OK) return st;
+    if (P->lists[kDq].n_groups() > 0) {
+      st = timed(P, 5, s, [&] { return launch_bwd_reduce_dq(a, m, (int)P->lists[kDq].n_groups(), s); }, "dQ reduce launch");
+      if (st != JFA_OK) return st;
+    }
+    if (dbias) st = timed(P, 6, s, [&] { return launch_bwd_dbias_finish(a, m, s); }, "bias-gradient finish launch");
+    return st;
+  }
   // The queue counters are zeroed by the dQ kernel, or here when there is no dQ item.
   if (dbias || (a.kv_queue && P->lists[kDq].n_items() == 0 && a.kv_n > 0)) {
     st = timed(P, 6, s, [&] { return launch_bwd_dbias_clear(a, m, s); }, "bias-gradient clear launch");
@@ -807,6 +826,11 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   }
   P->q_shared = (p.flags & JFA_PLAN_SHARED_Q) ? 1 : 0;
   if (P->q_shared) share_query_slots(P->lists[kDq]);
+  if (P->modes.kv_short && !P->modes.band && !P->q_shared) {
+    bool covered = true;
+    for (int b = 0; b < P->B; ++b) covered = covered && (lq[b] > 0 || lkv[b] == 0);
+    P->fused_bwd = covered ? 1 : 0;
+  }
   for (auto& L : P->lists) L.order = dispatch_order(L, P->B, P->H);
 
   // workspace layout
@@ -979,9 +1003,9 @@ jfa_status jfa_plan_schedule(jfa_plan_t P, int32_t which, int32_t* out, size_t c
 
 jfa_status jfa_plan_info(jfa_plan_t P, int32_t* info, size_t n) {
   if (!P || !info) return fail(JFA_ERR_NULL_ARG, "plan or info is NULL");
-  const int32_t v[9] = {kFwdBM, kFwdBN, kDqBM, kDqBN, kKvBM, P->kv_bn, P->lists[kFwd].slots, P->lists[kDq].slots,
-                        P->lists[kKv].slots};
-  std::copy_n(v, std::min<size_t>(n, 9), info);
+  const int32_t v[10] = {kFwdBM, kFwdBN, kDqBM, kDqBN, kKvBM, P->kv_bn, P->lists[kFwd].slots, P->lists[kDq].slots,
+                         P->lists[kKv].slots, P->fused_bwd};
+  std::copy_n(v, std::min<size_t>(n, 10), info);
   return JFA_OK;
 }
 

@@ -122,14 +122,15 @@ __global__ __launch_bounds__(256) void mx_quantize_v_kernel(const uint16_t* v, c
 }
 
 // ---------------------------------------------------------------- forward
-// LDS per ring stage: K tile 64 keys x 128 bytes (16-byte chunk c of row r at c ^ (r & 7)), V^T tile
-// 128 features x 64 bytes (chunk c of row r at c ^ ((r >> 1) & 3)), K scales (one word per key:
-// its four feature blocks), V scales ([g][d] bytes).
+// LDS per stage of a three-stage ring (tile kt + 2 is loaded while tile kt is used): K tile 64
+// keys x 128 bytes (16-byte chunk c of row r at c ^ (r & 7)), V^T tile 128 features x 64 bytes
+// (chunk c of row r at c ^ ((r >> 1) & 3)), K scales (one word per key: its four feature blocks),
+// V scales ([g][d] bytes).
 struct alignas(16) MxSmem {
-  unsigned char k[2][64 * 128];
-  unsigned char vt[2][128 * 64];
-  uint32_t ksc[2][64];
-  unsigned char vsc[2][256];
+  unsigned char k[3][64 * 128];
+  unsigned char vt[3][128 * 64];
+  uint32_t ksc[3][64];
+  unsigned char vsc[3][256];
   float tab[kBuckets];
   float diag[4][kDiagLen];
 };
@@ -229,6 +230,7 @@ void fwd_mx_kernel(MxArgs a) {
   };
 
   if (k0 < k1) issue(k0, 0);
+  if (k0 + 1 < k1) issue(k0 + 1, 1);
   if (BIAS == kBiasBucket) {
     if (tid < kBuckets) sm.tab[tid] = tabv;
     __syncthreads();
@@ -239,10 +241,17 @@ void fwd_mx_kernel(MxArgs a) {
     const int key0 = kt * BN;
     const bool wskip =
         row0 >= Lq || (CAUSAL ? key0 > row0 + 31 : (BAND ? (key0 > whi || key0 + BN - 1 < wlo) : false));
-    wait_vm();
+    // Tile kt has landed once at most the next tile's loads are outstanding (four per wave, five
+    // for the waves that also load the scales).
+    if (kt + 1 >= k1)
+      wait_vm();
+    else if (wave < 2)
+      wait_vm_keep<5>();
+    else
+      wait_vm_keep<4>();
     if (BIAS == kBiasBucket && !wskip) fill_diag(sm.diag[wave], sm.tab, key0 - row0 - 31, inv_scale, lane);
     __syncthreads();
-    if (kt + 1 < k1) issue(kt + 1, ST ^ 1);
+    if (kt + 2 < k1) issue(kt + 2, (ST + 2) % 3);
     if (wskip) return;
 
     // S^T: A = K rows kappa(l32) + 32 sb; product m takes features 64 m + 16 hh (+ 32).
@@ -285,12 +294,16 @@ void fwd_mx_kernel(MxArgs a) {
           sacc[sb][r] = masked ? kNegInf : sacc[sb][r];
         }
     }
-    float mx = kNegInf;
+    // Largest score of each 32-key block of the row (the lane's 16 and lane l^32's 16).
+    float bm[2];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < 2; ++sb) {
+      bm[sb] = sacc[sb][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[sb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * smul;
+      for (int r = 1; r < 16; ++r) bm[sb] = fmaxf(bm[sb], sacc[sb][r]);
+      bm[sb] = fmaxf(bm[sb], __shfl_xor(bm[sb], 32));
+    }
+    const float mx = fmaxf(bm[0], bm[1]) * smul;
     if (__ballot(mx > m_run + kLazyMx)) {
       const float m_new = ceilf(fmaxf(m_run, mx));
       const float alpha = m_new == kNegInf ? 0.0f : fast_exp2(m_run - m_new);  // a power of two
@@ -302,32 +315,34 @@ void fwd_mx_kernel(MxArgs a) {
       m_run = m_new;
     }
     const float nm = m_run == kNegInf ? 0.0f : -m_run;
-    float p[2][16];
-    float lsum = 0.0f, bmax[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      bmax[sb] = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[sb][r] = fast_exp2(__builtin_fmaf(sacc[sb][r], smul, nm));
-        bmax[sb] = fmaxf(bmax[sb], p[sb][r]);
-        lsum += p[sb][r];
-      }
-    }
-    l_run += lsum;
-    // P blocks: keys 32 sb .. 32 sb + 31 of the row, 16 values in each lane half.
+    // P blocks: keys 32 sb .. 32 sb + 31 of the row, 16 values in each lane half. P~ = 2^x with
+    // x = s smul - m_run, so the block's largest P~ is 2^xb (xb from its largest score) and its scale
+    // exponent is se = max(floor(xb) - 8, -127) with no need to look at the P~ values themselves; the
+    // scaled elements P~ / 2^se = 2^(x - se) come straight out of the exponential, and the row sum of
+    // P~ is the block sums of the scaled elements times 2^se. A block with no visible key has
+    // xb = -inf: its elements are 0 and its scale byte 0.
+    float lsum = 0.0f;
     int pscb[2];
     i32x8 pb;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-      const float am = fmaxf(bmax[sb], __shfl_xor(bmax[sb], 32));
-      float inv;
-      mx_scale(am, pscb[sb], inv);
+      const float xb = __builtin_fmaf(bm[sb], smul, nm);
+      const float se = bm[sb] == kNegInf ? -127.0f : fmaxf(floorf(xb) - 8.0f, -127.0f);
+      pscb[sb] = (int)se + 127;
+      const float c = nm - se;  // integers: exact
+      float pq[16], bsum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = fast_exp2(__builtin_fmaf(sacc[sb][r], smul, c));
+        bsum += x;
+        pq[r] = fminf(x, 448.0f);
+      }
+      lsum += __builtin_ldexpf(bsum, (int)se);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        pb[4 * sb + q] = (int)pack4_fp8(fminf(p[sb][4 * q] * inv, 448.0f), fminf(p[sb][4 * q + 1] * inv, 448.0f),
-                                        fminf(p[sb][4 * q + 2] * inv, 448.0f), fminf(p[sb][4 * q + 3] * inv, 448.0f));
+        pb[4 * sb + q] = (int)pack4_fp8(pq[4 * q], pq[4 * q + 1], pq[4 * q + 2], pq[4 * q + 3]);
     }
+    l_run += lsum;
     const int psc = hh ? pscb[1] : pscb[0];  // lane half hh scales contraction block hh = keys 32 hh ..
     // O^T += V^T P^T: A = V^T rows 32 db + l32, the lane half's 32 bytes at 32 hh.
 #pragma unroll
@@ -341,9 +356,10 @@ void fwd_mx_kernel(MxArgs a) {
       o[db] = mfma_mx(va, (int)sm.vsc[ST][128 * hh + r], pb, psc, o[db]);
     }
   };
-  for (int kt = k0; kt < k1; kt += 2) {
+  for (int kt = k0; kt < k1; kt += 3) {
     tile(kt, std::integral_constant<int, 0>{});
     if (kt + 1 < k1) tile(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 2 < k1) tile(kt + 2, std::integral_constant<int, 2>{});
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);

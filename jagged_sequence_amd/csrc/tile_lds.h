@@ -99,6 +99,16 @@ __device__ __forceinline__ void load_tile64_w8(const TileLoader& t, __amdgpu_buf
 // Wait for this wave's outstanding global loads (including loads into LDS).
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait on the vector-memory counter only, until at most N of this wave's vector memory operations
+// are outstanding. Loads complete in issue order, so once at most N operations are left, every
+// load followed by at least N loads has landed: with the next tile's N loads issued after the
+// current tile's, this waits for the current tile and leaves the next one in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
 // Row operand: lane reads logical chunk (2 kb + hh) of tile row `r`: byte address
 // r * 256 + (((2 kb + hh) ^ swz(r)) << 4) = (r * 256 + ((hh ^ swz(r)) << 4)) ^ (kb << 5).
 __device__ __forceinline__ uint32_t row_operand_base(int r, int hh) {

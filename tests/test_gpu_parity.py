@@ -153,7 +153,20 @@ def test_short_query_items(mask, bias):
     x = ji.make_inputs(lq, lkv, 2, 128, wid=45, mask=mask, act="softmax", bias_kind=bias, bias_sigma=0.5)
     say(f"case short-query mask={mask} bias={bias}")
     gpu = run_gpu(x)
-    assert gpu["plan"].info()["kv_bn"] == 64
+    info = gpu["plan"].info()
+    assert info["kv_bn"] == 64 and info["fused_bwd"] == 1
+    compare(x, gpu, oracle(x))
+
+
+@pytest.mark.parametrize("lq,lkv,fused", [([5, 0, 64, 3], [0, 0, 200, 70], 1), ([0, 30, 64], [50, 40, 129], 0)],
+                         ids=["no-keys", "keys-without-queries"])
+def test_short_query_empty_sequences(lq, lkv, fused):
+    """Short query sets with empty sequences: a sequence without keys (dQ = 0) keeps the fused
+    backward; one with keys but no queries (dK = dV = 0 for its keys) takes the separate passes."""
+    x = ji.make_inputs(lq, lkv, 2, 128, wid=48, mask="none", act="softmax", bias_kind="bucket", bias_sigma=0.5)
+    say(f"case short-query empty sequences lq={lq} lkv={lkv}")
+    gpu = run_gpu(x)
+    assert gpu["plan"].info()["fused_bwd"] == fused
     compare(x, gpu, oracle(x))
 
 
