@@ -215,8 +215,8 @@ jfa_status jfa_plan_schedule(jfa_plan_t plan, int32_t which, int32_t* out, size_
 /* Tile geometry and slot counts the plan used: writes up to `n` of
  * {fwd BM, fwd BN, dq BM, dq BN, dkdv BM, dkdv BN, fwd slots, dq slots, dkdv slots, fused backward}
  * (the last is 1 when the backward runs as one fused pass over the dQ items: every sequence has at
- * most 64 queries, head_dim 128, softmax, no window or block limit, no shared queries, and every
- * sequence with keys has queries). */
+ * most 64 queries, head_dim 128, no window or block limit, and every sequence with keys has
+ * queries). */
 jfa_status jfa_plan_info(jfa_plan_t plan, int32_t* info, size_t n);
 
 /* Per-kernel timing with HIP events recorded around every launch of this plan (for

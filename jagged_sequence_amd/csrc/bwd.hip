@@ -1339,35 +1339,37 @@ void bwd_dkdv_kernel2(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- fused backward, short query sets
-// D = 128, softmax, every sequence with at most 64 queries (a single query tile). One workgroup per
-// dQ item (sequence, head, range of 64-key tiles) keeps the sequence's Q and dO tiles in LDS for the
-// whole item and streams the range's K and V tiles through a three-stage ring, each tile read once.
-// Per tile: waves 0-1 (A) form S = Q K^T and P for keys 32 a .. 32 a + 31 and dV = P^T dO; waves
-// 2-3 (B) form dP = dO V^T, dS = P (dP - Delta) and dK = dS^T Q for the same keys; all four waves
+// D = 128, every sequence with at most 64 queries (a single query tile). One workgroup per dQ item
+// (sequence, head, range of 64-key tiles) keeps the sequence's Q and dO tiles in LDS for the whole
+// item and streams the range's K and V tiles through a three-stage ring, each tile read once. Per
+// tile: waves 0-1 (A) form S = Q K^T and P for keys 32 a .. 32 a + 31 and dV = P^T dO; waves 2-3 (B)
+// form dP = dO V^T, dS and dK = dS^T Q for the same keys (softmax: A hands B the probabilities and
+// dS = P (dP - Delta); GDPA: A hands B act'(S) / Lkv and dS = dP act'(S) / Lkv); all four waves
 // then add dS K to dQ (wave w: dimensions 32 w .. 32 w + 31). Since every query of the sequence is
-// in the tile, a tile's dK and dV are complete and stored at once; only dQ of split ranges needs
-// partial sums. Against separate dQ and dK/dV passes this reads K and V once instead of twice
-// (aihot.vn GEM page, "Generalized Dot-Product Attention (GDPA)": short and asymmetric key / value
-// sets).
+// in the tile, a tile's dK and dV are complete and stored at once; only dQ of split ranges (and of
+// shared queries, summed over sequences) needs partial sums. Against separate dQ and dK/dV passes
+// this reads K and V once instead of twice (aihot.vn GEM page, "Generalized Dot-Product Attention
+// (GDPA)": short and asymmetric key / value sets, and PMA's shared seed queries).
 struct alignas(16) FusedSmem {
   float lse2[kKvBM];                        // -lse in log2 units
   float dlt[kKvBM];                         // Delta
   float tab[kBuckets];
   float diag[2][kDiagLen];                  // per A wave: bias values of its 95 distances
   unsigned long long dbh[2][kDbiasBins];    // per B wave: bias-gradient bins (fixed point)
-  uint4 xch[2][2][2][64];                   // [key half][query block][8-row half][lane]: P (bf16)
+  uint4 xch[2][2][2][64];                   // [key half][query block][8-row half][lane]: P or act'/Lkv (bf16)
   unsigned char dst[64 * kRowBytes];        // dS^T: row = key of the tile, 64 queries (swizzled rows)
   unsigned char qg[2][kKvBM * kRowBytes];   // Q, dO
   unsigned char kv[3][2][64 * kRowBytes];   // ring: [stage][K, V]
 };
 
-template <int BIASX, int MK>
+template <int ACT, int BIASX, int MK>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void bwd_fused_kernel(BwdArgs a) {
   constexpr int D = 128, BM = kKvBM, BN = 64, NKB = D / 16, NDB = D / 32;
   constexpr int BIAS = BIASX & 3;
   constexpr bool DBIAS = (BIASX & kBiasGrad) != 0;
   constexpr bool CAUSAL = MK == kMaskCausal;
+  constexpr bool SOFTMAX = ACT == kSoftmax;
   constexpr int kLoadsPerTile = 8;  // dma16 instructions per wave per K / V tile (4 rows x 4, twice)
   __shared__ FusedSmem sm;
 
@@ -1380,19 +1382,22 @@ void bwd_fused_kernel(BwdArgs a) {
   const int qs = w.qs, Lq = w.Lq, ks = w.ks, Lkv = w.Lkv;
   const int H = a.H, rs = H * D;
   const float inv_scale = 1.0f / a.scale;
-  const float smul = a.scale * kLog2e;
+  const float smul = SOFTMAX ? a.scale * kLog2e : a.scale;
   const float bias_c = (BIAS == kBiasScalar) ? a.bias[h] : 0.0f;
-  const float lse_shift = (BIAS == kBiasScalar) ? bias_c : 0.0f;
+  const float lse_shift = (SOFTMAX && BIAS == kBiasScalar) ? bias_c : 0.0f;
+  // GDPA: a per-head scalar bias enters the scores (in units of the unscaled score)
+  const float acc0 = (!SOFTMAX && BIAS == kBiasScalar) ? bias_c * inv_scale : 0.0f;
+  const float invL = Lkv > 0 ? 1.0f / (float)Lkv : 0.0f;
 
   // ---- item prologue: Q and dO tiles, statistics, bias table, first two K / V tiles
-  const __amdgpu_buffer_rsrc_t qsr = slice_rsrc(a.q + (size_t)qs * rs + h * D, Lq, rs, D);
+  const __amdgpu_buffer_rsrc_t qsr = slice_rsrc(a.q + (size_t)(a.q_shared ? 0 : qs) * rs + h * D, Lq, rs, D);
   const __amdgpu_buffer_rsrc_t gsr = slice_rsrc(a.dout + (size_t)qs * rs + h * D, Lq, rs, D);
   const __amdgpu_buffer_rsrc_t ksr = slice_rsrc(a.k + (size_t)ks * rs + h * D, Lkv, rs, D);
   const __amdgpu_buffer_rsrc_t vsr = slice_rsrc(a.v + (size_t)ks * rs + h * D, Lkv, rs, D);
   const TileLoader ld = make_loader64(wave, lane, rs);
   load_tile64(ld, qsr, 0, rs, sm.qg[0], wave);
   load_tile64(ld, gsr, 0, rs, sm.qg[1], wave);
-  if (wave == 0) {
+  if (SOFTMAX && wave == 0) {
     const __amdgpu_buffer_rsrc_t lser = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.lse) + (size_t)h * a.Tq + qs, (short)0, Lq * 4, 0x00020000);
     dma4(lser, (uint32_t)lane * 4u, sm.lse2);
@@ -1408,8 +1413,8 @@ void bwd_fused_kernel(BwdArgs a) {
   };
   if (k0 < k1) issue(k0, 0);
   if (k0 + 1 < k1) issue(k0 + 1, 1);
-  // Delta_i = <dO_i, O_i>: four threads per row, 32 dimensions each.
-  {
+  // Delta_i = <dO_i, O_i> (softmax): four threads per row, 32 dimensions each.
+  if (SOFTMAX) {
     const int row = tid >> 2, part = tid & 3;
     float acc = 0.0f;
     if (row < Lq) {
@@ -1437,7 +1442,7 @@ void bwd_fused_kernel(BwdArgs a) {
   }
   if (DBIAS && isB) sm.dbh[half][lane] = 0ull;
   wait_vm();
-  if (wave == 0) {
+  if (SOFTMAX && wave == 0) {
     const float x = sm.lse2[lane];
     sm.lse2[lane] = (lane < Lq && x != kNegInf) ? -(x - lse_shift) * kLog2e : kNegInf;
   }
@@ -1452,8 +1457,10 @@ void bwd_fused_kernel(BwdArgs a) {
   dqa[1] = f32x16{};
 
   f32x16 acc[NDB];  // A: dV, B: dK of the current tile (dK unscaled)
-  auto tile = [&](const int kt, auto st_tag) {
+  // NQB: 32-row query blocks with rows (the second only when the sequence has more than 32 queries)
+  auto tile = [&](const int kt, auto st_tag, auto nqb_tag) {
     constexpr int ST = decltype(st_tag)::value;
+    constexpr bool qb1 = decltype(nqb_tag)::value == 2;
     // Outstanding at this point: tile kt's loads, then tile kt + 1's (and the previous tile's
     // stores). Loads complete in order, so with at most kLoadsPerTile operations left tile kt has
     // landed (tile kt + 1 may still be in flight).
@@ -1484,6 +1491,7 @@ void bwd_fused_kernel(BwdArgs a) {
       const bool need_mask = (key_w + 32 > Lkv) || (CAUSAL && key_w + 31 > 0);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
+        if (qb == 1 && !qb1) break;
         f32x16 sacc;
         if (BIAS == kBiasBucket) {
 #pragma unroll
@@ -1493,7 +1501,8 @@ void bwd_fused_kernel(BwdArgs a) {
             for (int j = 0; j < 8; ++j) sacc[8 * c + j] = dvp[j];
           }
         } else {
-          sacc = f32x16{};
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[r] = acc0;
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -1501,26 +1510,40 @@ void bwd_fused_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const int rbase = 32 * qb + 16 * c + 8 * hh;
-          const float4 x0 = *reinterpret_cast<const float4*>(&sm.lse2[rbase]);
-          const float4 x1 = *reinterpret_cast<const float4*>(&sm.lse2[rbase + 4]);
-          const float l8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          float pv[8];
+          float pv[8], gv[8];
+          if (SOFTMAX) {
+            const float4 x0 = *reinterpret_cast<const float4*>(&sm.lse2[rbase]);
+            const float4 x1 = *reinterpret_cast<const float4*>(&sm.lse2[rbase + 4]);
+            const float l8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(__builtin_fmaf(sacc[8 * c + j], smul, l8[j]));
-          if (need_mask) {
+            for (int j = 0; j < 8; ++j) pv[j] = fast_exp2(__builtin_fmaf(sacc[8 * c + j], smul, l8[j]));
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              float f, g;
+              act_fwd_grad<ACT>(sacc[8 * c + j] * smul, f, g);
+              pv[j] = f * invL;
+              gv[j] = g * invL;
+            }
+          }
+          if (need_mask || !SOFTMAX) {
+            // (softmax rows past the sequence's end already have P = 0 from their -inf statistic)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const int qi = rbase + j;
-              pv[j] = (kj >= Lkv || (CAUSAL && kj > qi)) ? 0.0f : pv[j];
+              const bool masked = kj >= Lkv || (CAUSAL && kj > qi) || (!SOFTMAX && qi >= Lq);
+              pv[j] = masked ? 0.0f : pv[j];
+              if (!SOFTMAX) gv[j] = masked ? 0.0f : gv[j];
             }
           }
           pk[qb][c] = pack8(pv);
-          sm.xch[half][qb][c][lane] = __builtin_bit_cast(uint4, pk[qb][c]);
+          sm.xch[half][qb][c][lane] = SOFTMAX ? __builtin_bit_cast(uint4, pk[qb][c]) : __builtin_bit_cast(uint4, pack8(gv));
         }
       }
     } else {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
+        if (qb == 1 && !qb1) break;
         pacc[qb] = f32x16{};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -1532,6 +1555,7 @@ void bwd_fused_kernel(BwdArgs a) {
       // dV^T += dO^T P
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        if (s == 2 && !qb1) break;
         const uint32_t base = (uint32_t)(16 * s * kRowBytes);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -1543,15 +1567,21 @@ void bwd_fused_kernel(BwdArgs a) {
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
+          if (qb == 1 && !qb1) break;
           const int rbase = 32 * qb + 16 * c + 8 * hh;
-          float pv[8];
-          unpack8(sm.xch[half][qb][c][lane], pv);
-          const float4 y0 = *reinterpret_cast<const float4*>(&sm.dlt[rbase]);
-          const float4 y1 = *reinterpret_cast<const float4*>(&sm.dlt[rbase + 4]);
-          const float d8[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+          float hv[8];  // softmax: P; GDPA: act'(S) / Lkv
+          unpack8(sm.xch[half][qb][c][lane], hv);
           float dsv[8];
+          if (SOFTMAX) {
+            const float4 y0 = *reinterpret_cast<const float4*>(&sm.dlt[rbase]);
+            const float4 y1 = *reinterpret_cast<const float4*>(&sm.dlt[rbase + 4]);
+            const float d8[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
 #pragma unroll
-          for (int j = 0; j < 8; ++j) dsv[j] = pv[j] * (pacc[qb][8 * c + j] - d8[j]);
+            for (int j = 0; j < 8; ++j) dsv[j] = hv[j] * (pacc[qb][8 * c + j] - d8[j]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dsv[j] = pacc[qb][8 * c + j] * hv[j];
+          }
           pk[qb][c] = pack8(dsv);
           // dS^T row (this lane's key), logical chunk rbase / 8 of the query columns
           const int r = 32 * half + l32;
@@ -1562,6 +1592,7 @@ void bwd_fused_kernel(BwdArgs a) {
       // dK^T += Q^T dS
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        if (s == 2 && !qb1) break;
         const uint32_t base = (uint32_t)(16 * s * kRowBytes);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -1576,9 +1607,11 @@ void bwd_fused_kernel(BwdArgs a) {
       const uint32_t base = (uint32_t)(16 * s * kRowBytes);
       const bf16x8 kop = lds_read_tr(Kt, base + (T[0] ^ (uint32_t)(64 * wave)), base + (T[1] ^ (uint32_t)(64 * wave)));
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb) {
+        if (qb == 1 && !qb1) break;
         dqa[qb] = mfma32(kop, lds_read_tr(sm.dst, base + (T[0] ^ (uint32_t)(64 * qb)), base + (T[1] ^ (uint32_t)(64 * qb))),
                          dqa[qb]);
+      }
     }
     // The tile's dV (A) or dK (B) is complete: store it. bf16 rows go out through LDS as whole
     // rows (a lane's accumulators hold 4-element pieces of its key's row): once every wave is done
@@ -1600,11 +1633,17 @@ void bwd_fused_kernel(BwdArgs a) {
                  acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc, 1);
     }
   };
-  for (int kt = k0; kt < k1; kt += 3) {
-    tile(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < k1) tile(kt + 1, std::integral_constant<int, 1>{});
-    if (kt + 2 < k1) tile(kt + 2, std::integral_constant<int, 2>{});
-  }
+  auto loop = [&](auto nqb_tag) {
+    for (int kt = k0; kt < k1; kt += 3) {
+      tile(kt, std::integral_constant<int, 0>{}, nqb_tag);
+      if (kt + 1 < k1) tile(kt + 1, std::integral_constant<int, 1>{}, nqb_tag);
+      if (kt + 2 < k1) tile(kt + 2, std::integral_constant<int, 2>{}, nqb_tag);
+    }
+  };
+  if (Lq > 32)
+    loop(std::integral_constant<int, 2>{});
+  else
+    loop(std::integral_constant<int, 1>{});
 
   if (DBIAS && isB) {
     dbl.flush(sm.dbh[half]);
@@ -1643,6 +1682,44 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_dq_kernel(BwdArgs a) {
   reduce_dq_group<D, 256>(load_group(a.dq_groups, blockIdx.x), a.part_dq, a.dq, a.H, a.scale, a.grad_f32,
                           threadIdx.x);
+}
+
+// The same sums for groups with many pieces (shared queries: one piece per sequence): one workgroup
+// per (group, row); lane group k of the workgroup adds pieces k, k + NL, k + 2 NL, ... of 4-column
+// slices, and the NL lane groups' sums are added in a fixed tree order, so the result does not
+// depend on scheduling.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce_dq_wide_kernel(BwdArgs a) {
+  constexpr int BM = kDqBM, NQ = D / 4, NL = 256 / NQ;
+  const int gi = blockIdx.x / BM, row = blockIdx.x % BM;
+  const WorkRec g = load_group(a.dq_groups, gi);
+  const int qi = g.tile * BM + row;
+  if (qi >= g.Lq) return;
+  const int slot0 = g.lo, R = g.hi;
+  const int cq = threadIdx.x % NQ, k = threadIdx.x / NQ;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 4
+  for (int r = k; r < R; r += NL) {
+    const float4 x = *reinterpret_cast<const float4*>(a.part_dq + ((size_t)(slot0 + r) * BM + row) * D + 4 * cq);
+    acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+  }
+  __shared__ float4 red[NL][NQ];
+  red[k][cq] = acc;
+  __syncthreads();
+  if (k == 0) {
+#pragma unroll
+    for (int st = 1; st < NL; st *= 2)  // pairwise tree: ((0 + 1) + (2 + 3)) + ...
+#pragma unroll
+      for (int i = 0; i < NL; i += 2 * st) {
+        red[i][cq].x += red[i + st][cq].x;
+        red[i][cq].y += red[i + st][cq].y;
+        red[i][cq].z += red[i + st][cq].z;
+        red[i][cq].w += red[i + st][cq].w;
+      }
+    const float4 t = red[0][cq];
+    const size_t base = ((size_t)(g.qs + qi) * a.H + g.h) * D + 4 * cq;
+    store4(a.dq, base, t.x * a.scale, t.y * a.scale, t.z * a.scale, t.w * a.scale, a.grad_f32);
+  }
 }
 
 template <int D>
@@ -1793,17 +1870,29 @@ hipError_t launch_bwd_fused(const BwdArgs& a, const Modes& m, int n, hipStream_t
     hipLaunchKernelGGL(kern, dim3(n), dim3(kThreads), 0, s, a);
     return hipGetLastError();
   };
-  // softmax only: a per-head scalar has a zero gradient, so only the bucket table has a gradient variant
-  const int bx = m.bias == kBiasBucket && m.dbias ? (kBiasBucket | kBiasGrad) : m.bias;
-  auto by_mask = [&](auto bias_tag) {
-    constexpr int BX = decltype(bias_tag)::value;
-    return m.causal ? go(bwd_fused_kernel<BX, kMaskCausal>) : go(bwd_fused_kernel<BX, kMaskNone>);
+  auto by_mask = [&](auto act_tag, auto bias_tag) {
+    constexpr int A = decltype(act_tag)::value, BX = decltype(bias_tag)::value;
+    return m.causal ? go(bwd_fused_kernel<A, BX, kMaskCausal>) : go(bwd_fused_kernel<A, BX, kMaskNone>);
   };
-  switch (bx) {
-    case kBiasNone: return by_mask(std::integral_constant<int, kBiasNone>{});
-    case kBiasScalar: return by_mask(std::integral_constant<int, kBiasScalar>{});
-    case kBiasBucket: return by_mask(std::integral_constant<int, kBiasBucket>{});
-    default: return by_mask(std::integral_constant<int, kBiasBucket | kBiasGrad>{});
+  auto by_bias = [&](auto act_tag) {
+    constexpr int A = decltype(act_tag)::value;
+    using I = std::integral_constant<int, 0>;
+    // under softmax a per-head scalar has a zero gradient: no gradient variant
+    const bool grad = m.dbias && !(A == kSoftmax && m.bias == kBiasScalar);
+    switch (m.bias | (grad ? kBiasGrad : 0)) {
+      case kBiasNone: return by_mask(act_tag, I{});
+      case kBiasScalar: return by_mask(act_tag, std::integral_constant<int, kBiasScalar>{});
+      case kBiasBucket: return by_mask(act_tag, std::integral_constant<int, kBiasBucket>{});
+      case kBiasScalar | kBiasGrad:
+        if constexpr (A != kSoftmax) return by_mask(act_tag, std::integral_constant<int, kBiasScalar | kBiasGrad>{});
+        return by_mask(act_tag, std::integral_constant<int, kBiasScalar>{});
+      default: return by_mask(act_tag, std::integral_constant<int, kBiasBucket | kBiasGrad>{});
+    }
+  };
+  switch (m.act) {
+    case kSoftmax: return by_bias(std::integral_constant<int, kSoftmax>{});
+    case kSilu: return by_bias(std::integral_constant<int, kSilu>{});
+    default: return by_bias(std::integral_constant<int, kGeluTanh>{});
   }
 }
 
@@ -1826,6 +1915,15 @@ hipError_t launch_bwd_reduce_dq(const BwdArgs& a, const Modes& m, int n, hipStre
     hipLaunchKernelGGL(bwd_reduce_dq_kernel<64>, dim3(n), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(bwd_reduce_dq_kernel<128>, dim3(n), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce_dq_wide(const BwdArgs& a, const Modes& m, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (m.D == 64)
+    hipLaunchKernelGGL(bwd_reduce_dq_wide_kernel<64>, dim3(n * kDqBM), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_reduce_dq_wide_kernel<128>, dim3(n * kDqBM), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -410,8 +410,7 @@ struct jfa_plan_s {
   int out_f32 = 0, grad_f32 = 0;
   int q_shared = 0;  // JFA_PLAN_SHARED_Q
   // Backward as one fused pass over the dQ items (every sequence has at most kKvBM queries, D = 128,
-  // softmax, no band limits, no shared queries, and every sequence with keys has queries, so that
-  // the dQ items cover every key)
+  // no band limits, and every sequence with keys has queries, so that the dQ items cover every key)
   int fused_bwd = 0;
   int mx = 0;        // JFA_PLAN_MXFP8
   int n_vtiles = 0;  // MXFP8: 64-key tiles over all sequences (transposed quantised V)
@@ -683,7 +682,10 @@ jfa_status run_backward(jfa_plan_s* P, const void* q, const void* k, const void*
     st = timed(P, 8, s, [&] { return launch_bwd_fused(a, m, (int)P->lists[kDq].n_items(), s); }, "fused backward launch");
     if (st != JFA_OK) return st;
     if (P->lists[kDq].n_groups() > 0) {
-      st = timed(P, 5, s, [&] { return launch_bwd_reduce_dq(a, m, (int)P->lists[kDq].n_groups(), s); }, "dQ reduce launch");
+      // shared queries: one piece per sequence in every group, summed by many workgroups per group
+      const int ng = (int)P->lists[kDq].n_groups();
+      st = timed(P, 5, s, [&] { return P->q_shared ? launch_bwd_reduce_dq_wide(a, m, ng, s) : launch_bwd_reduce_dq(a, m, ng, s); },
+                 "dQ reduce launch");
       if (st != JFA_OK) return st;
     }
     if (dbias) st = timed(P, 6, s, [&] { return launch_bwd_dbias_finish(a, m, s); }, "bias-gradient finish launch");
@@ -826,10 +828,10 @@ jfa_status jfa_plan(const jfa_problem* problem, jfa_stream_t stream, jfa_plan_t*
   }
   P->q_shared = (p.flags & JFA_PLAN_SHARED_Q) ? 1 : 0;
   if (P->q_shared) share_query_slots(P->lists[kDq]);
-  if (P->modes.kv_short && !P->modes.band && !P->q_shared) {
-    bool covered = true;
-    for (int b = 0; b < P->B; ++b) covered = covered && (lq[b] > 0 || lkv[b] == 0);
-    P->fused_bwd = covered ? 1 : 0;
+  if (P->D == 128 && !P->modes.band) {
+    bool fits = true;
+    for (int b = 0; b < P->B; ++b) fits = fits && lq[b] <= kKvBM && (lq[b] > 0 || lkv[b] == 0);
+    P->fused_bwd = fits ? 1 : 0;
   }
   for (auto& L : P->lists) L.order = dispatch_order(L, P->B, P->H);
 

@@ -136,8 +136,10 @@ hipError_t launch_forward_combine(const FwdArgs& a, const Modes& m, int n_groups
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const Modes& m, int n_items, int resident, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, const Modes& m, int n_items, hipStream_t s);
 hipError_t launch_bwd_reduce_dq(const BwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
-// Fused backward of plans whose sequences all have at most kKvBM queries (D = 128, softmax, no band
-// limits): one workgroup per dQ item computes dQ (or its partial) and the dK / dV of the item's keys.
+// The same fixed-order sums spread over one workgroup per (group, row), for groups of many pieces.
+hipError_t launch_bwd_reduce_dq_wide(const BwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
+// Fused backward of plans whose sequences all have at most kKvBM queries (D = 128, no band limits):
+// one workgroup per dQ item computes dQ (or its partial) and the dK / dV of the item's keys.
 hipError_t launch_bwd_fused(const BwdArgs& a, const Modes& m, int n_items, hipStream_t s);
 hipError_t launch_bwd_reduce_dkdv(const BwdArgs& a, const Modes& m, int n_groups, hipStream_t s);
 // Clears the bias-gradient totals (when a.dbias_acc is set) and the dK/dV queue counters.

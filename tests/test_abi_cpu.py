@@ -144,18 +144,19 @@ def test_short_query_problems_use_half_width_key_items():
 
 def test_fused_backward_eligibility():
     """The backward runs as one fused pass over the dQ items exactly when those items cover every
-    key: short query sets (softmax, D = 128), no window or block limit, no shared queries, and no
-    sequence that has keys but no queries."""
+    key: short query sets (D = 128, any activation, shared queries too), no window or block limit,
+    and no sequence that has keys but no queries."""
     fused = lambda *a, **kw: _host_plan(*a, **kw).info()["fused_bwd"]
     assert fused([1, 64, 30], [500, 64, 7], 2, 128, mask="none") == 1
     assert fused([1, 64, 30], [1, 64, 30], 2, 128, mask="causal") == 1
     assert fused([1, 0, 30], [500, 0, 7], 2, 128, mask="none") == 1      # empty sequence
     assert fused([1, 0, 30], [500, 64, 7], 2, 128, mask="none") == 0     # keys without queries
     assert fused([1, 64, 30], [500, 64, 7], 2, 128, mask="none", window=16) == 0
-    assert fused([1, 64, 30], [500, 64, 7], 2, 128, mask="none", act="silu") == 0
+    assert fused([1, 64, 30], [500, 64, 7], 2, 128, mask="none", act="silu") == 1
     assert fused([1, 65, 30], [500, 65, 7], 2, 128, mask="none") == 0
     assert fused([1, 64, 30], [500, 64, 7], 2, 64, mask="none") == 0
-    assert fused([32, 32, 32], [500, 64, 7], 2, 128, mask="none", shared_q=True) == 0
+    assert fused([32, 32, 32], [500, 64, 7], 2, 128, mask="none", shared_q=True) == 1
+    assert fused([65, 65, 65], [500, 64, 7], 2, 128, mask="none", shared_q=True) == 0
     w = ji.WORKLOADS["target_attn"]
     lq, lkv = ji.lengths(w)
     assert fused(lq, lkv, w.H, w.D, mask=w.mask, act=w.act, bias=w.bias) == 1

@@ -30,6 +30,8 @@ def test_shared_queries(D, act, bias, Ls):
     say(f"case shared queries Ls={Ls} D={D} act={act} bias={bias}")
     gpu = run_gpu(x)
     assert gpu["dq"].shape == (Ls, 2, D)
+    # at most 64 shared rows (D = 128): the fused backward, its dQ pieces summed over sequences
+    assert gpu["plan"].info()["fused_bwd"] == (1 if (D == 128 and Ls <= 64) else 0)
     rep = compare(x, gpu, oracle(x))
     say(f"  {rep}")
 

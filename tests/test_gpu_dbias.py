@@ -110,13 +110,15 @@ def test_dbias_full_causal_bucket_workload():
     say(f"  dbias rel-L2 {err:.2e}")
 
 
+@pytest.mark.parametrize("act", ["softmax", "silu"])
 @pytest.mark.parametrize("bias", ["scalar", "bucket"])
 @pytest.mark.parametrize("mask", ["none", "causal"])
-def test_dbias_short_query_items(mask, bias):
-    """Softmax problems whose sequences all have at most 64 queries use the half-width dK/dV items."""
+def test_dbias_short_query_items(mask, bias, act):
+    """Problems whose sequences all have at most 64 queries run the fused backward, which also
+    accumulates the bias gradient."""
     lq, lkv = ([1, 37, 64, 50], [1, 37, 64, 50]) if mask == "causal" else ([1, 37, 64, 5], [300, 64, 129, 1000])
-    x = ji.make_inputs(lq, lkv, 2, 128, wid=47, mask=mask, act="softmax", bias_kind=bias, bias_sigma=0.5)
-    say(f"case dbias short-query mask={mask} bias={bias}")
+    x = ji.make_inputs(lq, lkv, 2, 128, wid=47, mask=mask, act=act, bias_kind=bias, bias_sigma=0.5)
+    say(f"case dbias short-query mask={mask} bias={bias} act={act}")
     gpu = run_gpu(x, dbias=True)
-    assert gpu["plan"].info()["kv_bn"] == 64
+    assert gpu["plan"].info()["fused_bwd"] == 1
     check_dbias(x, to_np(gpu["dbias"]), oracle(x)["dbias"])

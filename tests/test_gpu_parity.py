@@ -146,15 +146,17 @@ SHORT_KV = [300, 64, 129, 1000]
 SHORT_SELF = [1, 37, 64, 50]
 
 
+@pytest.mark.parametrize("act", ["softmax", "silu", "gelu_tanh"])
 @pytest.mark.parametrize("mask", ["none", "causal"])
 @pytest.mark.parametrize("bias", ["none", "scalar", "bucket"])
-def test_short_query_items(mask, bias):
+def test_short_query_items(mask, bias, act):
+    """Every sequence with at most 64 queries: the backward is one fused pass over the dQ items."""
     lq, lkv = (SHORT_SELF, SHORT_SELF) if mask == "causal" else (SHORT_Q, SHORT_KV)
-    x = ji.make_inputs(lq, lkv, 2, 128, wid=45, mask=mask, act="softmax", bias_kind=bias, bias_sigma=0.5)
-    say(f"case short-query mask={mask} bias={bias}")
+    x = ji.make_inputs(lq, lkv, 2, 128, wid=45, mask=mask, act=act, bias_kind=bias, bias_sigma=0.5)
+    say(f"case short-query mask={mask} bias={bias} act={act}")
     gpu = run_gpu(x)
     info = gpu["plan"].info()
-    assert info["kv_bn"] == 64 and info["fused_bwd"] == 1
+    assert info["fused_bwd"] == 1 and info["kv_bn"] == (64 if act == "softmax" else 128)
     compare(x, gpu, oracle(x))
 
 

@@ -23,6 +23,7 @@ hipError_t launch_forward_combine(const FwdArgs&, const Modes&, int, hipStream_t
 hipError_t launch_bwd_dkdv(const BwdArgs&, const Modes&, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_bwd_dq(const BwdArgs&, const Modes&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_bwd_reduce_dq(const BwdArgs&, const Modes&, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_bwd_reduce_dq_wide(const BwdArgs&, const Modes&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_bwd_fused(const BwdArgs&, const Modes&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_bwd_reduce_dkdv(const BwdArgs&, const Modes&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_bwd_dbias_clear(const BwdArgs&, const Modes&, hipStream_t) { return hipErrorNotSupported; }
