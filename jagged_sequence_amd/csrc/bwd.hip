@@ -903,8 +903,9 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
 
   // Statistics of a query tile (softmax): lse and Delta of its 64 rows come into the tile's stage
   // with the tile itself (one 256-byte load each, by wave 0). After the wait that precedes the
-  // tile's publishing barrier, wave 0 turns lse into -lse in log2 units in place; rows past the end
-  // read zeros and get -inf, which makes their P 0.
+  // tile's publishing barrier, wave 0 turns lse into -lse in log2 units in place (rows past the end
+  // read zeros and get -inf, which makes their P 0) and Delta into -Delta, the initial value of the
+  // B waves' dP accumulators, so that dP - Delta comes out of the products.
   const __amdgpu_buffer_rsrc_t lser =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.lse) + (size_t)h * a.Tq + qs, (short)0, Lq * 4, 0x00020000);
   const __amdgpu_buffer_rsrc_t dltr =
@@ -914,6 +915,7 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
       const int r = lane_now();
       const float x = sm.lse2[stg][r];
       sm.lse2[stg][r] = (qt * BM + r < Lq && x != kNegInf) ? -(x - lse_shift) * kLog2e : kNegInf;
+      sm.dlt[stg][r] = -sm.dlt[stg][r];
     }
   };
   auto issue_tile = [&](int qt, int stg) {
@@ -1024,7 +1026,20 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
     } else {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        pacc[qb] = f32x16{};
+        if (SOFTMAX) {
+          // -Delta of the accumulator's rows (register 8 c + j: row 32 qb + 16 c + 8 hh + j)
+#pragma unroll
+          for (int c8 = 0; c8 < 2; ++c8) {
+            const float* dl = &sm.dlt[ST][32 * qb + 16 * c8 + 8 * hh];
+            const float4 y0 = *reinterpret_cast<const float4*>(dl);
+            const float4 y1 = *reinterpret_cast<const float4*>(dl + 4);
+            pacc[qb][8 * c8 + 0] = y0.x; pacc[qb][8 * c8 + 1] = y0.y; pacc[qb][8 * c8 + 2] = y0.z;
+            pacc[qb][8 * c8 + 3] = y0.w; pacc[qb][8 * c8 + 4] = y1.x; pacc[qb][8 * c8 + 5] = y1.y;
+            pacc[qb][8 * c8 + 6] = y1.z; pacc[qb][8 * c8 + 7] = y1.w;
+          }
+        } else {
+          pacc[qb] = f32x16{};
+        }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
           pacc[qb] = mfma32(lds_read16(Gt, (raddr ^ (uint32_t)(kb << 5)) + qb * 32 * kRowBytes), frag[kb], pacc[qb]);
@@ -1061,13 +1076,8 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
           if (SOFTMAX) {
             float pv[8];
             unpack8(sm.xch[XB][pair][0][qb][c8][lane], pv);
-            const int rbase = 32 * qb + 16 * c8 + 8 * hh;
-            const float* dl = sm.dlt[ST];
-            const float4 y0 = *reinterpret_cast<const float4*>(&dl[rbase]);
-            const float4 y1 = *reinterpret_cast<const float4*>(&dl[rbase + 4]);
-            const float d8[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
 #pragma unroll
-            for (int j = 0; j < 8; ++j) dsv[j] = pv[j] * (pacc[qb][8 * c8 + j] - d8[j]);
+            for (int j = 0; j < 8; ++j) dsv[j] = pv[j] * pacc[qb][8 * c8 + j];  // pacc = dP - Delta
           } else {
             float gv[8];
             unpack8(sm.xch[XB][pair][Smem::NPG - 1][qb][c8][lane], gv);

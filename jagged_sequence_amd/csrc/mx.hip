@@ -48,39 +48,41 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 // ---------------------------------------------------------------- quantisation
-// Q or K: one thread per block of 32 consecutive bf16 values (32 features of one row and head).
+// Q or K: four lanes per block of 32 consecutive bf16 values (32 features of one row and head),
+// eight values each, so that a wave reads 1 KB and writes 512 bytes contiguously; the block's
+// largest magnitude is exchanged among the four lanes.
 __global__ __launch_bounds__(256) void mx_quantize_rows_kernel(const uint16_t* x, uint8_t* xq, uint8_t* xs,
                                                                long long n_blocks) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n_blocks) return;
-  const uint4* src = reinterpret_cast<const uint4*>(x + i * 32);
-  uint4 w[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) w[c] = src[c];
-  float v[32];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint32_t u[4] = {w[c].x, w[c].y, w[c].z, w[c].w};
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long i = t >> 2;  // block
+  const int part = (int)(t & 3);
+  const bool valid = i < n_blocks;
+  float v[8];
+  if (valid) {
+    const uint4 w = *reinterpret_cast<const uint4*>(x + t * 8);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[8 * c + 2 * j] = bf16_lo(u[j]);
-      v[8 * c + 2 * j + 1] = bf16_hi(u[j]);
+      v[2 * j] = bf16_lo(u[j]);
+      v[2 * j + 1] = bf16_hi(u[j]);
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.0f;
   }
   float amax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  if (!valid) return;
   int byte;
   float inv;
   mx_scale(amax, byte, inv);
-  uint32_t o[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    o[j] = pack4_fp8(sat448(v[4 * j] * inv), sat448(v[4 * j + 1] * inv), sat448(v[4 * j + 2] * inv), sat448(v[4 * j + 3] * inv));
-  uint4* dst = reinterpret_cast<uint4*>(xq + i * 32);
-  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  xs[i] = (uint8_t)byte;
+  const uint32_t o0 = pack4_fp8(sat448(v[0] * inv), sat448(v[1] * inv), sat448(v[2] * inv), sat448(v[3] * inv));
+  const uint32_t o1 = pack4_fp8(sat448(v[4] * inv), sat448(v[5] * inv), sat448(v[6] * inv), sat448(v[7] * inv));
+  *reinterpret_cast<uint2*>(xq + t * 8) = make_uint2(o0, o1);
+  if (part == 0) xs[i] = (uint8_t)byte;
 }
 
 // V: one workgroup per (64-key tile of a sequence, head); thread (d, g) quantises keys
@@ -403,11 +405,12 @@ hipError_t mx_launch_b(const MxArgs& a, const Modes& m, int n, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_mx_quantize(const MxArgs& a, int Tq, int Tkv, int n_vtiles, hipStream_t s) {
+  // four blocks of 32 features per row and head, four lanes per block
   const long long nq = (long long)Tq * a.f.H * 4, nk = (long long)Tkv * a.f.H * 4;
   if (nq > 0)
-    hipLaunchKernelGGL(mx_quantize_rows_kernel, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, a.f.q, a.qq, a.qs, nq);
+    hipLaunchKernelGGL(mx_quantize_rows_kernel, dim3((unsigned)((4 * nq + 255) / 256)), dim3(256), 0, s, a.f.q, a.qq, a.qs, nq);
   if (nk > 0)
-    hipLaunchKernelGGL(mx_quantize_rows_kernel, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, s, a.f.k, a.kq, a.ks, nk);
+    hipLaunchKernelGGL(mx_quantize_rows_kernel, dim3((unsigned)((4 * nk + 255) / 256)), dim3(256), 0, s, a.f.k, a.kq, a.ks, nk);
   if (n_vtiles > 0)
     hipLaunchKernelGGL(mx_quantize_v_kernel, dim3(n_vtiles, a.f.H), dim3(256), 0, s, a.f.v, a.vtiles, a.f.H, a.vq, a.vs);
   return hipGetLastError();
