@@ -451,7 +451,7 @@ void bwd_dq_kernel2(BwdArgs a) {
         } else {
           float f, g;
           act_fwd_grad<ACT>(sacc[sb][r] * smul, f, g);
-          d = pacc[sb][r] * g * invL;
+          d = pacc[sb][r] * g;  // (the 1 / Lkv of the GDPA gradient is applied to dQ at the end)
         }
         ds[sb][r] = d;
       }
@@ -482,18 +482,19 @@ void bwd_dq_kernel2(BwdArgs a) {
     if (kt + 1 < k1) tile(kt + 1, std::integral_constant<int, 1>{});
   }
 
+  const float gscale = SOFTMAX ? 1.0f : invL;  // GDPA: the accumulators lack the factor 1 / Lkv of dS
   if (slot < 0 && !a.grad_f32) {
     // bf16 rows through the ring stage that the last tile did not use (every wave finished reading
     // it before the last tile's barrier, and no load went into it since): 8 KB per wave.
     const int free_st = ((k1 - 1 - k0) & 1) ^ 1;
     char* dst = static_cast<char*>(a.dq);
     const int H = a.H;
-    store_rows_staged(&sm.kv[free_st][0][0] + wave * (32 * kRowBytes), qacc, a.scale, lane, Lq - row0,
+    store_rows_staged(&sm.kv[free_st][0][0] + wave * (32 * kRowBytes), qacc, a.scale * gscale, lane, Lq - row0,
                       [&](int r) { return dst + (((size_t)(qs + row0 + r) * H + h) * D) * 2; });
   } else if (slot < 0) {
     if (qi < Lq) {
       const size_t base = ((size_t)(qs + qi) * a.H + h) * D;
-      const float sc = a.scale;
+      const float sc = a.scale * gscale;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -508,7 +509,8 @@ void bwd_dq_kernel2(BwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<float4*>(po + 32 * db + 8 * g + 4 * hh) =
-            make_float4(qacc[db][4 * g], qacc[db][4 * g + 1], qacc[db][4 * g + 2], qacc[db][4 * g + 3]);
+            make_float4(qacc[db][4 * g] * gscale, qacc[db][4 * g + 1] * gscale, qacc[db][4 * g + 2] * gscale,
+                        qacc[db][4 * g + 3] * gscale);
   }
 }
 
@@ -997,8 +999,8 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
               for (int j = 0; j < 8; ++j) {
                 float f, g;
                 act_fwd_grad<ACT>(sacc[8 * c8 + j] * smul, f, g);
-                pv[j] = f * invL;
-                gv[j] = g * invL;
+                pv[j] = f;  // (the 1 / Lkv of GDPA is applied to dV and dK at the end)
+                gv[j] = g;
               }
             }
             if (MASK || !SOFTMAX) {
@@ -1085,7 +1087,12 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
             for (int j = 0; j < 8; ++j) dsv[j] = pacc[qb][8 * c8 + j] * gv[j];
           }
           dsb[c8] = pack8(dsv);
-          if (DBIAS) dbl.add_run<BIAS == kBiasBucket>(sm.dbh[pair], qrow0 + 32 * qb + 16 * c8 + 8 * hh - kj, dsv);
+          if (DBIAS) {
+            if (!SOFTMAX)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) dsv[j] *= invL;
+            dbl.add_run<BIAS == kBiasBucket>(sm.dbh[pair], qrow0 + 32 * qb + 16 * c8 + 8 * hh - kj, dsv);
+          }
         }
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -1177,8 +1184,10 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
     }
   }
 
-  // Accumulator register r of d-block db: dimension 32 db + 8 (r/4) + 4 hh + r%4, key kj.
-  const float sc = isB ? a.scale : 1.0f;
+  // Accumulator register r of d-block db: dimension 32 db + 8 (r/4) + 4 hh + r%4, key kj. GDPA: the
+  // accumulators lack the factor 1 / Lkv of P and dS.
+  const float gscale = SOFTMAX ? 1.0f : (Lkv > 0 ? 1.0f / (float)Lkv : 0.0f);
+  const float sc = (isB ? a.scale : 1.0f) * gscale;
   if (slot < 0 && !a.grad_f32) {
     // bf16 rows go out through LDS as whole rows. Once every wave is past the last tile the Q / dO
     // ring is free: 8 KB per wave.
@@ -1205,7 +1214,8 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<float4*>(pp + 32 * db + 8 * g + 4 * hhe) =
-            make_float4(acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]);
+            make_float4(acc[db][4 * g] * gscale, acc[db][4 * g + 1] * gscale, acc[db][4 * g + 2] * gscale,
+                        acc[db][4 * g + 3] * gscale);
   }
   take_next(token);
 }
@@ -1532,8 +1542,8 @@ void bwd_fused_kernel(BwdArgs a) {
             for (int j = 0; j < 8; ++j) {
               float f, g;
               act_fwd_grad<ACT>(sacc[8 * c + j] * smul, f, g);
-              pv[j] = f * invL;
-              gv[j] = g * invL;
+              pv[j] = f;  // (the 1 / Lkv of GDPA is applied to dV, dK and dQ at the end)
+              gv[j] = g;
             }
           }
           if (need_mask || !SOFTMAX) {
@@ -1597,7 +1607,12 @@ void bwd_fused_kernel(BwdArgs a) {
           const int r = 32 * half + l32;
           *reinterpret_cast<uint4*>(&sm.dst[r * kRowBytes + (((rbase >> 3) ^ swz(r)) << 4)]) =
               __builtin_bit_cast(uint4, pk[qb][c]);
-          if (DBIAS) dbl.add_run<BIAS == kBiasBucket>(sm.dbh[half], rbase - kj, dsv);
+          if (DBIAS) {
+            if (!SOFTMAX)
+#pragma unroll
+              for (int j = 0; j < 8; ++j) dsv[j] *= invL;
+            dbl.add_run<BIAS == kBiasBucket>(sm.dbh[half], rbase - kj, dsv);
+          }
         }
       // dK^T += Q^T dS
 #pragma unroll
@@ -1628,7 +1643,7 @@ void bwd_fused_kernel(BwdArgs a) {
     // with this stage, its K and V tiles (32 KB) give each wave 8 KB; the stage is reloaded only
     // after the next tile's first barrier.
     void* dstp = isB ? a.dk : a.dv;
-    const float sc = isB ? a.scale : 1.0f;
+    const float sc = (isB ? a.scale : 1.0f) * (SOFTMAX ? 1.0f : invL);
     if (!a.grad_f32) {
       __syncthreads();
       store_rows_staged(sm.kv[ST][0] + wave * (32 * kRowBytes), acc, sc, lane, Lkv - key_w,
@@ -1670,18 +1685,20 @@ void bwd_fused_kernel(BwdArgs a) {
   for (int qb = 0; qb < 2; ++qb) {
     const int qi = 32 * qb + l32;
     if (qi >= Lq) continue;
+    const float gs = SOFTMAX ? 1.0f : invL;  // GDPA: dS lacks its factor 1 / Lkv
     if (slot < 0) {
       const size_t base = ((size_t)(qs + qi) * H + h) * D + 32 * wave;
+      const float sc = a.scale * gs;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        store4(a.dq, base + 8 * g + 4 * hh, dqa[qb][4 * g] * a.scale, dqa[qb][4 * g + 1] * a.scale,
-               dqa[qb][4 * g + 2] * a.scale, dqa[qb][4 * g + 3] * a.scale, a.grad_f32);
+        store4(a.dq, base + 8 * g + 4 * hh, dqa[qb][4 * g] * sc, dqa[qb][4 * g + 1] * sc, dqa[qb][4 * g + 2] * sc,
+               dqa[qb][4 * g + 3] * sc, a.grad_f32);
     } else {
       float* pp = a.part_dq + ((size_t)slot * kDqBM + qi) * D + 32 * wave;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         *reinterpret_cast<float4*>(pp + 8 * g + 4 * hh) =
-            make_float4(dqa[qb][4 * g], dqa[qb][4 * g + 1], dqa[qb][4 * g + 2], dqa[qb][4 * g + 3]);
+            make_float4(dqa[qb][4 * g] * gs, dqa[qb][4 * g + 1] * gs, dqa[qb][4 * g + 2] * gs, dqa[qb][4 * g + 3] * gs);
     }
   }
 }
