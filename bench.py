@@ -10,7 +10,9 @@ process) and ``plan_ms_steady`` (a plan for a reordered batch built while a step
 training loop would build the next batch's plan).
 
 ``value`` is useful FLOPs per step over the wall time of the K timed steps (bracketed by device
-synchronisations); ``median_step_ms`` is the median of the per-step HIP-event times.
+synchronisations); ``median_step_ms`` is the median of the per-step HIP-event times. The timed
+steps carry the library's per-launch timing events (the per-kernel times come from them);
+``no_kernel_events`` repeats the K steps without them.
 
 Useful FLOPs per visible (query, key) pair and head: 4 D forward + 10 D backward. Inputs are the
 seeded synthetic workload from ``jfa_inputs``, resident in HBM before timing starts.
@@ -354,6 +356,17 @@ def main() -> int:
             kernels[name] = {"avg_ms": ms / n, "launches_per_step": n / args.steps, "total_ms": ms}
     plan.timing_enable(False)
 
+    # The same number of steps without the per-launch timing events (outside the timed region), as a
+    # caller that does not time kernels runs them.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    no_events_ms = e0.elapsed_time(e1) / args.steps
+
     # Cold-cache rung of the metric ladder (outside the timed region): the same step after 512 MiB
     # have been written over the caches (twice the 256 MB last-level cache), so that every input
     # comes from HBM.
@@ -431,6 +444,9 @@ def main() -> int:
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "median_step_ms": round(median_ms, 4),
         "value_at_median_step": round((fw + bw) / (median_ms * 1e-3) / 1e12, 2),
+        "no_kernel_events": {"ms_per_step": round(no_events_ms, 4),
+                             "value": round((fw + bw) / (no_events_ms * 1e-3) / 1e12, 2),
+                             "note": "the same steps without the library's per-launch timing events"},
         "cold_cache": {"median_step_ms": round(cold_ms, 4), "steps": len(cold), "kernels_avg_ms": cold_kernels,
                        "value_at_median_step": round((fw + bw) / (cold_ms * 1e-3) / 1e12, 2),
                        "flush": "512 MiB written before each step (caches cold), outside the timed region"},
