@@ -128,29 +128,42 @@ def _parse_clock(tool: str, text: str):
 def gpu_clock_under_load(step, seconds: float, median_ms: float):
     """Shader (GFX) clock in MHz as the SMI tool samples it while steps run.
 
-    The tool is started first and steps keep the GPU busy until it has printed (at most
-    ``seconds``), so its sample falls inside the busy period; these steps are outside the timed
-    region. Not
-    run under a profiler (the tool is a script whose interpreter the profiler's preload would
-    follow)."""
+    Steps keep the GPU busy for a second before the tool starts (its reading averages over a recent
+    window, so a short busy period reads as idle) and until it has printed (at most ``seconds``):
+    chunks of about 50 ms of steps, a new one queued whenever the oldest of two queued chunks has
+    finished, so the queue never runs dry and never holds much more than the tool's remaining
+    sampling time. These steps are outside the timed region. Not run under a profiler (the tool is
+    a script whose interpreter the profiler's preload would follow)."""
     import subprocess
 
     import torch
     if any("ROCPROF" in k for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", ""):
         return None
+    per_chunk = max(1, int(50.0 / max(median_ms, 1e-3)))
+
+    def chunk():
+        for _ in range(per_chunk):
+            step()
+        ev = torch.cuda.Event()
+        ev.record()
+        return ev
+
     for tool, cmd in (("amd-smi", ["amd-smi", "metric", "--clock"]), ("rocm-smi", ["rocm-smi", "--showclocks"])):
+        queued = [chunk(), chunk()]
+        t_busy = time.perf_counter() + 1.0
+        while time.perf_counter() < t_busy:
+            queued.pop(0).synchronize()
+            queued.append(chunk())
         try:
             proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
         except OSError:
+            torch.cuda.synchronize()
             continue
-        # steps run until the tool has printed (at most ``seconds``), synchronised every ~50 ms so
-        # that the queue never holds much more than the tool's remaining sampling time
-        per_sync = max(1, int(50.0 / max(median_ms, 1e-3)))
         t_end = time.perf_counter() + seconds
         while proc.poll() is None and time.perf_counter() < t_end:
-            for _ in range(per_sync):
-                step()
-            torch.cuda.synchronize()
+            queued.pop(0).synchronize()
+            queued.append(chunk())
+        torch.cuda.synchronize()
         try:
             text = proc.communicate(timeout=60)[0]
         except subprocess.SubprocessError:
@@ -337,17 +350,23 @@ def main() -> int:
         del p2
     torch.cuda.synchronize()
 
+    # The library creates its timing events on first use: K untimed steps with timing on fill its
+    # event pool, and enabling timing again clears their records, so the timed steps reuse events.
     plan.timing_enable(True)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    plan.timing_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]  # step boundaries
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-        e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    step_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
     kernels = {}
     for name in J.KERNELS:

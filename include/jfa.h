@@ -225,7 +225,9 @@ jfa_status jfa_plan_info(jfa_plan_t plan, int32_t* info, size_t n);
  * partial reduce, 6 bias-gradient clear and finish, 7 MXFP8 quantisation, 8 fused backward of
  * short query sets (2 is not used).
  * jfa_timing_read waits for the recorded events and returns their summed time and count;
- * jfa_timing_enable(plan, 1) also clears previous records. Not thread safe. */
+ * jfa_timing_enable(plan, 1) also clears previous records and reuses the plan's events, which are
+ * created on first use and record without a system-scope memory fence (timing only). Not thread
+ * safe. */
 jfa_status jfa_timing_enable(jfa_plan_t plan, int32_t enable);
 jfa_status jfa_timing_read(jfa_plan_t plan, int32_t kernel, float* total_ms, int32_t* launches);
 

@@ -502,10 +502,13 @@ jfa_status check_problem(const jfa_problem* p, std::vector<int>& lq, std::vector
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Timing events only measure: recording one skips the system-scope memory fence (cache write-back
+// and invalidation) that a default event performs, which would otherwise slow the launches it
+// brackets.
 hipEvent_t take_event(jfa_plan_s* P) {
   if (P->pool_used == P->pool.size()) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     P->pool.push_back(e);
   }
   return P->pool[P->pool_used++];
