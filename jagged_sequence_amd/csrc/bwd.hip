@@ -768,6 +768,7 @@ struct alignas(16) KvSmem2<false, GDPA, NP> {
   float tab[kBuckets];
   float diag[NP][kDiagLen];
   unsigned long long dbh[NP][kDbiasBins];       // per-B-wave bias-gradient bins (fixed point)
+  unsigned char bkt[2][NP][kDiagLen];           // bucket of every distance of the bias window
 };
 
 // One barrier per tile: a three-stage ring and three hand-off buffers (152 KB). The small arrays
@@ -783,6 +784,7 @@ struct alignas(16) KvSmem2<true, GDPA, NP> {
   float dlt[3][kKvBM];
   uint4 xch[3][NP][NPG][2][2][64];
   unsigned char qg[3][2][kKvBM * kRowBytes];
+  unsigned char bkt[2][NP][kDiagLen];  // bucket of every distance of the bias window (tile parity)
 };
 
 // A wave-uniform value the compiler cannot fold into address immediates.
@@ -804,6 +806,43 @@ __device__ __forceinline__ void unpack8(uint4 w, float (&x)[8]) {
   for (int j = 0; j < 4; ++j) {
     x[2 * j] = __builtin_bit_cast(float, v[j] << 16);
     x[2 * j + 1] = __builtin_bit_cast(float, v[j] & 0xffff0000u);
+  }
+}
+
+// The per-wave bias window (see fill_diag) together with the bucket of each of its distances, which
+// the bias gradient of the same key block and query tile reads instead of computing them again.
+__device__ __forceinline__ void fill_diag_buckets(float* vec, unsigned char* bkt, const float* tab, int d0, float mul,
+                                                  int lane) {
+  const int u0 = rel_bucket(d0 + lane);
+  vec[lane] = tab[u0] * mul;
+  bkt[lane] = (unsigned char)u0;
+  if (lane < kDiagLen - 64) {
+    const int u1 = rel_bucket(d0 + 64 + lane);
+    vec[64 + lane] = tab[u1] * mul;
+    bkt[64 + lane] = (unsigned char)u1;
+  }
+}
+
+// DbiasLane::add_run for the bucket table with the buckets of distances d .. d + 7 read from bt[0..7].
+__device__ __forceinline__ void add_run_buckets(DbiasLane& dbl, unsigned long long* bins, int d,
+                                                const unsigned char* bt, const float (&v)[8]) {
+  const int ulo = bt[0], uhi = bt[7];
+  if ((d >= 0 || d + 7 <= 0) && ulo == uhi) {
+    dbl.add(bins, ulo, ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7])));
+  } else if (d >= 32) {
+    // buckets are at least 8 wide from distance 32 on: one edge inside the run
+    const int k = rel_bucket_start(uhi) - d;  // 1..7
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo += j < k ? v[j] : 0.0f;
+      hi += j < k ? 0.0f : v[j];
+    }
+    dbl.add(bins, ulo, lo);
+    dbl.add(bins, uhi, hi);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dbl.add(bins, bt[j], v[j]);
   }
 }
 
@@ -938,7 +977,12 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
     }
   };
   auto fill = [&](int qt) {
-    if (BIAS == kBiasBucket && !isB) fill_diag(sm.diag[pair], sm.tab, qt * BM - key_w - 31, inv_scale, lane_now());
+    if (BIAS == kBiasBucket && !isB) {
+      if constexpr (DBIAS)
+        fill_diag_buckets(sm.diag[pair], sm.bkt[qt & 1][pair], sm.tab, qt * BM - key_w - 31, inv_scale, lane_now());
+      else
+        fill_diag(sm.diag[pair], sm.tab, qt * BM - key_w - 31, inv_scale, lane_now());
+    }
   };
 
   auto stage_ptr = [&](auto st_tag, int which) -> const unsigned char* {
@@ -1091,7 +1135,11 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
             if (!SOFTMAX)
 #pragma unroll
               for (int j = 0; j < 8; ++j) dsv[j] *= invL;
-            dbl.add_run<BIAS == kBiasBucket>(sm.dbh[pair], qrow0 + 32 * qb + 16 * c8 + 8 * hh - kj, dsv);
+            const int d = qrow0 + 32 * qb + 16 * c8 + 8 * hh - kj;
+            if constexpr (BIAS == kBiasBucket)  // distance d sits at 31 + d - qrow0 + key_w of A's window
+              add_run_buckets(dbl, sm.dbh[pair], d, &sm.bkt[qt & 1][pair][31 + 32 * qb + 16 * c8 + 8 * hh - l32], dsv);
+            else
+              dbl.add_run<false>(sm.dbh[pair], d, dsv);
           }
         }
 #pragma unroll
