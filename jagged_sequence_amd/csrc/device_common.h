@@ -95,31 +95,35 @@ __host__ __device__ __forceinline__ int rel_bucket_start(int u) {
 // Only the exp2 and reciprocal units are used, no tanh.
 constexpr float kGeluK2 = 2.0f * 0.7978845608028654f;  // 2 sqrt(2/pi)
 constexpr float kGeluC = 0.044715f;
+// The exponent of sigma(2u) is -log2(e) 2u = x (kGeluE1 + kGeluE3 x^2); (2u)' = kGeluK2 + kGeluD3 x^2.
+constexpr float kGeluE1 = -kLog2e * kGeluK2;
+constexpr float kGeluE3 = -kLog2e * kGeluK2 * kGeluC;
+constexpr float kGeluD3 = 3.0f * kGeluK2 * kGeluC;
 
 template <int ACT>
 __device__ __forceinline__ float act_fwd(float x) {
   if (ACT == kSilu) {
     return x * fast_rcp(1.0f + fast_exp2(-kLog2e * x));
   } else {
-    float z = kGeluK2 * x * (1.0f + kGeluC * x * x);
-    return x * fast_rcp(1.0f + fast_exp2(-kLog2e * z));
+    const float x2 = x * x;
+    return x * fast_rcp(1.0f + fast_exp2(x * __builtin_fmaf(kGeluE3, x2, kGeluE1)));
   }
 }
 
-// act(x) and act'(x) together.
+// act(x) and act'(x) together: SiLU' = sigma + x sigma (1 - sigma) = sigma + f (1 - sigma);
+// GELU_tanh' = sigma(2u) + x sigma(2u) (1 - sigma(2u)) (2u)'.
 template <int ACT>
 __device__ __forceinline__ void act_fwd_grad(float x, float& f, float& g) {
   if (ACT == kSilu) {
-    float sg = fast_rcp(1.0f + fast_exp2(-kLog2e * x));
+    const float sg = fast_rcp(1.0f + fast_exp2(-kLog2e * x));
     f = x * sg;
-    g = sg * (1.0f + x * (1.0f - sg));
+    g = __builtin_fmaf(f, 1.0f - sg, sg);
   } else {
-    float x2 = x * x;
-    float z = kGeluK2 * x * (1.0f + kGeluC * x2);           // 2u
-    float dz = kGeluK2 * (1.0f + 3.0f * kGeluC * x2);        // 2u'
-    float sg = fast_rcp(1.0f + fast_exp2(-kLog2e * z));     // sigma(2u)
+    const float x2 = x * x;
+    const float sg = fast_rcp(1.0f + fast_exp2(x * __builtin_fmaf(kGeluE3, x2, kGeluE1)));  // sigma(2u)
+    const float dz = __builtin_fmaf(kGeluD3, x2, kGeluK2);                                    // (2u)'
     f = x * sg;
-    g = sg + x * sg * (1.0f - sg) * dz;
+    g = __builtin_fmaf(f * (1.0f - sg), dz, sg);
   }
 }
 
