@@ -1047,14 +1047,14 @@ __device__ __forceinline__ void dkdv_item2(const __attribute__((address_space(4)
                 gv[j] = g;
               }
             }
-            if (MASK || !SOFTMAX) {
+            // Rows past the sequence's end need no mask: their dO rows read as zeros, so they add
+            // nothing to dV and their dP, hence dS, is zero (softmax: their P is zero already).
+            if (MASK) {
 #pragma unroll
               for (int j = 0; j < 8; ++j) {
                 // row index from a fresh lane index: this path runs on diagonal tiles only
                 const int qi = qrow0 + 32 * qb + 16 * c8 + 8 * (lane_now() >> 5) + j;
-                const bool masked =
-                    (MASK && (kj >= Lkv || (CAUSAL && kj > qi) || (BAND && (qi < rlo || qi > rhi)))) ||
-                    (!SOFTMAX && qi >= Lq);
+                const bool masked = kj >= Lkv || (CAUSAL && kj > qi) || (BAND && (qi < rlo || qi > rhi));
                 pv[j] = masked ? 0.0f : pv[j];
                 if (!SOFTMAX) gv[j] = masked ? 0.0f : gv[j];
               }

@@ -419,7 +419,7 @@ void fwd_kernel2(FwdArgs a) {
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) p[sb][r] = fast_exp2(__builtin_fmaf(sacc[sb][r], smul, nm));
-    } else {
+    } else if (need_mask) {  // masked scores carry NaN (only on tiles that needed the mask)
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -427,6 +427,11 @@ void fwd_kernel2(FwdArgs a) {
           const float x = sacc[sb][r];
           p[sb][r] = x != x ? 0.0f : act_fwd<ACT>(x * smul);
         }
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[sb][r] = act_fwd<ACT>(sacc[sb][r] * smul);
     }
 
     bf16x8 pb[4];
