@@ -1594,12 +1594,13 @@ void bwd_fused_kernel(BwdArgs a) {
               gv[j] = g;
             }
           }
-          if (need_mask || !SOFTMAX) {
-            // (softmax rows past the sequence's end already have P = 0 from their -inf statistic)
+          // Rows past the sequence's end need no mask: their dO rows read as zeros, so they add
+          // nothing to dV and their dP, hence dS, is zero (softmax: their P is zero already).
+          if (need_mask) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
               const int qi = rbase + j;
-              const bool masked = kj >= Lkv || (CAUSAL && kj > qi) || (!SOFTMAX && qi >= Lq);
+              const bool masked = kj >= Lkv || (CAUSAL && kj > qi);
               pv[j] = masked ? 0.0f : pv[j];
               if (!SOFTMAX) gv[j] = masked ? 0.0f : gv[j];
             }
