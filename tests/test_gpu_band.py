@@ -92,6 +92,28 @@ def test_band_dbias(D, act):
     assert err <= GRAD_REL_L2
 
 
+SHORT_DBIAS = [("none", [1, 37, 64, 5], [300, 64, 129, 1000], 20, 48),
+               ("causal", [1, 37, 64, 50], [1, 37, 64, 50], 20, 48),
+               ("none", [0, 30, 64], [50, 40, 129], 0, 0)]
+
+
+@pytest.mark.parametrize("mask,lq,lkv,window,block", SHORT_DBIAS, ids=["band", "band-causal", "keys-without-queries"])
+def test_short_query_items_dbias(mask, lq, lkv, window, block):
+    """Half-width dK/dV items (two barriers per tile; used when the fused short-query pass is not
+    eligible) with the bias gradient, whose bucket ids come from the score wave's bias window."""
+    x = ji.make_inputs(lq, lkv, 2, 128, wid=55, mask=mask, act="softmax", bias_kind="bucket", bias_sigma=0.5,
+                       window=window, block=block)
+    say(f"case short-query dbias mask={mask} window={window} block={block} lq={lq}")
+    gpu = run_gpu(x, dbias=True)
+    info = gpu["plan"].info()
+    assert info["kv_bn"] == 64 and info["fused_bwd"] == 0
+    ref = oracle(x)
+    compare(x, gpu, ref)
+    err = float(rel_l2(to_np(gpu["dbias"]), ref["dbias"]))
+    say(f"  dbias rel-L2 {err:.2e}")
+    assert err <= GRAD_REL_L2
+
+
 def _sample(lq, cap, n_random, seed):
     """The longest sequence no longer than ``cap``, the shortest, and ``n_random`` random ones."""
     order = [int(b) for b in np.argsort(lq, kind="stable")]
